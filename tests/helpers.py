@@ -1,0 +1,57 @@
+"""Shared test helpers: convert synthetic inputs for the oracle, error metrics."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import OracleParams
+from vggt_global_attention_amd.configs import Workload
+
+
+def f64(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle_params(w: Workload, inp: dict, **over) -> OracleParams:
+    kw = dict(
+        Wqkv=f64(inp["Wqkv"]), Wo=f64(inp["Wo"]),
+        q_gamma=f64(inp["q_gamma"]), q_beta=f64(inp["q_beta"]),
+        k_gamma=f64(inp["k_gamma"]), k_beta=f64(inp["k_beta"]),
+        H=w.H, grid_h=w.grid_h, grid_w=w.grid_w,
+        rope_base=w.rope_base, ln_eps=w.ln_eps, pos_offset=0,
+    )
+    kw.update(over)
+    return OracleParams(**kw)
+
+
+def metrics(y, ref) -> dict:
+    """relL1 = sum|y-ref| / sum|ref|; max|err|/max|ref|; mean|err|/max|ref|."""
+    y = f64(y).ravel()
+    ref = f64(ref).ravel()
+    err = np.abs(y - ref)
+    mref = float(np.abs(ref).max()) if ref.size else 0.0
+    sref = float(np.abs(ref).sum()) if ref.size else 0.0
+    return {
+        "relL1": float(err.sum() / sref) if sref > 0 else float(err.sum()),
+        "max_over_max": float(err.max() / mref) if mref > 0 else float(err.max() if err.size else 0.0),
+        "mean_over_max": float(err.mean() / mref) if mref > 0 else float(err.mean() if err.size else 0.0),
+        "nonfinite": int((~np.isfinite(f64(y))).sum()),
+    }
+
+
+# Tolerance fixed by the benchmark spec for the bf16-in / fp32-accumulate path:
+# max|err| <= 1e-2 * max|ref| and mean relative error (read as relL1) <= 2e-3.
+TOL_MAX = 1e-2
+TOL_RELL1 = 2e-3
+
+
+def assert_parity(y, ref, label="", tol_rel=TOL_RELL1, tol_max=TOL_MAX):
+    m = metrics(y, ref)
+    msg = f"{label}: {m}"
+    assert m["nonfinite"] == 0, msg
+    assert m["max_over_max"] <= tol_max, msg
+    assert m["relL1"] <= tol_rel, msg
+    return m

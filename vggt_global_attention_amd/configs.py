@@ -1,0 +1,81 @@
+"""Workload registry: the shapes the library is tested and measured on.
+
+Each workload is one attention block of the VGGT Aggregator at a given frame
+count.  Frames are 416x624 images cut into 16-pixel patches (26 x 39 = 1014
+patches) plus 1 camera and 16 register tokens, so T = 1031 tokens per frame
+("VGGT-Omega Aggregator explainer", ksqn.cn, sections 二 and 五).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+N_SPECIAL = 17
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cid: int            # seed namespace: seed = 1000 * cid + tensor index
+    S: int              # frames
+    grid_h: int
+    grid_w: int
+    d: int
+    H: int
+    modes: tuple        # block modes this workload is run in, in order
+    dup_frames: int = 0  # frames replaced by a noisy copy of their predecessor
+    rope_base: float = 100.0
+    ln_eps: float = 1e-5
+
+    @property
+    def T(self) -> int:
+        return N_SPECIAL + self.grid_h * self.grid_w
+
+    @property
+    def N(self) -> int:
+        return self.S * self.T
+
+    @property
+    def R(self) -> int:
+        return self.S * N_SPECIAL
+
+    @property
+    def Dh(self) -> int:
+        return self.d // self.H
+
+    def attention_flop(self, mode: str) -> float:
+        """4 * sum(L^2) * d over the attention sets of one block (2 FLOP per MAC)."""
+        if mode == "frame":
+            return 4.0 * self.S * self.T ** 2 * self.d
+        if mode == "global":
+            return 4.0 * self.N ** 2 * self.d
+        if mode == "register":
+            return 4.0 * self.R ** 2 * self.d
+        raise ValueError(mode)
+
+    def gemm_flop(self, mode: str) -> float:
+        """QKV projection (6 M d^2) plus output projection (2 M d^2)."""
+        M = self.R if mode == "register" else self.N
+        return 8.0 * M * self.d ** 2
+
+    def flop(self, mode: str) -> float:
+        return self.attention_flop(mode) + self.gemm_flop(mode)
+
+
+WORKLOADS = {
+    # tiny alternating block: the full oracle finishes in well under a second
+    "tiny": Workload("tiny", 1, 2, 8, 8, 256, 4, ("frame", "global")),
+    # VGGT scale, 24 frames (N = 24,744): global layer, also run as frame layer
+    "s24": Workload("s24", 2, 24, 26, 39, 1024, 16, ("global", "frame")),
+    # long global attention, 100 frames (N = 103,100): the measured workload
+    "s100": Workload("s100", 3, 100, 26, 39, 1024, 16, ("global",)),
+    # register mode at scale: frame over 500 x 1031, then 8,500 special tokens
+    "s500": Workload("s500", 4, 500, 26, 39, 1024, 16, ("frame", "register")),
+    # stress global attention, 300 frames (N = 309,300), 10% duplicated frames
+    "s300": Workload("s300", 5, 300, 26, 39, 1024, 16, ("global",), dup_frames=30),
+}
+
+
+def custom(name: str, S: int, grid_h: int, grid_w: int, d: int, H: int,
+           cid: int = 99, modes=("frame", "global", "register")) -> Workload:
+    return Workload(name, cid, S, grid_h, grid_w, d, H, tuple(modes))
