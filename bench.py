@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark: one global-attention layer of the VGGT Aggregator at S = 100 frames.
+
+A step is one full call of the block -- range guards + QKV projection with QK
+LayerNorm and 2D RoPE + attention core + output projection -- over
+X[100, 1031, 1024] bf16 (N = 103,100 tokens, d = 1024, H = 16, Dh = 64), with
+every input already resident in HBM.  Prints ONE JSON line:
+
+  value        algorithmic TFLOP/s of the whole layer (4 N^2 d + 8 N d^2 FLOP)
+  ms_per_step  ms per layer
+  roofline     the attention-core kernel alone, timed on the call's stream
+               with HIP events, against the dense fp16/bf16 MFMA peak
+  cpu_baseline the fp64 NumPy oracle timed on this host on a bounded sample
+  extra        ms/layer of the other block modes and frame counts
+
+Inputs are seeded synthetic data (X ~ N(0,1), weights ~ N(0,1/d), gamma ~
+1+N(0,0.1), beta ~ N(0,0.1)); there are no trained weights.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "global-attention ms/layer + TFLOP/s (frac of bf16 MFMA peak) at S frames, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="s100")
+    ap.add_argument("--mode", default="global", choices=["global", "frame", "register"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other modes / sizes")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU sample")
+    ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
+                    help="time one stage in a loop (for profilers) and print its ms")
+    return ap.parse_args()
+
+
+def gpu_inputs(w):
+    import torch
+    from vggt_global_attention_amd import synth
+    inp = synth.make_inputs(w)
+    keys = ("X", "Wqkv", "Wo", "q_gamma", "q_beta", "k_gamma", "k_beta")
+    return inp, {k: inp[k].to("cuda").contiguous() for k in keys}
+
+
+def time_block(w, mode, d, steps, warmup):
+    """ms per full call and ms per attention-core stage, both with HIP events
+    on the stream the library launches on (torch's current stream)."""
+    import torch
+    from vggt_global_attention_amd import api
+    from vggt_global_attention_amd import binding as B
+    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w)
+    args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+    Y = torch.empty_like(d["X"])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        blk(*args, Y=Y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        blk(*args, Y=Y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    # attention core alone: the workspace holds q/k/v from the calls above; the
+    # core overwrites q with O, so rerun the QKV stage (untimed) before each core.
+    core = 0.0
+    for i in range(steps):
+        blk.stage(B.STAGE_QKV, *args, Y)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        blk.stage(B.STAGE_CORE, *args, Y)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        core += c0.elapsed_time(c1)
+    return ms_step, core / steps
+
+
+def loop_stage(w, mode, d, stage, steps):
+    import torch
+    from vggt_global_attention_amd import api
+    from vggt_global_attention_amd import binding as B
+    st = {"prep": B.STAGE_PREP, "qkv": B.STAGE_QKV, "core": B.STAGE_CORE, "out": B.STAGE_OUT}
+    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w)
+    args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+    Y = torch.empty_like(d["X"])
+    blk(*args, Y=Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if stage == "core":
+            blk.stage(B.STAGE_QKV, *args, Y)
+        blk.stage(st[stage], *args, Y)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def cpu_baseline(w, inp, n_rows):
+    """The fp64 oracle on a bounded sample of the same layer: k/v for all N
+    tokens, then q, attention and output projection for n_rows query rows."""
+    import numpy as np
+    import torch
+    import oracle
+    from vggt_global_attention_amd import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    os.environ["ORACLE_THREADS"] = str(threads)
+    p = oracle.OracleParams(
+        Wqkv=inp["Wqkv"].to(torch.float64).numpy(), Wo=inp["Wo"].to(torch.float64).numpy(),
+        q_gamma=inp["q_gamma"].double().numpy(), q_beta=inp["q_beta"].double().numpy(),
+        k_gamma=inp["k_gamma"].double().numpy(), k_beta=inp["k_beta"].double().numpy(),
+        H=w.H, grid_h=w.grid_h, grid_w=w.grid_w)
+    X = inp["X"].to(torch.float64).numpy()
+    rows = synth.sample_rows(w, n_rows).numpy()
+    t0 = time.perf_counter()
+    oracle.global_attention_rows(X, p, rows, threads=threads)
+    dt = time.perf_counter() - t0
+    n, d = w.N, w.d
+    flop = 4.0 * n * d * d + len(rows) * (2.0 * d * d + 4.0 * n * d + 2.0 * d * d)
+    full_s = dt * (w.flop("global") / flop)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name} global layer: k/v for all {n} tokens + {len(rows)} sampled query "
+                      f"rows (q, attention over all keys, Wo); {flop / 1e12:.3f} TFLOP in {dt:.1f} s; "
+                      f"full layer extrapolates to {full_s / 60:.0f} min",
+            "ms_per_step_extrapolated": full_s * 1e3}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "requested_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    from vggt_global_attention_amd import configs
+    from vggt_global_attention_amd import binding as B
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    B.lib()  # fails loudly without the HIP library
+    w = configs.WORKLOADS[a.workload]
+    print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
+    inp, d = gpu_inputs(w)
+    if a.only_stage:
+        ms = loop_stage(w, a.mode, d, a.only_stage, a.steps)
+        print(json.dumps({"stage": a.only_stage, "mode": a.mode, "workload": w.name,
+                          "ms_per_iter_wall": ms}))
+        return
+    print(f"[bench] timing {a.mode} ({a.warmup} warmup + {a.steps} steps)", file=sys.stderr, flush=True)
+    ms, core_ms = time_block(w, a.mode, d, a.steps, a.warmup)
+    flop = w.flop(a.mode)
+    attn_flop = w.attention_flop(a.mode)
+    achieved = attn_flop / (core_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": flop / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in/out; bf16 MFMA projections, fp16 MFMA attention, fp32 accumulate",
+        "data": "synthetic (seeded; no trained weights)",
+        "config": {"workload": f"{a.mode} attention layer, S={w.S} frames x T={w.T} tokens "
+                               f"({w.grid_h}x{w.grid_w} patches + 17 special), N={w.N}, "
+                               f"d={w.d}, H={w.H}, Dh={w.Dh}",
+                   "S": w.S, "T": w.T, "N": w.N, "d": w.d, "H": w.H, "mode": a.mode,
+                   "flop_per_step": flop},
+        "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (attention core)",
+                     "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "flop_per_launch": attn_flop, "ms_per_launch": core_ms},
+    }
+    if not a.no_extra and a.workload == "s100":
+        extra = {}
+        for name, mode in (("s24", "global"), ("s24", "frame"), ("s500", "frame"),
+                           ("s500", "register")):
+            ww = configs.WORKLOADS[name]
+            print(f"[bench] extra {name} {mode}", file=sys.stderr, flush=True)
+            _, dd = gpu_inputs(ww)
+            m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2)
+            extra[f"{name}_{mode}"] = {"ms_per_layer": m2, "tflops": ww.flop(mode) / m2 / 1e9,
+                                       "core_ms": c2,
+                                       "core_tflops": ww.attention_flop(mode) / c2 / 1e9}
+            del dd
+            torch.cuda.empty_cache()
+        out["extra"] = extra
+    if not a.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

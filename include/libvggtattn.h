@@ -1,0 +1,138 @@
+/*
+ * libvggtattn -- one VGGT Aggregator attention block per call, on an AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What a call computes (sources are the web pages this library is built from):
+ *   - Token recipe, "VGGT-Omega Aggregator explainer" (ksqn.cn), section 二:
+ *     every frame is [1 camera token][16 register tokens][grid_h*grid_w patch
+ *     tokens], so T = 17 + grid_h*grid_w; patches are in row-major grid order.
+ *   - Per attention set: [q|k|v] = x Wqkv^T (no bias); q and k are
+ *     LayerNorm-ed over the Dh features of each head (biased variance, eps =
+ *     ln_eps) with a per-head affine (gamma, beta) -- the page's "use_qk_norm"
+ *     (section 三); then patch tokens get a 2D rotary encoding (section 三, and
+ *     the HTTM article's RoPE analysis, figures 4-5): the first Dh/2 features
+ *     turn with the grid row + pos_offset, the last Dh/2 with the grid column
+ *     + pos_offset; feature i of a half pairs with feature i + Dh/4 and turns
+ *     by pos * rope_base^(-i/(Dh/4)).  Camera and register tokens are not
+ *     rotated, and nothing encodes the frame index.  Then, per head,
+ *     softmax(q k^T / sqrt(Dh)) v, heads concatenated, times Wo^T.  No bias,
+ *     no residual, no LayerScale: Y is the raw attention-branch output.
+ *   - vggt_attn_frame: one set per frame (the frame block, section 三).
+ *   - vggt_attn_global: all S*T tokens in one set (global mode, section 三;
+ *     the dominant cost per the HTTM article section 02 and the AVGGT summary).
+ *   - vggt_attn_global_register: only the 17 special tokens of every frame, as
+ *     one set of 17*S tokens (register mode, section 三); patch rows of Y are
+ *     a copy of X (patch tokens keep to their own frame in this block).
+ *
+ * Conventions for every entry point below:
+ *   - Tensor pointers are DEVICE pointers on the current HIP device; dense,
+ *     row-major, no strides.  X, Y: bf16 [S][T][d].  Wqkv: bf16 [3d][d], rows
+ *     = [Q heads 0..H-1; K heads; V heads], Dh rows per head.  Wo: bf16 [d][d]
+ *     (Y = O Wo^T).  q_gamma, q_beta, k_gamma, k_beta: fp32 [H][Dh] (replicate
+ *     one row H times for an affine shared across heads).
+ *   - X, Y, Wqkv, Wo must be 16-byte aligned, gamma/beta 4-byte aligned, the
+ *     workspace 256-byte aligned.
+ *   - v1 limits: Dh = d/H must be 64, d a multiple of 128, S >= 1, grid_h,
+ *     grid_w >= 0, T = 17 + grid_h*grid_w, S*T < 2^31 tokens.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it and the call returns without synchronising; kernel
+ *     faults surface at the caller's next synchronisation.
+ *   - Ownership: the caller owns every buffer, including the workspace of at
+ *     least vggt_attn_workspace_bytes() bytes.  The library allocates and frees
+ *     nothing and keeps no pointer after the call returns (beyond the work it
+ *     enqueued).  It holds no mutable global state and is re-entrant; calls
+ *     that share a workspace must be ordered on one stream.
+ *   - Aliasing: Y must not overlap X, the weights, gamma/beta or the
+ *     workspace, with one exception: vggt_attn_global_register accepts Y == X
+ *     (in place), and then writes only the 17*S special rows.
+ *   - Errors: every argument is checked before anything is enqueued; on a
+ *     nonzero return nothing was launched and Y is untouched.  Non-finite
+ *     values inside X or the weights are not checked and propagate to Y.
+ */
+#ifndef LIBVGGTATTN_H
+#define LIBVGGTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define VGGT_ATTN_OK          0
+#define VGGT_ATTN_EINVAL     (-1) /* null pointer, unknown mode/stage, forbidden aliasing */
+#define VGGT_ATTN_ESHAPE     (-2) /* shape outside the supported set (see above) */
+#define VGGT_ATTN_EALIGN     (-3) /* pointer misaligned */
+#define VGGT_ATTN_EWORKSPACE (-4) /* workspace smaller than vggt_attn_workspace_bytes() */
+#define VGGT_ATTN_EHIP       (-5) /* the HIP runtime rejected a launch */
+#define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of range */
+
+/* Block modes. */
+#define VGGT_ATTN_MODE_FRAME    0
+#define VGGT_ATTN_MODE_GLOBAL   1
+#define VGGT_ATTN_MODE_REGISTER 2
+
+/* Stages of one call, in order (see vggt_attn_stage). */
+#define VGGT_ATTN_STAGE_PREP 0 /* range bounds, RoPE table, fp16 copy of Wo */
+#define VGGT_ATTN_STAGE_QKV  1 /* QKV projection + per-head QK LayerNorm + 2D RoPE */
+#define VGGT_ATTN_STAGE_CORE 2 /* softmax(q k^T / sqrt(Dh)) v for every set and head */
+#define VGGT_ATTN_STAGE_OUT  3 /* output projection (+ register-mode patch copy) */
+
+typedef struct vggt_attn_shape {
+  int32_t S;          /* frames */
+  int32_t T;          /* tokens per frame = 17 + grid_h*grid_w */
+  int32_t d;          /* model width */
+  int32_t H;          /* heads; Dh = d/H */
+  int32_t grid_h;     /* patch grid rows (26 for a 416-pixel-high image at 16 px) */
+  int32_t grid_w;     /* patch grid columns (39 for 624 px) */
+  float rope_base;    /* RoPE frequency base, e.g. 100 */
+  float ln_eps;       /* QK LayerNorm epsilon, e.g. 1e-5 */
+  int32_t pos_offset; /* patch (r, c) sits at position (r + off, c + off); 0..65535 */
+} vggt_attn_shape;
+
+/* Bytes of device workspace a call in `mode` needs for `shape`; 0 if the
+   mode or shape is not supported.  Pure host arithmetic, no HIP call. */
+size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape);
+
+/* Frame block: attention inside each frame (S sets of T tokens). */
+int vggt_attn_frame(const vggt_attn_shape* shape, const void* X, const void* Wqkv,
+                    const void* Wo, const float* q_gamma, const float* q_beta,
+                    const float* k_gamma, const float* k_beta, void* Y,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Global mode: all S*T tokens form one set. */
+int vggt_attn_global(const vggt_attn_shape* shape, const void* X, const void* Wqkv,
+                     const void* Wo, const float* q_gamma, const float* q_beta,
+                     const float* k_gamma, const float* k_beta, void* Y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Register mode: tokens 0..16 of every frame form one set of 17*S tokens;
+   patch rows of Y are copied from X (nothing is written there when Y == X). */
+int vggt_attn_global_register(const vggt_attn_shape* shape, const void* X,
+                              const void* Wqkv, const void* Wo, const float* q_gamma,
+                              const float* q_beta, const float* k_gamma,
+                              const float* k_beta, void* Y, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* One stage of a call in `mode` (VGGT_ATTN_STAGE_*), same arguments and
+   checks as the full call.  Running the four stages in order on one stream
+   with one workspace is exactly the full call; a stage reads what the
+   previous stages left in the workspace.  Meant for timing and profiling
+   the kernels one by one. */
+int vggt_attn_stage(int mode, int stage, const vggt_attn_shape* shape, const void* X,
+                    const void* Wqkv, const void* Wo, const float* q_gamma,
+                    const float* q_beta, const float* k_gamma, const float* k_beta,
+                    void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* vggt_attn_status_str(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int vggt_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBVGGTATTN_H */

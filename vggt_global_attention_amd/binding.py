@@ -1,0 +1,111 @@
+"""ctypes binding of libvggtattn: the C entry points under the same names.
+
+Argument marshalling only -- every step of the computation runs in the HIP
+library.  If the library is missing this module raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
+MODE_FRAME, MODE_GLOBAL, MODE_REGISTER = 0, 1, 2
+STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
+MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER}
+
+EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
+           "vggt_attn_global_register", "vggt_attn_stage", "vggt_attn_status_str",
+           "vggt_attn_version")
+
+
+class vggt_attn_shape(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("T", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("ln_eps", ctypes.c_float),
+                ("pos_offset", ctypes.c_int32)]
+
+
+class VggtAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+_lib = None
+_CALL_ARGS = [ctypes.POINTER(vggt_attn_shape)] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 4 + \
+    [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+
+def lib(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) the built library; raise if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"libvggtattn not built ({path} missing): run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    L.vggt_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.vggt_attn_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(vggt_attn_shape)]
+    for name in ("vggt_attn_frame", "vggt_attn_global", "vggt_attn_global_register"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = _CALL_ARGS
+    L.vggt_attn_stage.restype = ctypes.c_int
+    L.vggt_attn_stage.argtypes = [ctypes.c_int, ctypes.c_int] + _CALL_ARGS
+    L.vggt_attn_status_str.restype = ctypes.c_char_p
+    L.vggt_attn_status_str.argtypes = [ctypes.c_int]
+    L.vggt_attn_version.restype = ctypes.c_int
+    L.vggt_attn_version.argtypes = []
+    _lib = L
+    return L
+
+
+def make_shape(S, T, d, H, grid_h, grid_w, rope_base=100.0, ln_eps=1e-5, pos_offset=0):
+    return vggt_attn_shape(S, T, d, H, grid_h, grid_w, rope_base, ln_eps, pos_offset)
+
+
+def vggt_attn_workspace_bytes(mode: int, shape: vggt_attn_shape) -> int:
+    return lib().vggt_attn_workspace_bytes(mode, ctypes.byref(shape))
+
+
+def _call(name, *args):
+    return getattr(lib(), name)(*args)
+
+
+def vggt_attn_frame(shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace,
+                    workspace_bytes, stream) -> int:
+    return _call("vggt_attn_frame", ctypes.byref(shape), X, Wqkv, Wo, q_gamma, q_beta,
+                 k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global(shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace,
+                     workspace_bytes, stream) -> int:
+    return _call("vggt_attn_global", ctypes.byref(shape), X, Wqkv, Wo, q_gamma, q_beta,
+                 k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global_register(shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y,
+                              workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_global_register", ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
+                 q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_stage(mode, stage, shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y,
+                    workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_stage", mode, stage, ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
+                 q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().vggt_attn_status_str(status).decode()
+    except Exception:
+        return "?"
+
+
+def vggt_attn_version() -> int:
+    return lib().vggt_attn_version()

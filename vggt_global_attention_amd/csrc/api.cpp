@@ -1,0 +1,204 @@
+// C ABI of libvggtattn: argument checks, planning and stage dispatch.  Every
+// check runs before the first HIP call, so a rejected call launches nothing.
+#include <math.h>
+#include <string.h>
+
+#include "plan.h"
+
+namespace vggt {
+
+static int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
+  if (!s || !p) return VGGT_ATTN_EINVAL;
+  if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
+      mode != VGGT_ATTN_MODE_REGISTER)
+    return VGGT_ATTN_EINVAL;
+  if (s->S < 1 || s->H < 1 || s->d < 1 || s->grid_h < 0 || s->grid_w < 0) return VGGT_ATTN_ESHAPE;
+  if (s->d != s->H * kDh || s->d % kGemmBN != 0) return VGGT_ATTN_ESHAPE;
+  const int64_t patches = (int64_t)s->grid_h * s->grid_w;
+  if (patches > (1 << 24) || (int64_t)s->T != kSpecial + patches) return VGGT_ATTN_ESHAPE;
+  const int64_t N = (int64_t)s->S * s->T;
+  if (N >= ((int64_t)1 << 31)) return VGGT_ATTN_ESHAPE;
+  if (!(isfinite(s->rope_base) && s->rope_base > 0.f)) return VGGT_ATTN_ERANGE;
+  if (!(isfinite(s->ln_eps) && s->ln_eps > 0.f)) return VGGT_ATTN_ERANGE;
+  if (s->pos_offset < 0 || s->pos_offset > 65535) return VGGT_ATTN_ERANGE;
+
+  memset(p, 0, sizeof(*p));
+  p->mode = mode;
+  p->S = s->S;
+  p->T = s->T;
+  p->d = s->d;
+  p->H = s->H;
+  p->gh = s->grid_h;
+  p->gw = s->grid_w;
+  p->off = s->pos_offset;
+  p->base = s->rope_base;
+  p->eps = s->ln_eps;
+  const int64_t R = (int64_t)s->S * kSpecial;
+  int64_t cover;  // workspace rows the attention kernel may touch
+  if (mode == VGGT_ATTN_MODE_GLOBAL) {
+    p->nseq = 1;
+    p->L = (int)N;
+    p->seq_stride = round_up(N, kAttnBK);
+    cover = p->seq_stride;
+    p->attn_qb = 4;
+    p->attn_waves = 4;
+  } else if (mode == VGGT_ATTN_MODE_FRAME) {
+    p->nseq = s->S;
+    p->L = s->T;
+    p->seq_stride = round_up(s->T, kAttnBK);
+    cover = p->seq_stride * s->S;
+    p->attn_qb = 2;
+    p->attn_waves = 4;
+  } else {
+    p->nseq = 1;
+    p->L = (int)R;
+    p->seq_stride = round_up(R, kAttnBK);
+    cover = p->seq_stride;
+    p->attn_qb = 4;
+    p->attn_waves = 4;
+  }
+  p->rows = round_up(cover, kRowAlign);
+  if (mode == VGGT_ATTN_MODE_GLOBAL) {
+    p->map = RowMap{p->rows, 0, (int32_t)N, 1};
+  } else if (mode == VGGT_ATTN_MODE_FRAME) {
+    p->map = RowMap{p->seq_stride, s->T, s->T, s->S};
+  } else {
+    p->map = RowMap{kSpecial, s->T, kSpecial, s->S};
+  }
+  p->rope_npos = (s->grid_h > s->grid_w ? s->grid_h : s->grid_w) + s->pos_offset;
+  if (p->rope_npos < 1) p->rope_npos = 1;
+
+  size_t off = 0;
+  p->off_scal = off;
+  off += round_up((int64_t)sizeof(float) * (4 + s->H), 256);
+  p->off_rope = off;
+  off += round_up((int64_t)p->rope_npos * 16 * sizeof(float2), 256);
+  p->off_wo = off;
+  off += round_up((int64_t)s->d * s->d * 2, 256);
+  const size_t qkv = (size_t)s->H * (size_t)p->rows * kDh * 2;
+  p->off_q = off;
+  off += qkv;
+  p->off_k = off;
+  off += qkv;
+  p->off_v = off;
+  off += qkv;
+  p->total = off;
+  return VGGT_ATTN_OK;
+}
+
+}  // namespace vggt
+
+using namespace vggt;
+
+namespace {
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int check_call(int mode, const vggt_attn_shape* shape, const void* X, const void* Wqkv,
+               const void* Wo, const float* qg, const float* qb, const float* kg, const float* kb,
+               void* Y, void* ws, size_t ws_bytes, Plan* plan) {
+  int st = make_plan(mode, shape, plan);
+  if (st != VGGT_ATTN_OK) return st;
+  if (!X || !Wqkv || !Wo || !qg || !qb || !kg || !kb || !Y || !ws) return VGGT_ATTN_EINVAL;
+  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(Wqkv, 16) || !aligned(Wo, 16) ||
+      !aligned(qg, 4) || !aligned(qb, 4) || !aligned(kg, 4) || !aligned(kb, 4) || !aligned(ws, 256))
+    return VGGT_ATTN_EALIGN;
+  if (ws_bytes < plan->total) return VGGT_ATTN_EWORKSPACE;
+  const size_t nx = (size_t)plan->S * plan->T * plan->d * 2;
+  const size_t nw = (size_t)3 * plan->d * plan->d * 2, no = (size_t)plan->d * plan->d * 2;
+  const size_t ng = (size_t)plan->H * kDh * 4;
+  const bool in_place = (mode == VGGT_ATTN_MODE_REGISTER && Y == X);
+  if (!in_place && overlap(Y, nx, X, nx)) return VGGT_ATTN_EINVAL;
+  if (overlap(Y, nx, Wqkv, nw) || overlap(Y, nx, Wo, no) || overlap(Y, nx, qg, ng) ||
+      overlap(Y, nx, qb, ng) || overlap(Y, nx, kg, ng) || overlap(Y, nx, kb, ng) ||
+      overlap(Y, nx, ws, plan->total))
+    return VGGT_ATTN_EINVAL;
+  // The workspace is written by the library: it must not hold any input.
+  if (overlap(ws, plan->total, X, nx) || overlap(ws, plan->total, Wqkv, nw) ||
+      overlap(ws, plan->total, Wo, no) || overlap(ws, plan->total, qg, ng) ||
+      overlap(ws, plan->total, qb, ng) || overlap(ws, plan->total, kg, ng) ||
+      overlap(ws, plan->total, kb, ng))
+    return VGGT_ATTN_EINVAL;
+  return VGGT_ATTN_OK;
+}
+
+int run(int mode, int first_stage, int last_stage, const vggt_attn_shape* shape, const void* X,
+        const void* Wqkv, const void* Wo, const float* qg, const float* qb, const float* kg,
+        const float* kb, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  Plan plan;
+  int st = check_call(mode, shape, X, Wqkv, Wo, qg, qb, kg, kb, Y, ws, ws_bytes, &plan);
+  if (st != VGGT_ATTN_OK) return st;
+  Ptrs a{reinterpret_cast<const bf16*>(X), reinterpret_cast<const bf16*>(Wqkv),
+         reinterpret_cast<const bf16*>(Wo), qg, qb, kg, kb, reinterpret_cast<bf16*>(Y),
+         reinterpret_cast<char*>(ws)};
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  for (int stage = first_stage; stage <= last_stage; ++stage) {
+    hipError_t e = hipSuccess;
+    switch (stage) {
+      case VGGT_ATTN_STAGE_PREP: e = launch_prep(plan, a, hs); break;
+      case VGGT_ATTN_STAGE_QKV: e = launch_qkv(plan, a, hs); break;
+      case VGGT_ATTN_STAGE_CORE: e = launch_core(plan, a, hs); break;
+      case VGGT_ATTN_STAGE_OUT: e = launch_out(plan, a, hs); break;
+    }
+    if (e != hipSuccess) return VGGT_ATTN_EHIP;
+  }
+  return VGGT_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape) {
+  Plan plan;
+  if (make_plan(mode, shape, &plan) != VGGT_ATTN_OK) return 0;
+  return plan.total;
+}
+
+#define VGGT_ARGS                                                                          \
+  const vggt_attn_shape *shape, const void *X, const void *Wqkv, const void *Wo,            \
+      const float *q_gamma, const float *q_beta, const float *k_gamma, const float *k_beta, \
+      void *Y, void *workspace, size_t workspace_bytes, void *stream
+#define VGGT_PASS \
+  shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream
+
+int vggt_attn_frame(VGGT_ARGS) {
+  return run(VGGT_ATTN_MODE_FRAME, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_global(VGGT_ARGS) {
+  return run(VGGT_ATTN_MODE_GLOBAL, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_global_register(VGGT_ARGS) {
+  return run(VGGT_ATTN_MODE_REGISTER, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {
+  if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
+  return run(mode, stage, stage, VGGT_PASS);
+}
+
+const char* vggt_attn_status_str(int status) {
+  switch (status) {
+    case VGGT_ATTN_OK: return "ok";
+    case VGGT_ATTN_EINVAL: return "invalid argument (null pointer, unknown mode or stage, or forbidden aliasing)";
+    case VGGT_ATTN_ESHAPE: return "unsupported shape (need Dh = 64, d % 128 == 0, T = 17 + grid_h*grid_w, S*T < 2^31)";
+    case VGGT_ATTN_EALIGN: return "misaligned pointer (tensors 16 B, gamma/beta 4 B, workspace 256 B)";
+    case VGGT_ATTN_EWORKSPACE: return "workspace smaller than vggt_attn_workspace_bytes()";
+    case VGGT_ATTN_EHIP: return "HIP runtime error while enqueueing a kernel";
+    case VGGT_ATTN_ERANGE: return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535";
+    default: return "unknown status";
+  }
+}
+
+int vggt_attn_version(void) { return 10000; }
+
+}  // extern "C"

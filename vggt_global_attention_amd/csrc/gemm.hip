@@ -1,0 +1,318 @@
+// Projection GEMMs of the attention block on gfx950 MFMA, with fused epilogues.
+//
+//   QKV: [q|k|v] = x Wqkv^T for every workspace row (bf16 x bf16 -> fp32),
+//        then per (token, head): LayerNorm of q and k over the 64 features
+//        with the per-head gamma/beta, 2D RoPE on patch tokens, q scaled by
+//        log2(e)/sqrt(64) (the attention kernel works in base 2), fp16 store.
+//        v is scaled by an exact power of two (range guard) and stored
+//        transposed, key-major, for the attention kernel.
+//   OUT: Y = O Wo^T (fp16 x fp16 -> fp32), exact power-of-two un-scaling,
+//        bf16 store scattered to the X-row of every workspace row.
+//
+// Tile: 128 token rows x 128 output features x 64-deep k-steps, 4 waves, each
+// wave a 64 x 64 block = one head for 64 tokens, so the LayerNorm and the RoPE
+// pairs (feature i, i+16) of a (token, head) never leave the wave.  MFMA
+// 16x16x32 computes the block transposed (features x tokens): each lane then
+// holds one token and 16 of its features, the other 48 sitting in the three
+// lanes 16 apart.  LDS tiles are 128-byte rows with the 16-byte chunk index
+// XOR-swizzled by (row & 7); global->LDS is double buffered through registers.
+#include "plan.h"
+
+namespace vggt {
+
+struct GemmArgs {
+  const void* A;  // weights [Nf][K], row-major (bf16 for QKV, fp16 for OUT)
+  const void* B;  // QKV: X bf16 [S*T][d] through `map`; OUT: O fp16 [H][rows][64]
+  int64_t rows;   // workspace rows (multiple of 128)
+  int Nf, K;
+  RowMap map;
+  int T, gw, off, d;
+  float eps;
+  const float *qg, *qb, *kg, *kb;
+  const float2* rope;
+  Scalars* sc;
+  f16 *q, *k, *vt;
+  bf16* y;
+};
+
+enum { kEpiQKV = 0, kEpiOut = 1 };
+
+template <int EPI>
+struct GemmTypes;
+template <>
+struct GemmTypes<kEpiQKV> {
+  typedef bf16x8 V8;
+};
+template <>
+struct GemmTypes<kEpiOut> {
+  typedef f16x8 V8;
+};
+
+__device__ __forceinline__ int swz(int row, int col) { return row * 128 + ((col ^ (row & 7)) << 4); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+  typedef typename GemmTypes<EPI>::V8 V8;
+  __shared__ __attribute__((aligned(16))) char smem[2][2][kGemmBM * 128];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int j = lane & 15, gq = lane >> 4;
+
+  const int ntn = g.Nf / kGemmBN;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(logical / ntn) * kGemmBM;
+  const int n0 = (logical % ntn) * kGemmBN;
+
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (int64_t)n0 * g.K;
+  const uint16_t* Bbase = reinterpret_cast<const uint16_t*>(g.B);
+
+  // This thread's four A chunks and four B chunks per k-step.
+  const uint16_t* aptr[4];
+  const uint16_t* bptr[4];
+  bool bval[4];
+  int soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, col = c & 7;
+    soff[i] = swz(row, col);
+    aptr[i] = A + (int64_t)row * g.K + col * 8;
+    if (EPI == kEpiQKV) {
+      const int64_t src = g.map.src(m0 + row);
+      bval[i] = src >= 0;
+      bptr[i] = Bbase + (bval[i] ? src : 0) * g.K + col * 8;
+    } else {
+      bval[i] = true;
+      bptr[i] = Bbase + (m0 + row) * kDh + col * 8;
+    }
+  }
+
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + kt * kGemmBK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (EPI == kEpiQKV) {
+        rb[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + kt * kGemmBK) : u32x4{0, 0, 0, 0};
+      } else {
+        rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + (int64_t)kt * g.rows * kDh);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][soff[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][1][soff[i]]) = rb[i];
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = g.K / kGemmBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const char* As = smem[buf][0];
+    const char* Bs = smem[buf][1];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      V8 af[4], bfr[4];
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+        af[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 16 + j, kc * 4 + gq));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 64 + tb * 16 + j, kc * 4 + gq));
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mfma16x16x32(af[fb], bfr[tb], acc[fb][tb]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // acc[fb][tb][r]: feature n0 + wn*64 + fb*16 + 4*gq + r of token m0 + wm*64 + tb*16 + j.
+  if (EPI == kEpiQKV) {
+    const int fbase = n0 + wn * 64;
+    const int blk = fbase / g.d;  // 0: q, 1: k, 2: v
+    const int h = (fbase - blk * g.d) / kDh;
+    if (blk < 2) {
+      const float* gam = (blk == 0 ? g.qg : g.kg) + h * kDh;
+      const float* bet = (blk == 0 ? g.qb : g.kb) + h * kDh;
+      float gm[4][4], bt[4][4];
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gm[fb][r] = gam[fb * 16 + 4 * gq + r];
+          bt[fb][r] = bet[fb * 16 + 4 * gq + r];
+        }
+      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)h * g.rows * kDh;
+      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
+      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
+      float kmx = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int64_t w = m0 + wm * 64 + tb * 16 + j;
+        const int64_t src = g.map.src(w);
+        float s1 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s1 += acc[fb][tb][r];
+        const float mean = sum_across_groups(s1) * (1.f / kDh);
+        float s2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dv = acc[fb][tb][r] - mean;
+            s2 = fmaf(dv, dv, s2);
+          }
+        const float var = sum_across_groups(s2) * (1.f / kDh);
+        const float rstd = 1.f / sqrtf(var + g.eps);
+        float y[4][4];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
+        if (src >= 0) {
+          const int t = (int)(src % g.T);
+          if (t >= kSpecial) {
+            const int pidx = t - kSpecial;
+            const int pr = pidx / g.gw + g.off, pc = pidx % g.gw + g.off;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * gq + r;
+              const float2 cr = g.rope[pr * 16 + i], cc = g.rope[pc * 16 + i];
+              float a = y[0][r], b = y[1][r];
+              y[0][r] = a * cr.x - b * cr.y;
+              y[1][r] = b * cr.x + a * cr.y;
+              a = y[2][r];
+              b = y[3][r];
+              y[2][r] = a * cc.x - b * cc.y;
+              y[3][r] = b * cc.x + a * cc.y;
+            }
+          }
+        }
+        float n2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+          f16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            o[r] = (f16)(y[fb][r] * oscale);
+            const float back = (float)o[r];
+            n2 = fmaf(back, back, n2);
+          }
+          *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 16 + 4 * gq) = o;
+        }
+        n2 = sum_across_groups(n2);
+        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
+      }
+      if (blk == 1) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[h], kmx);
+      }
+    } else {
+      const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+      f16* dst = g.vt + (int64_t)h * kDh * g.rows;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int64_t w = m0 + wm * 64 + tb * 16 + j;
+        // Key position inside its aligned group of 32: key 16a + 4c + b is
+        // stored at 8c + 4a + b, the order in which the attention kernel's
+        // MFMA consumes probabilities (see attention.hip).
+        const int64_t pos = (w & ~(int64_t)31) | (((w >> 2) & 3) << 3) | (((w >> 4) & 1) << 2) | (w & 3);
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = fb * 16 + 4 * gq + r;
+            dst[(int64_t)e * g.rows + pos] = (f16)ldexpf(acc[fb][tb][r], kv);
+          }
+      }
+    }
+  } else {
+    const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+    const int ws = range_exponent(g.sc->woabs);
+    const float scale = ldexpf(1.f, -(kv + ws));
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int64_t w = m0 + wm * 64 + tb * 16 + j;
+      const int64_t src = g.map.src(w);
+      if (src < 0) continue;
+      bf16* dst = g.y + src * g.d + n0 + wn * 64 + 4 * gq;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][r] * scale);
+        *reinterpret_cast<bf16x4*>(dst + fb * 16) = o;
+      }
+    }
+  }
+}
+
+static GemmArgs base_args(const Plan& p, const Ptrs& a) {
+  GemmArgs g{};
+  g.rows = p.rows;
+  g.map = p.map;
+  g.T = p.T;
+  g.gw = p.gw;
+  g.off = p.off;
+  g.d = p.d;
+  g.eps = p.eps;
+  g.qg = a.qg;
+  g.qb = a.qb;
+  g.kg = a.kg;
+  g.kb = a.kb;
+  g.rope = ws_rope(p, a);
+  g.sc = ws_scalars(p, a);
+  g.q = ws_q(p, a);
+  g.k = ws_k(p, a);
+  g.vt = ws_v(p, a);
+  g.y = a.Y;
+  return g;
+}
+
+hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
+  GemmArgs g = base_args(p, a);
+  g.A = a.Wqkv;
+  g.B = a.X;
+  g.Nf = 3 * p.d;
+  g.K = p.d;
+  const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
+  hipLaunchKernelGGL(gemm_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st);
+
+hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
+  GemmArgs g = base_args(p, a);
+  g.A = ws_wo(p, a);
+  g.B = ws_q(p, a);  // the attention kernel leaves O in place of q
+  g.Nf = p.d;
+  g.K = p.d;
+  const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
+  hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.mode == VGGT_ATTN_MODE_REGISTER && a.Y != a.X) return launch_patch_copy(p, a, st);
+  return hipSuccess;
+}
+
+}  // namespace vggt

@@ -1,0 +1,129 @@
+// Prep-stage kernels (all HBM-bound and small next to the GEMMs and the
+// attention core):
+//   * clear the workspace scalars and tabulate cos/sin of the 2D RoPE angles;
+//   * range bounds: max L2 norm of the X rows of the attention set(s), of the
+//     V rows of Wqkv, and max |Wo| -- they pick exact power-of-two scales that
+//     keep V, O and Wo inside fp16 range for the attention and output kernels;
+//   * an fp16 copy of Wo scaled by 2^s (the output GEMM runs on fp16 MFMA);
+//   * the register-mode patch-row copy Y = X.
+#include "plan.h"
+
+namespace vggt {
+
+// RoPE table entry (pos, i) = (cos, sin)(pos * base^(-i/16)) for the 16
+// frequencies of a 32-feature half of a 64-wide head; angles in double.
+__global__ void prep_kernel(float* scal, int nscal, float2* rope, int npos, float base) {
+  for (int i = threadIdx.x; i < nscal; i += blockDim.x) scal[i] = 0.f;
+  for (int i = threadIdx.x; i < npos * 16; i += blockDim.x) {
+    int pos = i >> 4, f = i & 15;
+    double theta = pow((double)base, -(double)f / 16.0);
+    double sn, cs;
+    sincos((double)pos * theta, &sn, &cs);
+    rope[i] = make_float2((float)cs, (float)sn);
+  }
+}
+
+// One wave per row: max over rows of the L2 norm of a bf16 row of `len`
+// elements (len a multiple of 8).  Rows are workspace rows mapped through
+// `map`; unmapped rows are skipped.
+__global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int64_t nrows,
+                                                          int len, RowMap map, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  float best = 0.f;
+  for (int64_t w = wave; w < nrows; w += nwaves) {
+    int64_t src = map.src(w);
+    if (src < 0) continue;
+    const bf16* row = base + src * len;
+    float acc = 0.f;
+    for (int c = lane * 8; c < len; c += 512) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float f = (float)v[e];
+        acc = fmaf(f, f, acc);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    best = fmaxf(best, sqrtf(acc));
+  }
+  if (lane == 0 && best > 0.f) atomic_max_nonneg(out, best);
+}
+
+__global__ __launch_bounds__(256) void absmax_kernel(const bf16* x, int64_t n8, float* out) {
+  float best = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    bf16x8 v = reinterpret_cast<const bf16x8*>(x)[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) best = fmaxf(best, fabsf((float)v[e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
+  if ((threadIdx.x & 63) == 0 && best > 0.f) atomic_max_nonneg(out, best);
+}
+
+// Wo (bf16) -> fp16 * 2^s with s chosen from max|Wo| so the largest entry
+// lands near 2^14; exact for every entry within 2^-24 of the largest.
+__global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t n8,
+                                                         const Scalars* sc, f16* out) {
+  const int s = range_exponent(sc->woabs);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    bf16x8 v = reinterpret_cast<const bf16x8*>(wo)[i];
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16)ldexpf((float)v[e], s);
+    reinterpret_cast<f16x8*>(out)[i] = o;
+  }
+}
+
+// Register mode, Y != X: copy the patch rows (tokens 17..T-1) of every frame.
+__global__ __launch_bounds__(256) void patch_copy_kernel(const bf16* X, bf16* Y, int S,
+                                                         int64_t frame_elems, int64_t skip_elems) {
+  const int64_t per = (frame_elems - skip_elems) / 8;  // 16-byte chunks per frame
+  const int64_t total = per * S;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / per, c = i - s * per;
+    int64_t off = s * frame_elems + skip_elems + c * 8;
+    *reinterpret_cast<u32x4*>(Y + off) = *reinterpret_cast<const u32x4*>(X + off);
+  }
+}
+
+static int grid_for(int64_t work, int per_block, int cap) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)(g > cap ? cap : g);
+}
+
+hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
+  Scalars* sc = ws_scalars(p, a);
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(sc),
+                     4 + p.H, ws_rope(p, a), p.rope_npos, p.base);
+  // X rows of the set(s): walk the workspace rows through the row map.
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 4, 4096)), dim3(256), 0, st,
+                     a.X, p.rows, p.d, p.map, &sc->xnorm);
+  RowMap ident{INT64_MAX / 2, 0, p.d, 1};
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 4, 4096)), dim3(256), 0, st,
+                     a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
+  const int64_t n8 = (int64_t)p.d * p.d / 8;
+  hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 256, 1024)), dim3(256), 0, st, a.Wo, n8,
+                     &sc->woabs);
+  hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
+                     n8, (const Scalars*)sc, ws_wo(p, a));
+  return hipGetLastError();
+}
+
+hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st) {
+  if (p.T <= kSpecial) return hipSuccess;
+  const int64_t frame = (int64_t)p.T * p.d, skip = (int64_t)kSpecial * p.d;
+  const int64_t work = (frame - skip) / 8 * p.S;
+  hipLaunchKernelGGL(patch_copy_kernel, dim3(grid_for(work, 256, 8192)), dim3(256), 0, st, a.X,
+                     a.Y, p.S, frame, skip);
+  return hipGetLastError();
+}
+
+}  // namespace vggt
