@@ -1,6 +1,7 @@
 // C ABI of libvggtattn: argument checks, planning and stage dispatch.  Every
 // check runs before the first HIP call, so a rejected call launches nothing.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "plan.h"
@@ -42,22 +43,25 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
     p->L = (int)N;
     p->seq_stride = round_up(N, kAttnBK);
     cover = p->seq_stride;
-    p->attn_qb = 4;
-    p->attn_waves = 4;
+    p->attn_qb = 2;
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->nseq = s->S;
     p->L = s->T;
     p->seq_stride = round_up(s->T, kAttnBK);
     cover = p->seq_stride * s->S;
-    p->attn_qb = 2;
-    p->attn_waves = 4;
+    p->attn_qb = 1;
   } else {
     p->nseq = 1;
     p->L = (int)R;
     p->seq_stride = round_up(R, kAttnBK);
     cover = p->seq_stride;
-    p->attn_qb = 4;
-    p->attn_waves = 4;
+    p->attn_qb = 1;
+  }
+  // Tuning override of the attention tile: VGGT_ATTN_QB = 1 or 2 query
+  // blocks of 32 per wave (128 or 256 queries per workgroup).
+  if (const char* e = getenv("VGGT_ATTN_QB")) {
+    const int q = atoi(e);
+    if (q == 1 || q == 2) p->attn_qb = q;
   }
   p->rows = round_up(cover, kRowAlign);
   if (mode == VGGT_ATTN_MODE_GLOBAL) {

@@ -1,129 +1,306 @@
 // Attention core on gfx950: O = softmax(q k^T / sqrt(Dh)) v for every
-// (attention set, head), Dh = 64, no mask inside a set.  One kernel serves the
-// per-frame sets (S sets of T tokens), the global set (S*T tokens) and the
+// (attention set, head), Dh = 64, no mask inside a set.  The same code serves
+// the per-frame sets (S sets of T tokens), the global set (S*T tokens) and the
 // register set (17*S tokens): a set is just a run of workspace rows.
 //
-// Work split: a workgroup owns BQ = NW*QB*16 query rows of one (set, head)
-// and streams that set's keys/values through LDS in 64-key tiles (double
-// buffered through registers, one barrier per tile).  Each wave keeps its
-// QB*16 queries in registers and runs two MFMA 16x16x32 fp16 products per
-// tile, both computed transposed so no data moves between lanes:
-//   S^T[key, query] = K[key, :] . Q[query, :]      (A = K tile, B = Q)
-//   O^T[feat, query] += V^T[feat, key] . P^T[key, query]  (A = V^T tile, B = P)
-// With this orientation a lane holds one query column and, per 16-key block,
-// keys 4*(lane/16) + 0..3.  Two adjacent key blocks give a lane the 8
-// probabilities its B operand needs for a 32-key step, in the order
-// (4c+0..3, 16+4c+0..3); the QKV kernel stores v^T with that same order inside
-// every aligned group of 32 keys, so the PV product is exact.
+// MFMA layout.  Each wave keeps QB*32 queries in registers and per 64-key tile
+// runs two MFMA 32x32x16 fp16 products, both computed transposed so no data
+// moves between lanes:
+//   S^T[key, query] = K[key, :] . Q[query, :]            (A = K tile, B = Q)
+//   O^T[feat, query] += V^T[feat, key] . P^T[key, query] (A = V^T tile, B = P)
+// With this orientation lane l holds query column l%32 and, per 32-key block,
+// keys 8*(r/4) + 4*(l/32) + r%4 (r = 0..15).  Eight consecutive accumulator
+// registers then hold exactly the 8 probabilities the lane's B operand needs
+// for a 16-key step, in the order (4h+0..3, 8+4h+0..3) with h = l/32; the QKV
+// kernel stores v^T with that same order inside every aligned group of 16
+// keys (key bits 2 and 3 swapped), so the PV product is exact.  (32x32x16
+// rather than 16x16x32: on gfx950 the smaller MFMA holds the VALU issue port
+// for a larger share of its run time, which the exp2 stream cannot spare.)
 //
-// Softmax (base 2: q carries log2(e)/sqrt(Dh)): an online softmax with a
-// per-query reference m.  Logits come out of the MFMA already shifted
-// (accumulator initialised to -m).  A tile's row max is taken with one
-// in-lane max and two cross-lane steps; m is only moved when a logit exceeds
-// m + kTau, so P = 2^(s-m) <= 2^kTau always fits fp16 and O and the row sum
-// are rescaled rarely.  Once m >= bound - kTauSkip, where bound =
-// |q| * max|k| >= every logit (Cauchy-Schwarz on the LayerNorm-ed vectors),
-// no later logit can push P past 2^kTauSkip and the max is no longer taken.
-// The row sum accumulates the fp16-rounded probabilities with v_dot2
-// (the same values the PV MFMA consumes).
+// Softmax (base 2: q carries log2(e)/sqrt(Dh)): online softmax with a
+// per-query reference m; logits leave the MFMA already shifted (the
+// accumulator starts at -m) and P = 2^(s-m) goes to fp16.  Two facts keep the max
+// out of the steady state:
+//   * bound = |q| * max_k |k| >= every logit of the row (Cauchy-Schwarz on
+//     the LayerNorm-ed, rotated vectors), known before the first tile;
+//   * fp16 holds P <= 2^15 without overflow and keeps full relative precision
+//     for P >= 2^-14.
+// The first tile takes the row max m0.  If bound - m0 <= 29, the reference is
+// pinned at max(m0, bound - 15): no later logit can push P above 2^15, and the
+// largest term of the row (>= m0) stays >= 2^-14, so the row is "settled" and
+// its max is never taken again.  Rows that are not settled (very peaked rows
+// whose first tile is far below the bound) keep an ordinary online max with
+// lazy rescaling (only when a logit exceeds m + 8) and re-check the settle
+// condition after each tile.  The row sum accumulates the fp16-rounded
+// probabilities with v_dot2 (the same values the PV MFMA consumes).
+//
+// One kernel, attn_kernel: 4 waves and QB*128 queries per workgroup, two
+// workgroups per CU.  Measured alternatives that did not pay on gfx950: an
+// 8-wave "ping-pong" split (waves sharing a SIMD alternating MFMA and softmax
+// phases between barriers), 16x16x32 MFMAs, direct global->LDS loads three
+// buffers deep, and 128 queries per wave at one wave per SIMD (spills).  With
+// random fp16 operands this loop is power-bound: the shader clock settles near
+// 1.9 GHz, so lowering the energy per FLOP matters as much as issue slots.
 #include "plan.h"
 
 namespace vggt {
 
-constexpr float kTau = 8.f;       // rescale when a logit exceeds m + kTau
-constexpr float kTauSkip = 15.f;  // stop tracking the max once bound - m <= kTauSkip
+constexpr float kTau = 8.f;        // unsettled rows: rescale when a logit exceeds m + kTau
+constexpr float kPinBelow = 15.f;  // settled rows: reference pinned at bound - kPinBelow (P <= 2^15)
+constexpr float kSettleGap = 29.f; // settle once bound - m <= kSettleGap (top term stays >= 2^-14)
 
 struct AttnArgs {
   f16* q;            // [H][rows][64] scaled queries; overwritten with O
   const f16* k;      // [H][rows][64]
-  const f16* vt;     // [H][64][rows], keys permuted inside aligned 32-groups
+  const f16* vt;     // [H][64][rows], keys permuted inside aligned 16-groups
   int64_t rows;
   int64_t seq_stride;
   int nseq, L, H, qtiles;
   const Scalars* sc;
 };
 
+// LDS tiles are 64 rows x 128 bytes.  The MFMA operand reads take one
+// 16-byte chunk from each of 32 consecutive rows; XOR-ing the chunk index
+// with row bits 0..2 and bit 3 spreads such a read over all banks (measured
+// on gfx950: 5.2 cycles per ds_read_b128 per CU, against 8.8 with bits 0..2
+// alone).
 __device__ __forceinline__ int lds_swz(int row, int col) {
-  return row * 128 + ((col ^ (row & 7)) << 4);
+  return row * 128 + ((col ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
 }
 
-template <int QB, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
-  constexpr int BQ = NW * QB * 16;
-  constexpr int NT = NW * 64;
-  constexpr int CH = (2 * 512) / NT;  // 16-byte chunks per thread per K+V tile
+// Softmax state of the QB*32 query rows one wave owns (lane: row l%32 of
+// each 32-row block, half h = l/32 of the keys / features).
+template <int QB>
+struct Rows {
+  f16x8 qf[QB][4];   // B operand of S^T: q[row][16*dc + 8*h .. +7]
+  float bound[QB];   // upper bound of every logit of the row (-inf: no row)
+  float m[QB];       // reference the logits are taken relative to
+  float l[QB];       // partial row sum (this lane's keys)
+  f32x16 O[2][QB];   // O^T[32*db + 8*(r/4) + 4*h + r%4][row]
+  bool track;        // wave-uniform: some row is not settled yet
+};
+
+__device__ __forceinline__ f32x16 splat16(float v) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = v;
+  return r;
+}
+
+template <int QB>
+__device__ __forceinline__ void rows_init(Rows<QB>& R, const f16* qh, int64_t seq0, int qloc0,
+                                          int L, int j, int h, float kmax) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qloc0 + qb * 32 + j;
+    const bool ok = row < L;
+    float n2 = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      if (ok) {
+        R.qf[qb][dc] = *reinterpret_cast<const f16x8*>(qh + (seq0 + row) * kDh + dc * 16 + h * 8);
+      } else {
+        R.qf[qb][dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)R.qf[qb][dc][e];
+        n2 = fmaf(f, f, n2);
+      }
+    }
+    n2 += __shfl_xor(n2, 32);
+    // 2^-10 relative margin covers the fp32 rounding of norms and dot products.
+    R.bound[qb] = ok ? sqrtf(n2) * kmax * (1.f + 0x1p-10f) : -INFINITY;
+    R.m[qb] = 0.f;
+    R.l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) R.O[db][qb] = splat16(0.f);
+  }
+  R.track = true;
+}
+
+// S^T = K Q^T - m for one 64-key tile in LDS.  MASK: keys at or beyond
+// `valid` (the last tile of a set) start from -inf instead of -m, so their
+// probability is exactly 0.
+template <int QB, bool MASK>
+__device__ __forceinline__ void tile_qk(const Rows<QB>& R, const char* Ks, int j, int h, int valid,
+                                        f32x16 (&S)[2][QB]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f16x8 kf[4];
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc)
+      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + lds_swz(kb * 32 + j, dc * 2 + h));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 c = splat16(-R.m[qb]);
+      if (MASK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          c[r] = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= valid ? -INFINITY : c[r];
+      }
+      S[kb][qb] = mfma32x32x16(kf[0], R.qf[qb][0], c);
+#pragma unroll
+      for (int dc = 1; dc < 4; ++dc) S[kb][qb] = mfma32x32x16(kf[dc], R.qf[qb][dc], S[kb][qb]);
+    }
+  }
+}
+
+template <int QB>
+__device__ __forceinline__ void tile_qk_any(const Rows<QB>& R, const char* Ks, int j, int h,
+                                            bool last, int last_valid, f32x16 (&S)[2][QB]) {
+  if (last && last_valid < 64) tile_qk<QB, true>(R, Ks, j, h, last_valid, S);
+  else tile_qk<QB, false>(R, Ks, j, h, 64, S);
+}
+
+// Softmax of one tile: on the first tile, or while a row is unsettled, take
+// the row max and move / pin the reference; then P = 2^S in fp16 and the row
+// sums.  pf[qb][c] is the B operand of the PV product for keys 16c..16c+15.
+template <int QB>
+__device__ __forceinline__ void tile_softmax(Rows<QB>& R, f32x16 (&S)[2][QB], f16x8 (&pf)[QB][4],
+                                             bool first) {
+  if (first || R.track) {
+    bool unsettled = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mt = S[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(S[kb][qb][r], S[kb][qb][r + 1]));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));  // row max of this tile, relative to m (m = 0 before the first)
+      // new reference: the observed max (first tile, or a jump past kTau) ...
+      float mn = (first || mt > kTau) ? R.m[qb] + mt : R.m[qb];
+      // ... pinned just under the bound once the bound leaves fp16 room.
+      const bool settled = mn >= R.bound[qb] - kSettleGap;
+      if (settled) mn = fmaxf(mn, R.bound[qb] - kPinBelow);
+      unsettled = unsettled || !settled;
+      const float dl = mn - R.m[qb];
+      if (dl != 0.f) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[kb][qb][r] -= dl;
+        // O and l are still zero before the first tile: leave them alone
+        // (2^-dl may not even be finite there).
+        const float al = first ? 1.f : __builtin_amdgcn_exp2f(-dl);
+        R.l[qb] *= al;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) R.O[db][qb][r] *= al;
+      }
+      R.m[qb] = mn;
+    }
+    R.track = __ballot(unsettled) != 0;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f16x8 v;
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const f32x2 e2 = {__builtin_amdgcn_exp2f(S[c >> 1][qb][8 * (c & 1) + r]),
+                          __builtin_amdgcn_exp2f(S[c >> 1][qb][8 * (c & 1) + r + 1])};
+        const f16x2 h2 = __builtin_convertvector(e2, f16x2);
+        v[r] = h2[0];
+        v[r + 1] = h2[1];
+        R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
+      }
+      pf[qb][c] = v;
+    }
+}
+
+// O^T += V^T P^T for one tile in LDS.
+template <int QB>
+__device__ __forceinline__ void tile_pv(Rows<QB>& R, const char* Vs, const f16x8 (&pf)[QB][4],
+                                        int j, int h) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + lds_swz(db * 32 + j, c * 2 + h));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) R.O[db][qb] = mfma32x32x16(vf, pf[qb][c], R.O[db][qb]);
+    }
+}
+
+// Normalise and store O in place of q, valid rows only.
+template <int QB>
+__device__ __forceinline__ void rows_store(const Rows<QB>& R, f16* qh, int64_t seq0, int qloc0,
+                                           int L, int j, int h) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = R.l[qb] + __shfl_xor(R.l[qb], 32);
+    const float inv = 1.f / lt;
+    const int row = qloc0 + qb * 32 + j;
+    if (row < L) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          f16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (f16)(R.O[db][qb][4 * rq + r] * inv);
+          *reinterpret_cast<f16x4*>(qh + (seq0 + row) * kDh + db * 32 + 8 * rq + 4 * h) = o;
+        }
+    }
+  }
+}
+
+struct BlockCoord {
+  int h, s, qt;
+};
+__device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  BlockCoord c;
+  c.qt = logical % p.qtiles;
+  const int t2 = logical / p.qtiles;
+  c.h = t2 % p.H;
+  c.s = t2 / p.H;
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// 4-wave kernel
+// ---------------------------------------------------------------------------
+// K / V^T tiles are double buffered in LDS and fetched one tile ahead through
+// registers (global_load -> ds_write after the tile's compute), with one
+// workgroup barrier per tile; two workgroups per CU.
+template <int QB>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
+  constexpr int BQ = 4 * QB * 32;
   __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, gq = lane >> 4;
+  const int j = lane & 31, h = lane >> 5;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = logical % p.qtiles;
-  const int t2 = logical / p.qtiles;
-  const int h = t2 % p.H;
-  const int s = t2 / p.H;
-  const int64_t seq0 = (int64_t)s * p.seq_stride;
+  const BlockCoord bc = block_coord(p);
+  const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int L = p.L;
-  const int qloc0 = qt * BQ + wave * QB * 16;
-  const bool wave_active = qloc0 < L;
+  const int qloc0 = bc.qt * BQ + wave * QB * 32;
+  const bool active = __builtin_amdgcn_readfirstlane(qloc0) < L;
+  f16* qh = p.q + (int64_t)bc.h * p.rows * kDh;
+  const f16* kh = p.k + (int64_t)bc.h * p.rows * kDh;
+  const f16* vh = p.vt + (int64_t)bc.h * kDh * p.rows;
 
-  f16* qh = p.q + (int64_t)h * p.rows * kDh;
-  const f16* kh = p.k + (int64_t)h * p.rows * kDh;
-  const f16* vh = p.vt + (int64_t)h * kDh * p.rows;
-
-  // ---- queries of this wave (B operand of S^T), their norms and bounds
-  f16x8 qf[QB][2];
-  float bound[QB];
-  const float kmax = p.sc->kmax[h];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qloc0 + qb * 16 + j;
-    const bool ok = row < L;
-    float n2 = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < 2; ++dc) {
-      if (ok) {
-        qf[qb][dc] = *reinterpret_cast<const f16x8*>(qh + (seq0 + row) * kDh + dc * 32 + gq * 8);
-      } else {
-        qf[qb][dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)qf[qb][dc][e];
-        n2 = fmaf(f, f, n2);
-      }
-    }
-    n2 = sum_across_groups(n2);
-    // 2^-10 relative margin covers the fp32 rounding of norms and dot products.
-    bound[qb] = ok ? sqrtf(n2) * kmax * (1.f + 0x1p-10f) : -INFINITY;
-  }
-
-  float m[QB], l[QB];
-  f32x4 negm[QB];
-  f32x4 O[4][QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = 0.f;
-    l[qb] = 0.f;
-    negm[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 4; ++db) O[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bool track = true;
+  Rows<QB> R;
+  rows_init<QB>(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
 
   const int ntiles = (L + 63) / 64;
   const int last_valid = L - 64 * (ntiles - 1);
 
-  // ---- K / V^T tile loader: chunk c < 512 is K (row c>>3, 16B col c&7),
-  // chunk c >= 512 is V^T (feature row, 16B col).
-  u32x4 rg[CH];
-  int soff[CH];
-  const f16* gsrc[CH];
-  int64_t gstep[CH];
+  // 1024 16-byte chunks per K+V tile, 4 per thread: chunk c < 512 is K (row
+  // c>>3, col c&7), chunk c >= 512 is V^T (feature row, col).
+  u32x4 rg[4];
+  int soff[4];
+  const f16* gsrc[4];
+  int64_t gstep[4];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = tid + NT * i;
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
     const int cc = c & 511, row = cc >> 3, col = cc & 7;
     soff[i] = (c >> 9) * (64 * 128) + lds_swz(row, col);
     if (c < 512) {
@@ -136,145 +313,44 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   }
   auto gload = [&](int tile) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < 4; ++i)
       rg[i] = *reinterpret_cast<const u32x4*>(gsrc[i] + (int64_t)tile * gstep[i]);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      *reinterpret_cast<u32x4*>(&smem[buf][0][0] + soff[i]) = rg[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][0] + soff[i]) = rg[i];
   };
 
+  f32x16 S[2][QB];
+  f16x8 pf[QB][4];
   gload(0);
   sstore(0);
   __syncthreads();
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntiles) gload(tile + 1);
-
-    if (wave_active) {
-      const char* Ks = smem[buf][0];
-      const char* Vs = smem[buf][1];
-      // ---- S^T = K Q^T - m
-      f32x4 S[4][QB];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f16x8 k0 = *reinterpret_cast<const f16x8*>(Ks + lds_swz(kb * 16 + j, gq));
-        const f16x8 k1 = *reinterpret_cast<const f16x8*>(Ks + lds_swz(kb * 16 + j, 4 + gq));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          S[kb][qb] = mfma16x16x32(k0, qf[qb][0], negm[qb]);
-          S[kb][qb] = mfma16x16x32(k1, qf[qb][1], S[kb][qb]);
-        }
-      }
-      if (tile == ntiles - 1 && last_valid < 64) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb * 16 + 4 * gq + r >= last_valid) {
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb) S[kb][qb][r] = -INFINITY;
-            }
-      }
-      // ---- online max (first tile, then only while the bound leaves room)
-      if (tile == 0 || track) {
-        const bool first = tile == 0;
-        float delta[QB];
-        bool any = first;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float mt = fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3]));
-#pragma unroll
-          for (int kb = 1; kb < 4; ++kb)
-            mt = fmaxf(mt, fmaxf(fmaxf(S[kb][qb][0], S[kb][qb][1]), fmaxf(S[kb][qb][2], S[kb][qb][3])));
-          mt = max_across_groups(mt);
-          delta[qb] = first ? mt : (mt > kTau ? mt : 0.f);
-          any = any || (delta[qb] != 0.f);
-        }
-        if (__ballot(any)) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float dl = delta[qb];
-            m[qb] += dl;
-            negm[qb] = f32x4{-m[qb], -m[qb], -m[qb], -m[qb]};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) S[kb][qb][r] -= dl;
-            if (!first) {
-              const float al = __builtin_amdgcn_exp2f(-dl);
-              l[qb] *= al;
-#pragma unroll
-              for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) O[db][qb][r] *= al;
-            }
-          }
-        }
-        bool need = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) need = need || (m[qb] < bound[qb] - kTauSkip);
-        track = __ballot(need) != 0;
-      }
-      // ---- P = 2^S in fp16, row sums, O^T += V^T P^T
-      f16x8 pf[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f16x8 v;
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-              const f32x2 e2 = {__builtin_amdgcn_exp2f(S[2 * c + half][qb][r]),
-                                __builtin_amdgcn_exp2f(S[2 * c + half][qb][r + 1])};
-              const f16x2 h2 = __builtin_convertvector(e2, f16x2);
-              v[half * 4 + r] = h2[0];
-              v[half * 4 + r + 1] = h2[1];
-              l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, l[qb], false);
-            }
-          pf[qb][c] = v;
-        }
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + lds_swz(db * 16 + j, c * 4 + gq));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) O[db][qb] = mfma16x16x32(vf, pf[qb][c], O[db][qb]);
-        }
+  // all tiles but the last: no mask
+  for (int t = 0; t < ntiles - 1; ++t) {
+    const int buf = t & 1;
+    gload(t + 1);
+    if (active) {
+      tile_qk<QB, false>(R, smem[buf][0], j, h, 64, S);
+      tile_softmax<QB>(R, S, pf, t == 0);
+      tile_pv<QB>(R, smem[buf][1], pf, j, h);
     }
-
-    if (tile + 1 < ntiles) sstore(buf ^ 1);
+    sstore(buf ^ 1);
     __syncthreads();
   }
-
-  // ---- normalise and store O (in place of q), valid rows only
-  if (wave_active) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float lt = sum_across_groups(l[qb]);
-      const float inv = 1.f / lt;
-      const int row = qloc0 + qb * 16 + j;
-      if (row < L) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          f16x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (f16)(O[db][qb][r] * inv);
-          *reinterpret_cast<f16x4*>(qh + (seq0 + row) * kDh + db * 16 + 4 * gq) = o;
-        }
-      }
-    }
+  // last tile: keys past the end of the set masked
+  if (active) {
+    const int buf = (ntiles - 1) & 1;
+    tile_qk<QB, true>(R, smem[buf][0], j, h, last_valid, S);
+    tile_softmax<QB>(R, S, pf, ntiles == 1);
+    tile_pv<QB>(R, smem[buf][1], pf, j, h);
   }
+  if (active) rows_store<QB>(R, qh, seq0, qloc0, L, j, h);
 }
 
-template <int QB, int NW>
+template <int QB>
 static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
-  constexpr int BQ = NW * QB * 16;
+  constexpr int BQ = 4 * QB * 32;
   AttnArgs g;
   g.q = ws_q(p, a);
   g.k = ws_k(p, a);
@@ -287,13 +363,13 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.qtiles = (p.L + BQ - 1) / BQ;
   g.sc = ws_scalars(p, a);
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
-  hipLaunchKernelGGL((attn_kernel<QB, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, g);
+  hipLaunchKernelGGL((attn_kernel<QB>), dim3((unsigned)blocks), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_core(const Plan& p, const Ptrs& a, hipStream_t st) {
-  if (p.attn_qb == 4 && p.attn_waves == 4) return launch_attn_t<4, 4>(p, a, st);
-  if (p.attn_qb == 2 && p.attn_waves == 4) return launch_attn_t<2, 4>(p, a, st);
+  if (p.attn_qb == 2) return launch_attn_t<2>(p, a, st);
+  if (p.attn_qb == 1) return launch_attn_t<1>(p, a, st);
   return hipErrorInvalidValue;
 }
 

@@ -232,10 +232,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int64_t w = m0 + wm * 64 + tb * 16 + j;
-        // Key position inside its aligned group of 32: key 16a + 4c + b is
-        // stored at 8c + 4a + b, the order in which the attention kernel's
-        // MFMA consumes probabilities (see attention.hip).
-        const int64_t pos = (w & ~(int64_t)31) | (((w >> 2) & 3) << 3) | (((w >> 4) & 1) << 2) | (w & 3);
+        // Key position inside its aligned group of 16: key 8a + 4c + b is
+        // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
+        // the attention kernel's MFMA consumes probabilities.
+        const int64_t pos = (w & ~(int64_t)15) | (((w >> 2) & 1) << 3) | (((w >> 3) & 1) << 2) | (w & 3);
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll

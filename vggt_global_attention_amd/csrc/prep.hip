@@ -23,33 +23,49 @@ __global__ void prep_kernel(float* scal, int nscal, float2* rope, int npos, floa
   }
 }
 
-// One wave per row: max over rows of the L2 norm of a bf16 row of `len`
-// elements (len a multiple of 8).  Rows are workspace rows mapped through
-// `map`; unmapped rows are skipped.
+// Max over rows of the L2 norm of a bf16 row of `len` elements (len a
+// multiple of 8).  Rows are workspace rows mapped through `map`; unmapped
+// rows are skipped.  Each wave walks rows w, w + nwaves, ... (four at a time,
+// loads issued together); the workgroup reduces in LDS and issues a single
+// atomic.
 __global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int64_t nrows,
                                                           int len, RowMap map, float* out) {
+  __shared__ float red[4];
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   float best = 0.f;
-  for (int64_t w = wave; w < nrows; w += nwaves) {
-    int64_t src = map.src(w);
-    if (src < 0) continue;
-    const bf16* row = base + src * len;
-    float acc = 0.f;
-    for (int c = lane * 8; c < len; c += 512) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+  for (int64_t w0 = wave; w0 < nrows; w0 += 4 * nwaves) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float f = (float)v[e];
-        acc = fmaf(f, f, acc);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t w = w0 + u * nwaves;
+      const int64_t src = w < nrows ? map.src(w) : -1;
+      if (src < 0) continue;
+      const bf16* row = base + src * len;
+      for (int c = lane * 8; c < len; c += 512) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)v[e];
+          acc[u] = fmaf(f, f, acc[u]);
+        }
       }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    best = fmaxf(best, sqrtf(acc));
+    for (int u = 0; u < 4; ++u) {
+      float a = acc[u];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+      best = fmaxf(best, sqrtf(a));
+    }
   }
-  if (lane == 0 && best > 0.f) atomic_max_nonneg(out, best);
+  if (lane == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (m > 0.f) atomic_max_nonneg(out, m);
+  }
 }
 
 __global__ __launch_bounds__(256) void absmax_kernel(const bf16* x, int64_t n8, float* out) {
@@ -104,10 +120,10 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(sc),
                      4 + p.H, ws_rope(p, a), p.rope_npos, p.base);
   // X rows of the set(s): walk the workspace rows through the row map.
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 4, 4096)), dim3(256), 0, st,
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 16, 2048)), dim3(256), 0, st,
                      a.X, p.rows, p.d, p.map, &sc->xnorm);
   RowMap ident{INT64_MAX / 2, 0, p.d, 1};
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 4, 4096)), dim3(256), 0, st,
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 16, 2048)), dim3(256), 0, st,
                      a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
   const int64_t n8 = (int64_t)p.d * p.d / 8;
   hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 256, 1024)), dim3(256), 0, st, a.Wo, n8,
