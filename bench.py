@@ -20,6 +20,7 @@ Inputs are seeded synthetic data (X ~ N(0,1), weights ~ N(0,1/d), gamma ~
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,30 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "global-attention ms/layer + TFLOP/s (frac of bf16 MFMA peak) at S frames, 1 GPU"
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_kernel_s100_global_hbm_bytes.md")
+
+
+def attention_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attention.hip", "common.h"):
+        with open(os.path.join(ROOT, "vggt_global_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the attention sources changed since the counters were taken."""
+    try:
+        kv = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
+                  if line.startswith(("traffic_bytes_per_launch:", "attention_source_sha256_16:")))
+    except OSError:
+        return None
+    if kv.get("attention_source_sha256_16", "").strip() != attention_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -45,6 +70,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -152,6 +179,16 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     B.lib()  # fails loudly without the HIP library
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n,
+                          "bytes_written_per_copy": n, "copies": 3}))
+        return
     w = configs.WORKLOADS[a.workload]
     print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
     inp, d = gpu_inputs(w)
@@ -186,7 +223,9 @@ def main():
         "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (attention core)",
                      "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_MFMA_TFLOPS,
+                     "traffic": recorded_traffic() if (a.workload, a.mode) == ("s100", "global") else None,
+                     "traffic_unit": "bytes per launch (FETCH_SIZE*2.0 + WRITE_SIZE*1.0)",
                      "flop_per_launch": attn_flop, "ms_per_launch": core_ms},
     }
     if not a.no_extra and a.workload == "s100":

@@ -10,7 +10,7 @@
  *     LayerNorm-ed over the Dh features of each head (biased variance, eps =
  *     ln_eps) with a per-head affine (gamma, beta) -- the page's "use_qk_norm"
  *     (section 三); then patch tokens get a 2D rotary encoding (section 三, and
- *     the HTTM article's RoPE analysis, figures 4-5): the first Dh/2 features
+ *     the HTTM article, section 04, RoPE-effect paragraph): the first Dh/2 features
  *     turn with the grid row + pos_offset, the last Dh/2 with the grid column
  *     + pos_offset; feature i of a half pairs with feature i + Dh/4 and turns
  *     by pos * rope_base^(-i/(Dh/4)).  Camera and register tokens are not

@@ -26,9 +26,11 @@ What it computes (the plain definition, no tiling, no online softmax):
 * Q/K normalisation -- same page, section 三 ("use_qk_norm" is on).  Read as a
   LayerNorm over the Dh features of every (token, head), biased variance,
   followed by a per-head affine gamma/beta.
-* 2D RoPE -- same page, section 三 (frame block), and the HTTM article's RoPE
-  analysis (figures 4-5: every frame carries the same positional code, nothing
-  marks the frame index).  Read as: the first Dh/2 features are rotated by the
+* 2D RoPE -- same page, section 三 (frame block), and the HTTM article
+  ("HTTM: Head-wise Temporal Token Merging for Faster VGGT", 10100.com),
+  section 04, RoPE-effect paragraph around figure 3: the rotary code is
+  applied in every attention layer and identically in every frame, nothing
+  marks the frame index.  Read as: the first Dh/2 features are rotated by the
   patch's grid row, the last Dh/2 by its grid column; inside each half, feature
   i pairs with feature i + Dh/4 (rotate-half) and turns by pos * theta_i with
   theta_i = base ** (-i / (Dh/4)).  Special tokens are not rotated.  Applied to
