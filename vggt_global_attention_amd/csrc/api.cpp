@@ -44,24 +44,31 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
     p->seq_stride = round_up(N, kAttnBK);
     cover = p->seq_stride;
     p->attn_qb = 2;
+    p->attn_waves = 8;
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->nseq = s->S;
     p->L = s->T;
     p->seq_stride = round_up(s->T, kAttnBK);
     cover = p->seq_stride * s->S;
     p->attn_qb = 1;
+    p->attn_waves = 4;
   } else {
     p->nseq = 1;
     p->L = (int)R;
     p->seq_stride = round_up(R, kAttnBK);
     cover = p->seq_stride;
     p->attn_qb = 1;
+    p->attn_waves = 4;
   }
   // Tuning override of the attention tile: VGGT_ATTN_QB = 1 or 2 query
-  // blocks of 32 per wave (128 or 256 queries per workgroup).
+  // blocks of 32 per wave, VGGT_ATTN_WAVES = 4 or 8 waves per workgroup.
   if (const char* e = getenv("VGGT_ATTN_QB")) {
     const int q = atoi(e);
     if (q == 1 || q == 2) p->attn_qb = q;
+  }
+  if (const char* e = getenv("VGGT_ATTN_WAVES")) {
+    const int w = atoi(e);
+    if (w == 4 || w == 8) p->attn_waves = w;
   }
   p->rows = round_up(cover, kRowAlign);
   if (mode == VGGT_ATTN_MODE_GLOBAL) {

@@ -34,13 +34,16 @@
 // condition after each tile.  The row sum accumulates the fp16-rounded
 // probabilities with v_dot2 (the same values the PV MFMA consumes).
 //
-// One kernel, attn_kernel: 4 waves and QB*128 queries per workgroup, two
-// workgroups per CU.  Measured alternatives that did not pay on gfx950: an
-// 8-wave "ping-pong" split (waves sharing a SIMD alternating MFMA and softmax
-// phases between barriers), 16x16x32 MFMAs, direct global->LDS loads three
-// buffers deep, and 128 queries per wave at one wave per SIMD (spills).  With
-// random fp16 operands this loop is power-bound: the shader clock settles near
-// 1.9 GHz, so lowering the energy per FLOP matters as much as issue slots.
+// One kernel, attn_kernel<QB, NW>: NW waves and NW*QB*32 queries per
+// workgroup.  Global sets use 8 waves x 64 queries (512 queries share each
+// K/V tile, one workgroup per CU, the -m initialiser kept resident); frame and
+// register sets use 4 waves x 32 queries (small sets, ragged ends).  Measured
+// alternatives that did not pay on gfx950: an 8-wave "ping-pong" split (waves
+// sharing a SIMD alternating MFMA and softmax phases between barriers),
+// 16x16x32 MFMAs, direct global->LDS loads three buffers deep, and 128
+// queries per wave (spills).  With random fp16 operands this loop is
+// power-bound: the shader clock settles near 1.9 GHz, so lowering the energy
+// per FLOP (LDS bytes, non-MFMA instructions) matters as much as issue slots.
 #include "plan.h"
 
 namespace vggt {
@@ -70,12 +73,13 @@ __device__ __forceinline__ int lds_swz(int row, int col) {
 
 // Softmax state of the QB*32 query rows one wave owns (lane: row l%32 of
 // each 32-row block, half h = l/32 of the keys / features).
-template <int QB>
+template <int QB, bool RES>
 struct Rows {
   f16x8 qf[QB][4];   // B operand of S^T: q[row][16*dc + 8*h .. +7]
   float bound[QB];   // upper bound of every logit of the row (-inf: no row)
   float m[QB];       // reference the logits are taken relative to
   float l[QB];       // partial row sum (this lane's keys)
+  f32x16 negm[RES ? QB : 1];  // -m broadcast, kept resident when RES (else splat per tile)
   f32x16 O[2][QB];   // O^T[32*db + 8*(r/4) + 4*h + r%4][row]
   bool track;        // wave-uniform: some row is not settled yet
 };
@@ -87,8 +91,8 @@ __device__ __forceinline__ f32x16 splat16(float v) {
   return r;
 }
 
-template <int QB>
-__device__ __forceinline__ void rows_init(Rows<QB>& R, const f16* qh, int64_t seq0, int qloc0,
+template <int QB, bool RES>
+__device__ __forceinline__ void rows_init(Rows<QB, RES>& R, const f16* qh, int64_t seq0, int qloc0,
                                           int L, int j, int h, float kmax) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -113,6 +117,7 @@ __device__ __forceinline__ void rows_init(Rows<QB>& R, const f16* qh, int64_t se
     R.bound[qb] = ok ? sqrtf(n2) * kmax * (1.f + 0x1p-10f) : -INFINITY;
     R.m[qb] = 0.f;
     R.l[qb] = 0.f;
+    if (RES) R.negm[RES ? qb : 0] = splat16(0.f);
 #pragma unroll
     for (int db = 0; db < 2; ++db) R.O[db][qb] = splat16(0.f);
   }
@@ -122,9 +127,9 @@ __device__ __forceinline__ void rows_init(Rows<QB>& R, const f16* qh, int64_t se
 // S^T = K Q^T - m for one 64-key tile in LDS.  MASK: keys at or beyond
 // `valid` (the last tile of a set) start from -inf instead of -m, so their
 // probability is exactly 0.
-template <int QB, bool MASK>
-__device__ __forceinline__ void tile_qk(const Rows<QB>& R, const char* Ks, int j, int h, int valid,
-                                        f32x16 (&S)[2][QB]) {
+template <int QB, bool RES, bool MASK>
+__device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, int j, int h,
+                                        int valid, f32x16 (&S)[2][QB]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f16x8 kf[4];
@@ -133,7 +138,7 @@ __device__ __forceinline__ void tile_qk(const Rows<QB>& R, const char* Ks, int j
       kf[dc] = *reinterpret_cast<const f16x8*>(Ks + lds_swz(kb * 32 + j, dc * 2 + h));
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      f32x16 c = splat16(-R.m[qb]);
+      f32x16 c = RES ? R.negm[RES ? qb : 0] : splat16(-R.m[qb]);
       if (MASK) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -146,19 +151,19 @@ __device__ __forceinline__ void tile_qk(const Rows<QB>& R, const char* Ks, int j
   }
 }
 
-template <int QB>
-__device__ __forceinline__ void tile_qk_any(const Rows<QB>& R, const char* Ks, int j, int h,
+template <int QB, bool RES>
+__device__ __forceinline__ void tile_qk_any(const Rows<QB, RES>& R, const char* Ks, int j, int h,
                                             bool last, int last_valid, f32x16 (&S)[2][QB]) {
-  if (last && last_valid < 64) tile_qk<QB, true>(R, Ks, j, h, last_valid, S);
-  else tile_qk<QB, false>(R, Ks, j, h, 64, S);
+  if (last && last_valid < 64) tile_qk<QB, RES, true>(R, Ks, j, h, last_valid, S);
+  else tile_qk<QB, RES, false>(R, Ks, j, h, 64, S);
 }
 
 // Softmax of one tile: on the first tile, or while a row is unsettled, take
 // the row max and move / pin the reference; then P = 2^S in fp16 and the row
 // sums.  pf[qb][c] is the B operand of the PV product for keys 16c..16c+15.
-template <int QB>
-__device__ __forceinline__ void tile_softmax(Rows<QB>& R, f32x16 (&S)[2][QB], f16x8 (&pf)[QB][4],
-                                             bool first) {
+template <int QB, bool RES>
+__device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB],
+                                             f16x8 (&pf)[QB][4], bool first) {
   if (first || R.track) {
     bool unsettled = false;
 #pragma unroll
@@ -191,6 +196,7 @@ __device__ __forceinline__ void tile_softmax(Rows<QB>& R, f32x16 (&S)[2][QB], f1
           for (int r = 0; r < 16; ++r) R.O[db][qb][r] *= al;
       }
       R.m[qb] = mn;
+      if (RES) R.negm[RES ? qb : 0] = splat16(-mn);
     }
     R.track = __ballot(unsettled) != 0;
   }
@@ -213,9 +219,9 @@ __device__ __forceinline__ void tile_softmax(Rows<QB>& R, f32x16 (&S)[2][QB], f1
 }
 
 // O^T += V^T P^T for one tile in LDS.
-template <int QB>
-__device__ __forceinline__ void tile_pv(Rows<QB>& R, const char* Vs, const f16x8 (&pf)[QB][4],
-                                        int j, int h) {
+template <int QB, bool RES>
+__device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs,
+                                        const f16x8 (&pf)[QB][4], int j, int h) {
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -227,8 +233,8 @@ __device__ __forceinline__ void tile_pv(Rows<QB>& R, const char* Vs, const f16x8
 }
 
 // Normalise and store O in place of q, valid rows only.
-template <int QB>
-__device__ __forceinline__ void rows_store(const Rows<QB>& R, f16* qh, int64_t seq0, int qloc0,
+template <int QB, bool RES>
+__device__ __forceinline__ void rows_store(const Rows<QB, RES>& R, f16* qh, int64_t seq0, int qloc0,
                                            int L, int j, int h) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -267,10 +273,12 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // ---------------------------------------------------------------------------
 // K / V^T tiles are double buffered in LDS and fetched one tile ahead through
 // registers (global_load -> ds_write after the tile's compute), with one
-// workgroup barrier per tile; two workgroups per CU.
-template <int QB>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
-  constexpr int BQ = 4 * QB * 32;
+// workgroup barrier per tile.
+template <int QB, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
+  constexpr int BQ = NW * QB * 32;
+  constexpr int NT = NW * 64;
+  constexpr int CH = 1024 / NT;  // 16-byte chunks per thread per K+V tile
   __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];
 
   const int tid = threadIdx.x;
@@ -286,21 +294,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
   const f16* kh = p.k + (int64_t)bc.h * p.rows * kDh;
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.rows;
 
-  Rows<QB> R;
-  rows_init<QB>(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
+  // The -m accumulator initialiser stays resident when the 8-wave tile leaves
+  // the registers for it; otherwise it is re-splatted before each QK chain.
+  constexpr bool RES = NW == 8;
+  Rows<QB, RES> R;
+  rows_init(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
 
   const int ntiles = (L + 63) / 64;
   const int last_valid = L - 64 * (ntiles - 1);
 
-  // 1024 16-byte chunks per K+V tile, 4 per thread: chunk c < 512 is K (row
+  // 1024 16-byte chunks per K+V tile, CH per thread: chunk c < 512 is K (row
   // c>>3, col c&7), chunk c >= 512 is V^T (feature row, col).
-  u32x4 rg[4];
-  int soff[4];
-  const f16* gsrc[4];
-  int64_t gstep[4];
+  u32x4 rg[CH];
+  int soff[CH];
+  const f16* gsrc[CH];
+  int64_t gstep[CH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + NT * i;
     const int cc = c & 511, row = cc >> 3, col = cc & 7;
     soff[i] = (c >> 9) * (64 * 128) + lds_swz(row, col);
     if (c < 512) {
@@ -313,12 +324,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
   }
   auto gload = [&](int tile) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < CH; ++i)
       rg[i] = *reinterpret_cast<const u32x4*>(gsrc[i] + (int64_t)tile * gstep[i]);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][0] + soff[i]) = rg[i];
+    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][0] + soff[i]) = rg[i];
   };
 
   f32x16 S[2][QB];
@@ -331,9 +342,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
     const int buf = t & 1;
     gload(t + 1);
     if (active) {
-      tile_qk<QB, false>(R, smem[buf][0], j, h, 64, S);
-      tile_softmax<QB>(R, S, pf, t == 0);
-      tile_pv<QB>(R, smem[buf][1], pf, j, h);
+      tile_qk<QB, RES, false>(R, smem[buf][0], j, h, 64, S);
+      tile_softmax(R, S, pf, t == 0);
+      tile_pv(R, smem[buf][1], pf, j, h);
     }
     sstore(buf ^ 1);
     __syncthreads();
@@ -341,16 +352,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs p) {
   // last tile: keys past the end of the set masked
   if (active) {
     const int buf = (ntiles - 1) & 1;
-    tile_qk<QB, true>(R, smem[buf][0], j, h, last_valid, S);
-    tile_softmax<QB>(R, S, pf, ntiles == 1);
-    tile_pv<QB>(R, smem[buf][1], pf, j, h);
+    tile_qk<QB, RES, true>(R, smem[buf][0], j, h, last_valid, S);
+    tile_softmax(R, S, pf, ntiles == 1);
+    tile_pv(R, smem[buf][1], pf, j, h);
   }
-  if (active) rows_store<QB>(R, qh, seq0, qloc0, L, j, h);
+  if (active) rows_store(R, qh, seq0, qloc0, L, j, h);
 }
 
-template <int QB>
+template <int QB, int NW>
 static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
-  constexpr int BQ = 4 * QB * 32;
+  constexpr int BQ = NW * QB * 32;
   AttnArgs g;
   g.q = ws_q(p, a);
   g.k = ws_k(p, a);
@@ -363,13 +374,18 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.qtiles = (p.L + BQ - 1) / BQ;
   g.sc = ws_scalars(p, a);
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
-  hipLaunchKernelGGL((attn_kernel<QB>), dim3((unsigned)blocks), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((attn_kernel<QB, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_core(const Plan& p, const Ptrs& a, hipStream_t st) {
-  if (p.attn_qb == 2) return launch_attn_t<2>(p, a, st);
-  if (p.attn_qb == 1) return launch_attn_t<1>(p, a, st);
+  if (p.attn_waves == 8) {
+    if (p.attn_qb == 2) return launch_attn_t<2, 8>(p, a, st);
+    if (p.attn_qb == 1) return launch_attn_t<1, 8>(p, a, st);
+  } else {
+    if (p.attn_qb == 2) return launch_attn_t<2, 4>(p, a, st);
+    if (p.attn_qb == 1) return launch_attn_t<1, 4>(p, a, st);
+  }
   return hipErrorInvalidValue;
 }
 

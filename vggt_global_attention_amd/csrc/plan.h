@@ -30,6 +30,7 @@ struct Plan {
   RowMap map;          // workspace row -> X row
   int rope_npos;       // entries per axis of the RoPE table
   int attn_qb;         // 32-query blocks per wave in the attention kernel
+  int attn_waves;      // waves per attention workgroup (4 or 8)
   // workspace carve-up (byte offsets)
   size_t off_scal, off_rope, off_wo, off_q, off_k, off_v, total;
 };
