@@ -12,10 +12,13 @@
 // Tile: 128 token rows x 128 output features x 64-deep k-steps, 4 waves, each
 // wave a 64 x 64 block = one head for 64 tokens, so the LayerNorm and the RoPE
 // pairs (feature i, i+16) of a (token, head) never leave the wave.  MFMA
-// 16x16x32 computes the block transposed (features x tokens): each lane then
-// holds one token and 16 of its features, the other 48 sitting in the three
-// lanes 16 apart.  LDS tiles are 128-byte rows with the 16-byte chunk index
-// XOR-swizzled by (row & 7); global->LDS is double buffered through registers.
+// 32x32x16 computes the block transposed (features x tokens): lane l holds
+// token l%32 of each 32-token block and features 8*(r/4) + 4*(l/32) + r%4
+// (r = 0..15) of each 32-feature block -- 32 of the head's 64 features; the
+// other 32 sit in lane l^32, and both RoPE partners (r, r+8) in the lane
+// itself.  LDS tiles are 128-byte rows with the 16-byte chunk index XOR-ed with
+// row bits 0..2 and bit 3 (conflict-free for 32-row operand reads);
+// global->LDS is double buffered through registers.
 #include "plan.h"
 
 namespace vggt {
@@ -48,7 +51,9 @@ struct GemmTypes<kEpiOut> {
   typedef f16x8 V8;
 };
 
-__device__ __forceinline__ int swz(int row, int col) { return row * 128 + ((col ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * 128 + ((col ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
@@ -58,12 +63,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int j = lane & 15, gq = lane >> 4;
+  const int j = lane & 31, h = lane >> 5;
 
+  // Block order.  Blocks go to the 8 XCDs round-robin.  When the output
+  // features split evenly, XCD x owns feature tiles [x*ntn/8, (x+1)*ntn/8):
+  // that slice of the weights (768 KB of Wqkv, 256 KB of Wo at d = 1024) stays
+  // in the XCD's L2 while token tiles stream past, each reused for the XCD's
+  // few feature tiles back to back.  Otherwise fall back to one contiguous
+  // range of (token tile, feature tile) per XCD.
   const int ntn = g.Nf / kGemmBN;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t m0 = (int64_t)(logical / ntn) * kGemmBM;
-  const int n0 = (logical % ntn) * kGemmBN;
+  int64_t m0;
+  int n0;
+  if (ntn % kXcds == 0) {
+    const int per = ntn / kXcds;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    m0 = (int64_t)(slot / per) * kGemmBM;
+    n0 = (xcd * per + slot % per) * kGemmBN;
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    m0 = (int64_t)(logical / ntn) * kGemmBM;
+    n0 = (logical % ntn) * kGemmBN;
+  }
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (int64_t)n0 * g.K;
   const uint16_t* Bbase = reinterpret_cast<const uint16_t*>(g.B);
@@ -108,11 +128,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][1][soff[i]]) = rb[i];
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nk = g.K / kGemmBK;
   gload(0);
@@ -124,123 +146,126 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     const char* As = smem[buf][0];
     const char* Bs = smem[buf][1];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      V8 af[4], bfr[4];
+    for (int kc = 0; kc < 4; ++kc) {
+      V8 af[2], bfr[2];
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-        af[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 16 + j, kc * 4 + gq));
+      for (int fb = 0; fb < 2; ++fb)
+        af[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 32 + j, kc * 2 + h));
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 64 + tb * 16 + j, kc * 4 + gq));
+      for (int tb = 0; tb < 2; ++tb)
+        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 64 + tb * 32 + j, kc * 2 + h));
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
+      for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mfma16x16x32(af[fb], bfr[tb], acc[fb][tb]);
+        for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32x32x16(af[fb], bfr[tb], acc[fb][tb]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // acc[fb][tb][r]: feature n0 + wn*64 + fb*16 + 4*gq + r of token m0 + wm*64 + tb*16 + j.
+  // acc[fb][tb][r]: feature n0 + wn*64 + fb*32 + fo(r) of token m0 + wm*64 + tb*32 + j,
+  // fo(r) = 8*(r/4) + 4*h + r%4.  Block fb = 0 is the first half of the head.
   if (EPI == kEpiQKV) {
     const int fbase = n0 + wn * 64;
     const int blk = fbase / g.d;  // 0: q, 1: k, 2: v
-    const int h = (fbase - blk * g.d) / kDh;
+    const int hd = (fbase - blk * g.d) / kDh;
     if (blk < 2) {
-      const float* gam = (blk == 0 ? g.qg : g.kg) + h * kDh;
-      const float* bet = (blk == 0 ? g.qb : g.kb) + h * kDh;
-      float gm[4][4], bt[4][4];
+      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
+      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
+      float gm[2][16], bt[2][16];
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
+      for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gm[fb][r] = gam[fb * 16 + 4 * gq + r];
-          bt[fb][r] = bet[fb * 16 + 4 * gq + r];
+        for (int r = 0; r < 16; ++r) {
+          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          gm[fb][r] = gam[f];
+          bt[fb][r] = bet[f];
         }
-      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)h * g.rows * kDh;
+      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
       // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
       const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
       float kmx = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int64_t w = m0 + wm * 64 + tb * 16 + j;
+      for (int tb = 0; tb < 2; ++tb) {
+        const int64_t w = m0 + wm * 64 + tb * 32 + j;
         const int64_t src = g.map.src(w);
         float s1 = 0.f;
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s1 += acc[fb][tb][r];
-        const float mean = sum_across_groups(s1) * (1.f / kDh);
+          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
+        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
         float s2 = 0.f;
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < 16; ++r) {
             const float dv = acc[fb][tb][r] - mean;
             s2 = fmaf(dv, dv, s2);
           }
-        const float var = sum_across_groups(s2) * (1.f / kDh);
+        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
         const float rstd = 1.f / sqrtf(var + g.eps);
-        float y[4][4];
+        float y[2][16];
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 16; ++r)
             y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
         if (src >= 0) {
           const int t = (int)(src % g.T);
           if (t >= kSpecial) {
             const int pidx = t - kSpecial;
-            const int pr = pidx / g.gw + g.off, pc = pidx % g.gw + g.off;
+            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * gq + r;
-              const float2 cr = g.rope[pr * 16 + i], cc = g.rope[pc * 16 + i];
-              float a = y[0][r], b = y[1][r];
-              y[0][r] = a * cr.x - b * cr.y;
-              y[1][r] = b * cr.x + a * cr.y;
-              a = y[2][r];
-              b = y[3][r];
-              y[2][r] = a * cc.x - b * cc.y;
-              y[3][r] = b * cc.x + a * cc.y;
-            }
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                // feature i of the half pairs with i + 16: registers r and r + 8
+                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+                const float2 cs = g.rope[pos[fb] * 16 + i];
+                const float a = y[fb][r], b = y[fb][r + 8];
+                y[fb][r] = a * cs.x - b * cs.y;
+                y[fb][r + 8] = b * cs.x + a * cs.y;
+              }
           }
         }
         float n2 = 0.f;
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-          f16x4 o;
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            o[r] = (f16)(y[fb][r] * oscale);
-            const float back = (float)o[r];
-            n2 = fmaf(back, back, n2);
+          for (int rq = 0; rq < 4; ++rq) {
+            f16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
+              const float back = (float)o[r];
+              n2 = fmaf(back, back, n2);
+            }
+            *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 32 + 8 * rq + 4 * h) = o;
           }
-          *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 16 + 4 * gq) = o;
-        }
-        n2 = sum_across_groups(n2);
+        n2 += __shfl_xor(n2, 32);
         if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
       }
       if (blk == 1) {
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[h], kmx);
+        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
       }
     } else {
       const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
-      f16* dst = g.vt + (int64_t)h * kDh * g.rows;
+      f16* dst = g.vt + (int64_t)hd * kDh * g.rows;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int64_t w = m0 + wm * 64 + tb * 16 + j;
+      for (int tb = 0; tb < 2; ++tb) {
+        const int64_t w = m0 + wm * 64 + tb * 32 + j;
         // Key position inside its aligned group of 16: key 8a + 4c + b is
         // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
         // the attention kernel's MFMA consumes probabilities.
         const int64_t pos = (w & ~(int64_t)15) | (((w >> 2) & 1) << 3) | (((w >> 3) & 1) << 2) | (w & 3);
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = fb * 16 + 4 * gq + r;
+          for (int r = 0; r < 16; ++r) {
+            const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             dst[(int64_t)e * g.rows + pos] = (f16)ldexpf(acc[fb][tb][r], kv);
           }
       }
@@ -250,18 +275,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     const int ws = range_exponent(g.sc->woabs);
     const float scale = ldexpf(1.f, -(kv + ws));
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int64_t w = m0 + wm * 64 + tb * 16 + j;
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t w = m0 + wm * 64 + tb * 32 + j;
       const int64_t src = g.map.src(w);
       if (src < 0) continue;
-      bf16* dst = g.y + src * g.d + n0 + wn * 64 + 4 * gq;
+      bf16* dst = g.y + src * g.d + n0 + wn * 64 + 4 * h;
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        bf16x4 o;
+      for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][r] * scale);
-        *reinterpret_cast<bf16x4*>(dst + fb * 16) = o;
-      }
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][4 * rq + r] * scale);
+          *reinterpret_cast<bf16x4*>(dst + fb * 32 + 8 * rq) = o;
+        }
     }
   }
 }

@@ -69,6 +69,7 @@ __global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int6
 }
 
 __global__ __launch_bounds__(256) void absmax_kernel(const bf16* x, int64_t n8, float* out) {
+  __shared__ float red[4];
   float best = 0.f;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -78,7 +79,12 @@ __global__ __launch_bounds__(256) void absmax_kernel(const bf16* x, int64_t n8, 
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
-  if ((threadIdx.x & 63) == 0 && best > 0.f) atomic_max_nonneg(out, best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (m > 0.f) atomic_max_nonneg(out, m);
+  }
 }
 
 // Wo (bf16) -> fp16 * 2^s with s chosen from max|Wo| so the largest entry
@@ -97,15 +103,25 @@ __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t
 }
 
 // Register mode, Y != X: copy the patch rows (tokens 17..T-1) of every frame.
+// Each thread moves four 16-byte chunks per step (loads first, then stores).
 __global__ __launch_bounds__(256) void patch_copy_kernel(const bf16* X, bf16* Y, int S,
                                                          int64_t frame_elems, int64_t skip_elems) {
   const int64_t per = (frame_elems - skip_elems) / 8;  // 16-byte chunks per frame
   const int64_t total = per * S;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int64_t s = i / per, c = i - s * per;
-    int64_t off = s * frame_elems + skip_elems + c * 8;
-    *reinterpret_cast<u32x4*>(Y + off) = *reinterpret_cast<const u32x4*>(X + off);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < total; i0 += 4 * stride) {
+    u32x4 v[4];
+    int64_t off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      const int64_t s = i / per, c = i - s * per;
+      off[u] = i < total ? s * frame_elems + skip_elems + c * 8 : -1;
+      if (off[u] >= 0) v[u] = *reinterpret_cast<const u32x4*>(X + off[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (off[u] >= 0) *reinterpret_cast<u32x4*>(Y + off[u]) = v[u];
   }
 }
 
@@ -126,7 +142,7 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 16, 2048)), dim3(256), 0, st,
                      a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
   const int64_t n8 = (int64_t)p.d * p.d / 8;
-  hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 256, 1024)), dim3(256), 0, st, a.Wo, n8,
+  hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 1024, 256)), dim3(256), 0, st, a.Wo, n8,
                      &sc->woabs);
   hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
                      n8, (const Scalars*)sc, ws_wo(p, a));
@@ -137,7 +153,7 @@ hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st) {
   if (p.T <= kSpecial) return hipSuccess;
   const int64_t frame = (int64_t)p.T * p.d, skip = (int64_t)kSpecial * p.d;
   const int64_t work = (frame - skip) / 8 * p.S;
-  hipLaunchKernelGGL(patch_copy_kernel, dim3(grid_for(work, 256, 8192)), dim3(256), 0, st, a.X,
+  hipLaunchKernelGGL(patch_copy_kernel, dim3(grid_for(work, 1024, 4096)), dim3(256), 0, st, a.X,
                      a.Y, p.S, frame, skip);
   return hipGetLastError();
 }
