@@ -20,3 +20,9 @@ from .vggt_oracle import (  # noqa: F401
     attention_probs,
     token_positions,
 )
+from .avggt_sga import (  # noqa: F401
+    kept_tokens,
+    sga_core,
+    sga_attention,
+    sga_attention_rows,
+)
