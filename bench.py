@@ -64,7 +64,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="s100")
-    ap.add_argument("--mode", default="global", choices=["global", "frame", "register"])
+    ap.add_argument("--mode", default="global",
+                    choices=["global", "frame", "register", "subsampled"])
+    ap.add_argument("--sub", default="3x3", help="subsampled mode: windows sub_h x sub_w")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other modes / sizes")
     ap.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU sample")
@@ -83,13 +85,13 @@ def gpu_inputs(w):
     return inp, {k: inp[k].to("cuda").contiguous() for k in keys}
 
 
-def time_block(w, mode, d, steps, warmup):
+def time_block(w, mode, d, steps, warmup, sub=(1, 1)):
     """ms per full call and ms per attention-core stage, both with HIP events
     on the stream the library launches on (torch's current stream)."""
     import torch
     from vggt_global_attention_amd import api
     from vggt_global_attention_amd import binding as B
-    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w)
+    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
     args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
     Y = torch.empty_like(d["X"])
     stream = torch.cuda.current_stream()
@@ -117,12 +119,12 @@ def time_block(w, mode, d, steps, warmup):
     return ms_step, core / steps
 
 
-def loop_stage(w, mode, d, stage, steps):
+def loop_stage(w, mode, d, stage, steps, sub=(1, 1)):
     import torch
     from vggt_global_attention_amd import api
     from vggt_global_attention_amd import binding as B
     st = {"prep": B.STAGE_PREP, "qkv": B.STAGE_QKV, "core": B.STAGE_CORE, "out": B.STAGE_OUT}
-    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w)
+    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
     args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
     Y = torch.empty_like(d["X"])
     blk(*args, Y=Y)
@@ -190,17 +192,18 @@ def main():
                           "bytes_written_per_copy": n, "copies": 3}))
         return
     w = configs.WORKLOADS[a.workload]
+    sub = tuple(int(x) for x in a.sub.lower().split("x")) if a.mode == "subsampled" else (1, 1)
     print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
     inp, d = gpu_inputs(w)
     if a.only_stage:
-        ms = loop_stage(w, a.mode, d, a.only_stage, a.steps)
+        ms = loop_stage(w, a.mode, d, a.only_stage, a.steps, sub)
         print(json.dumps({"stage": a.only_stage, "mode": a.mode, "workload": w.name,
                           "ms_per_iter_wall": ms}))
         return
     print(f"[bench] timing {a.mode} ({a.warmup} warmup + {a.steps} steps)", file=sys.stderr, flush=True)
-    ms, core_ms = time_block(w, a.mode, d, a.steps, a.warmup)
-    flop = w.flop(a.mode)
-    attn_flop = w.attention_flop(a.mode)
+    ms, core_ms = time_block(w, a.mode, d, a.steps, a.warmup, sub)
+    flop = w.flop(a.mode, sub)
+    attn_flop = w.attention_flop(a.mode, sub)
     achieved = attn_flop / (core_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -228,18 +231,31 @@ def main():
                      "traffic_unit": "bytes per launch (FETCH_SIZE*2.0 + WRITE_SIZE*1.0)",
                      "flop_per_launch": attn_flop, "ms_per_launch": core_ms},
     }
-    if not a.no_extra and a.workload == "s100":
+    if a.mode == "subsampled":
+        out["config"]["sub"] = list(sub)
+        out["config"]["kept_keys"] = w.kept_keys(*sub)
+        out["roofline"]["kernel"] = "CORE stage: K/V gather + discarded sums + attn_kernel<SGA>"
+    if not a.no_extra and a.workload == "s100" and a.mode == "global":
         extra = {}
-        for name, mode in (("s24", "global"), ("s24", "frame"), ("s500", "frame"),
-                           ("s500", "register")):
+        for name, mode, esub in (("s24", "global", (1, 1)), ("s24", "frame", (1, 1)),
+                                 ("s500", "frame", (1, 1)), ("s500", "register", (1, 1)),
+                                 ("s100", "subsampled", (3, 3)),
+                                 ("s300", "subsampled", (3, 3))):
             ww = configs.WORKLOADS[name]
-            print(f"[bench] extra {name} {mode}", file=sys.stderr, flush=True)
-            _, dd = gpu_inputs(ww)
-            m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2)
-            extra[f"{name}_{mode}"] = {"ms_per_layer": m2, "tflops": ww.flop(mode) / m2 / 1e9,
-                                       "core_ms": c2,
-                                       "core_tflops": ww.attention_flop(mode) / c2 / 1e9}
-            del dd
+            print(f"[bench] extra {name} {mode} {esub}", file=sys.stderr, flush=True)
+            if name == a.workload:
+                dd = d
+            else:
+                _, dd = gpu_inputs(ww)
+            m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub)
+            key = f"{name}_{mode}" + (f"{esub[0]}x{esub[1]}" if mode == "subsampled" else "")
+            extra[key] = {"ms_per_layer": m2, "tflops": ww.flop(mode, esub) / m2 / 1e9,
+                          "core_ms": c2,
+                          "core_tflops": ww.attention_flop(mode, esub) / c2 / 1e9}
+            if mode == "subsampled":
+                extra[key]["kept_keys"] = ww.kept_keys(*esub)
+            if dd is not d:
+                del dd
             torch.cuda.empty_cache()
         out["extra"] = extra
     if not a.no_cpu:

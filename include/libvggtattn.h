@@ -23,6 +23,8 @@
  *   - vggt_attn_global_register: only the 17 special tokens of every frame, as
  *     one set of 17*S tokens (register mode, section 三); patch rows of Y are
  *     a copy of X (patch tokens keep to their own frame in this block).
+ *   - vggt_attn_global_subsampled: global mode with AVGGT's subsampled keys and
+ *     values (see its declaration).
  *
  * Conventions for every entry point below:
  *   - Tensor pointers are DEVICE pointers on the current HIP device; dense,
@@ -66,12 +68,14 @@ extern "C" {
 #define VGGT_ATTN_EALIGN     (-3) /* pointer misaligned */
 #define VGGT_ATTN_EWORKSPACE (-4) /* workspace smaller than vggt_attn_workspace_bytes() */
 #define VGGT_ATTN_EHIP       (-5) /* the HIP runtime rejected a launch */
-#define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of range */
+#define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of
+                                     range, subsampling window < 1 */
 
 /* Block modes. */
 #define VGGT_ATTN_MODE_FRAME    0
 #define VGGT_ATTN_MODE_GLOBAL   1
 #define VGGT_ATTN_MODE_REGISTER 2
+#define VGGT_ATTN_MODE_SUBSAMPLED 3 /* global mode, AVGGT subsampled keys / values */
 
 /* Stages of one call, in order (see vggt_attn_stage). */
 #define VGGT_ATTN_STAGE_PREP 0 /* range bounds, RoPE table, fp16 copy of Wo */
@@ -92,7 +96,8 @@ typedef struct vggt_attn_shape {
 } vggt_attn_shape;
 
 /* Bytes of device workspace a call in `mode` needs for `shape`; 0 if the
-   mode or shape is not supported.  Pure host arithmetic, no HIP call. */
+   mode or shape is not supported.  Pure host arithmetic, no HIP call.  For
+   VGGT_ATTN_MODE_SUBSAMPLED the size covers every subsampling window. */
 size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape);
 
 /* Frame block: attention inside each frame (S sets of T tokens). */
@@ -115,6 +120,25 @@ int vggt_attn_global_register(const vggt_attn_shape* shape, const void* X,
                               const float* k_beta, void* Y, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Global mode with AVGGT subsampled global attention ("AVGGT: Rethinking
+   Global Attention for Accelerating VGGT", gist.science summary, technical
+   summary section 2B).  Every token stays a query, but the keys / values are
+   only (a) the 17 special tokens of every frame and (b) one patch per
+   sub_h x sub_w window of the patch grid -- patch (r, c) with r % sub_h == 0
+   and c % sub_w == 0 (the window's top-left cell; windows cut by the grid edge
+   keep theirs) -- plus (c) each query's own key / value (the diagonal), and
+   (d) one mean key / value pair, the mean over the discarded tokens of the
+   normalised, rotated keys and of the values, which stands in for every
+   discarded column of the query's row: it enters the softmax with
+   multiplicity n_i = (discarded tokens) - [query i itself is discarded].
+   sub_h = sub_w = 1 is exact global attention.  sub_h, sub_w >= 1 (else
+   VGGT_ATTN_ERANGE).  Workspace: vggt_attn_workspace_bytes(VGGT_ATTN_MODE_SUBSAMPLED). */
+int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int32_t sub_w,
+                                const void* X, const void* Wqkv, const void* Wo,
+                                const float* q_gamma, const float* q_beta,
+                                const float* k_gamma, const float* k_beta, void* Y,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* One stage of a call in `mode` (VGGT_ATTN_STAGE_*), same arguments and
    checks as the full call.  Running the four stages in order on one stream
    with one workspace is exactly the full call; a stage reads what the
@@ -124,6 +148,13 @@ int vggt_attn_stage(int mode, int stage, const vggt_attn_shape* shape, const voi
                     const void* Wqkv, const void* Wo, const float* q_gamma,
                     const float* q_beta, const float* k_gamma, const float* k_beta,
                     void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One stage of vggt_attn_global_subsampled, as vggt_attn_stage. */
+int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t sub_h,
+                               int32_t sub_w, const void* X, const void* Wqkv, const void* Wo,
+                               const float* q_gamma, const float* q_beta, const float* k_gamma,
+                               const float* k_beta, void* Y, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* vggt_attn_status_str(int status);

@@ -116,3 +116,54 @@ def test_status_strings():
         assert B.status_str(code) and B.status_str(code) != "unknown status"
     assert B.status_str(12345) == "unknown status"
     assert B.vggt_attn_version() >= 10000
+
+
+# ----------------------------------------------------------------------------
+# Subsampled global attention entry points
+# ----------------------------------------------------------------------------
+
+def sub_fn(sub_h, sub_w):
+    def fn(s, *rest):
+        return B.vggt_attn_global_subsampled(s, sub_h, sub_w, *rest)
+    return fn
+
+
+def test_subsampled_workspace_bytes():
+    s = shape()
+    g = B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, s)
+    sub = B.vggt_attn_workspace_bytes(B.MODE_SUBSAMPLED, s)
+    N = 100 * 1031
+    # compact keys / values sized for every window choice (1 x 1 keeps all tokens)
+    assert sub >= g + 2 * 16 * N * 64 * 2
+    assert B.vggt_attn_workspace_bytes(B.MODE_SUBSAMPLED, shape(T=1030)) == 0
+
+
+def test_subsampled_errors():
+    s = B.make_shape(**TINY)
+    big = B.vggt_attn_workspace_bytes(B.MODE_SUBSAMPLED, s)
+    for sh, sw in ((0, 3), (3, 0), (-1, 1)):
+        assert call(sub_fn(sh, sw), s, ws_bytes=big) == B.ERANGE
+    fn = sub_fn(3, 3)
+    assert call(fn, s, ws_bytes=big, X=0) == B.EINVAL
+    assert call(fn, s, ws_bytes=big, X=0x100008) == B.EALIGN
+    assert call(fn, s, ws_bytes=big - 256) == B.EWORKSPACE
+    # the global mode's workspace is too small for the compact key / value copies
+    assert call(fn, s) == B.EWORKSPACE
+    assert call(fn, s, ws_bytes=big, Y=0x100000 + 64) == B.EINVAL
+    bad = dict(TINY)
+    bad.update(T=80)
+    assert call(fn, B.make_shape(**bad), ws_bytes=big) == B.ESHAPE
+
+
+def test_subsampled_stage_errors():
+    s = B.make_shape(**TINY)
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    big = B.vggt_attn_workspace_bytes(B.MODE_SUBSAMPLED, s)
+    # the generic stage entry has no windows to pass
+    assert B.vggt_attn_stage(B.MODE_SUBSAMPLED, B.STAGE_CORE, s, *a, 0x10000000, big,
+                             None) == B.EINVAL
+    assert B.vggt_attn_subsampled_stage(7, s, 3, 3, *a, 0x10000000, big, None) == B.EINVAL
+    assert B.vggt_attn_subsampled_stage(B.STAGE_CORE, s, 0, 3, *a, 0x10000000, big,
+                                        None) == B.ERANGE
+    assert B.vggt_attn_subsampled_stage(B.STAGE_CORE, s, 3, 3, *a, 0x10000000, 16,
+                                        None) == B.EWORKSPACE

@@ -11,7 +11,7 @@ import torch
 from . import binding as B
 
 _ENTRY = {"frame": "vggt_attn_frame", "global": "vggt_attn_global",
-          "register": "vggt_attn_global_register"}
+          "register": "vggt_attn_global_register", "subsampled": "vggt_attn_global_subsampled"}
 
 
 def shape_of(X: torch.Tensor, H: int, grid_h: int, grid_w: int, rope_base=100.0,
@@ -50,10 +50,11 @@ class Block:
     """One attention block configuration with its workspace, reusable across calls."""
 
     def __init__(self, mode: str, X: torch.Tensor, H: int, grid_h: int, grid_w: int,
-                 rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None):
+                 rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None, sub=(1, 1)):
         if mode not in _ENTRY:
             raise ValueError(f"unknown mode {mode!r}")
         self.mode = mode
+        self.sub = (int(sub[0]), int(sub[1]))  # subsampled mode: (sub_h, sub_w) windows
         self.shape = shape_of(X, H, grid_h, grid_w, rope_base, ln_eps, pos_offset)
         need = workspace_bytes(mode, self.shape)
         if workspace is None:
@@ -69,23 +70,31 @@ class Block:
     def __call__(self, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y=None, stream=None):
         if Y is None:
             Y = torch.empty_like(X)
-        st = getattr(B, _ENTRY[self.mode])(*self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma,
-                                                        k_beta, Y), _stream_handle(stream))
+        args = self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y)
+        if self.mode == "subsampled":
+            st = B.vggt_attn_global_subsampled(args[0], *self.sub, *args[1:],
+                                               _stream_handle(stream))
+        else:
+            st = getattr(B, _ENTRY[self.mode])(*args, _stream_handle(stream))
         if st != B.OK:
             raise B.VggtAttnError(st, _ENTRY[self.mode])
         return Y
 
     def stage(self, stage: int, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, stream=None):
-        st = B.vggt_attn_stage(B.MODES[self.mode], stage,
-                               *self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y),
-                               _stream_handle(stream))
+        args = self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y)
+        if self.mode == "subsampled":
+            st = B.vggt_attn_subsampled_stage(stage, args[0], *self.sub, *args[1:],
+                                              _stream_handle(stream))
+        else:
+            st = B.vggt_attn_stage(B.MODES[self.mode], stage, *args, _stream_handle(stream))
         if st != B.OK:
             raise B.VggtAttnError(st, "vggt_attn_stage")
         return Y
 
 
 def attention(mode: str, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, H: int, grid_h: int,
-              grid_w: int, Y=None, stream=None, **shape_kw):
-    """One call of the block in `mode` ('frame', 'global' or 'register')."""
-    blk = Block(mode, X, H, grid_h, grid_w, **shape_kw)
+              grid_w: int, Y=None, stream=None, sub=(1, 1), **shape_kw):
+    """One call of the block in `mode` ('frame', 'global', 'register' or 'subsampled';
+    `sub` = (sub_h, sub_w) windows of the subsampled mode)."""
+    blk = Block(mode, X, H, grid_h, grid_w, sub=sub, **shape_kw)
     return blk(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y=Y, stream=stream)

@@ -12,13 +12,14 @@ import os
 from .build import LIB
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
-MODE_FRAME, MODE_GLOBAL, MODE_REGISTER = 0, 1, 2
+MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED = 0, 1, 2, 3
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
-MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER}
+MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
+         "subsampled": MODE_SUBSAMPLED}
 
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
-           "vggt_attn_global_register", "vggt_attn_stage", "vggt_attn_status_str",
-           "vggt_attn_version")
+           "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_stage",
+           "vggt_attn_subsampled_stage", "vggt_attn_status_str", "vggt_attn_version")
 
 
 class vggt_attn_shape(ctypes.Structure):
@@ -56,6 +57,11 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         f.argtypes = _CALL_ARGS
     L.vggt_attn_stage.restype = ctypes.c_int
     L.vggt_attn_stage.argtypes = [ctypes.c_int, ctypes.c_int] + _CALL_ARGS
+    sub = [ctypes.POINTER(vggt_attn_shape), ctypes.c_int32, ctypes.c_int32] + _CALL_ARGS[1:]
+    L.vggt_attn_global_subsampled.restype = ctypes.c_int
+    L.vggt_attn_global_subsampled.argtypes = sub
+    L.vggt_attn_subsampled_stage.restype = ctypes.c_int
+    L.vggt_attn_subsampled_stage.argtypes = [ctypes.c_int] + sub
     L.vggt_attn_status_str.restype = ctypes.c_char_p
     L.vggt_attn_status_str.argtypes = [ctypes.c_int]
     L.vggt_attn_version.restype = ctypes.c_int
@@ -98,6 +104,18 @@ def vggt_attn_stage(mode, stage, shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k
                     workspace, workspace_bytes, stream) -> int:
     return _call("vggt_attn_stage", mode, stage, ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
                  q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global_subsampled(shape, sub_h, sub_w, X, Wqkv, Wo, q_gamma, q_beta, k_gamma,
+                                k_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_global_subsampled", ctypes.byref(shape), sub_h, sub_w, X, Wqkv, Wo,
+                 q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_subsampled_stage(stage, shape, sub_h, sub_w, X, Wqkv, Wo, q_gamma, q_beta,
+                               k_gamma, k_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_subsampled_stage", stage, ctypes.byref(shape), sub_h, sub_w, X, Wqkv,
+                 Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
 
 
 def status_str(status: int) -> str:

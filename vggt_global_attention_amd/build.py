@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvggtattn.so")
-SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip", "subsample.hip"]
 
 # Packed fp32 VALU ops are kept out of every kernel on purpose.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -43,8 +43,17 @@ class Workload:
     def Dh(self) -> int:
         return self.d // self.H
 
-    def attention_flop(self, mode: str) -> float:
-        """4 * sum(L^2) * d over the attention sets of one block (2 FLOP per MAC)."""
+    def kept_keys(self, sub_h: int, sub_w: int) -> int:
+        """Keys of subsampled global attention: 17 specials plus one patch per
+        sub_h x sub_w window, in every frame."""
+        return self.S * (N_SPECIAL + (-(-self.grid_h // sub_h)) * (-(-self.grid_w // sub_w)))
+
+    def attention_flop(self, mode: str, sub=(1, 1)) -> float:
+        """4 * sum(L^2) * d over the attention sets of one block (2 FLOP per MAC);
+        subsampled mode: 4 * N * (kept keys) * d (the two per-row extra columns
+        are not counted)."""
+        if mode == "subsampled":
+            return 4.0 * self.N * self.kept_keys(*sub) * self.d
         if mode == "frame":
             return 4.0 * self.S * self.T ** 2 * self.d
         if mode == "global":
@@ -58,8 +67,8 @@ class Workload:
         M = self.R if mode == "register" else self.N
         return 8.0 * M * self.d ** 2
 
-    def flop(self, mode: str) -> float:
-        return self.attention_flop(mode) + self.gemm_flop(mode)
+    def flop(self, mode: str, sub=(1, 1)) -> float:
+        return self.attention_flop(mode, sub) + self.gemm_flop(mode)
 
 
 WORKLOADS = {

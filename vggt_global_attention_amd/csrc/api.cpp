@@ -10,10 +10,16 @@ namespace vggt {
 
 static int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
+// Kept tokens per frame in subsampled mode: the 17 specials and the top-left
+// cell of every sub_h x sub_w window of the grid.
+static int64_t kept_per_frame(const vggt_attn_shape* s, int sub_h, int sub_w) {
+  return kSpecial + (int64_t)((s->grid_h + sub_h - 1) / sub_h) * ((s->grid_w + sub_w - 1) / sub_w);
+}
+
+int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p) {
   if (!s || !p) return VGGT_ATTN_EINVAL;
   if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
-      mode != VGGT_ATTN_MODE_REGISTER)
+      mode != VGGT_ATTN_MODE_REGISTER && mode != VGGT_ATTN_MODE_SUBSAMPLED)
     return VGGT_ATTN_EINVAL;
   if (s->S < 1 || s->H < 1 || s->d < 1 || s->grid_h < 0 || s->grid_w < 0) return VGGT_ATTN_ESHAPE;
   if (s->d != s->H * kDh || s->d % kGemmBN != 0) return VGGT_ATTN_ESHAPE;
@@ -24,6 +30,9 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
   if (!(isfinite(s->rope_base) && s->rope_base > 0.f)) return VGGT_ATTN_ERANGE;
   if (!(isfinite(s->ln_eps) && s->ln_eps > 0.f)) return VGGT_ATTN_ERANGE;
   if (s->pos_offset < 0 || s->pos_offset > 65535) return VGGT_ATTN_ERANGE;
+  const bool subsampled = mode == VGGT_ATTN_MODE_SUBSAMPLED;
+  if (!subsampled) sub_h = sub_w = 1;
+  if (sub_h < 1 || sub_w < 1) return VGGT_ATTN_ERANGE;
 
   memset(p, 0, sizeof(*p));
   p->mode = mode;
@@ -38,7 +47,7 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
   p->eps = s->ln_eps;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
-  if (mode == VGGT_ATTN_MODE_GLOBAL) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled) {
     p->nseq = 1;
     p->L = (int)N;
     p->seq_stride = round_up(N, kAttnBK);
@@ -71,7 +80,23 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
     if (w == 4 || w == 8) p->attn_waves = w;
   }
   p->rows = round_up(cover, kRowAlign);
-  if (mode == VGGT_ATTN_MODE_GLOBAL) {
+  p->sub_h = sub_h;
+  p->sub_w = sub_w;
+  if (subsampled) {
+    p->Lk = (int)(kept_per_frame(s, sub_h, sub_w) * s->S);
+    p->kv_rows = round_up(p->Lk, kRowAlign);
+    p->kv_seq_stride = round_up(p->Lk, kAttnBK);
+    p->nD = (int)(N - p->Lk);
+    // the subsampled kernel has a single tile shape
+    p->attn_qb = 2;
+    p->attn_waves = 8;
+  } else {
+    p->Lk = p->L;
+    p->kv_rows = p->rows;
+    p->kv_seq_stride = p->seq_stride;
+    p->nD = 0;
+  }
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled) {
     p->map = RowMap{p->rows, 0, (int32_t)N, 1};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->map = RowMap{p->seq_stride, s->T, s->T, s->S};
@@ -95,6 +120,18 @@ int make_plan(int mode, const vggt_attn_shape* s, Plan* p) {
   off += qkv;
   p->off_v = off;
   off += qkv;
+  if (subsampled) {
+    // compact keys / values sized for the largest kept set (sub_h = sub_w = 1:
+    // every token), so the workspace size does not depend on the windows
+    p->off_kc = off;
+    off += qkv;
+    p->off_vc = off;
+    off += qkv;
+    p->off_sums = off;  // [H][128] fp32: sums of discarded keys, then values
+    off += round_up((int64_t)s->H * 128 * sizeof(float), 256);
+    p->off_part = off;  // [H][ceil(N/1024)][128] fp32 partial sums
+    off += round_up((int64_t)s->H * ((N + 1023) / 1024) * 128 * sizeof(float), 256);
+  }
   p->total = off;
   return VGGT_ATTN_OK;
 }
@@ -112,10 +149,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-int check_call(int mode, const vggt_attn_shape* shape, const void* X, const void* Wqkv,
-               const void* Wo, const float* qg, const float* qb, const float* kg, const float* kb,
-               void* Y, void* ws, size_t ws_bytes, Plan* plan) {
-  int st = make_plan(mode, shape, plan);
+int check_call(int mode, const vggt_attn_shape* shape, int sub_h, int sub_w, const void* X,
+               const void* Wqkv, const void* Wo, const float* qg, const float* qb, const float* kg,
+               const float* kb, void* Y, void* ws, size_t ws_bytes, Plan* plan) {
+  int st = make_plan(mode, shape, sub_h, sub_w, plan);
   if (st != VGGT_ATTN_OK) return st;
   if (!X || !Wqkv || !Wo || !qg || !qb || !kg || !kb || !Y || !ws) return VGGT_ATTN_EINVAL;
   if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(Wqkv, 16) || !aligned(Wo, 16) ||
@@ -140,11 +177,13 @@ int check_call(int mode, const vggt_attn_shape* shape, const void* X, const void
   return VGGT_ATTN_OK;
 }
 
-int run(int mode, int first_stage, int last_stage, const vggt_attn_shape* shape, const void* X,
-        const void* Wqkv, const void* Wo, const float* qg, const float* qb, const float* kg,
-        const float* kb, void* Y, void* ws, size_t ws_bytes, void* stream) {
+int run(int mode, int sub_h, int sub_w, int first_stage, int last_stage,
+        const vggt_attn_shape* shape, const void* X, const void* Wqkv, const void* Wo,
+        const float* qg, const float* qb, const float* kg, const float* kb, void* Y, void* ws,
+        size_t ws_bytes, void* stream) {
   Plan plan;
-  int st = check_call(mode, shape, X, Wqkv, Wo, qg, qb, kg, kb, Y, ws, ws_bytes, &plan);
+  int st = check_call(mode, shape, sub_h, sub_w, X, Wqkv, Wo, qg, qb, kg, kb, Y, ws, ws_bytes,
+                      &plan);
   if (st != VGGT_ATTN_OK) return st;
   Ptrs a{reinterpret_cast<const bf16*>(X), reinterpret_cast<const bf16*>(Wqkv),
          reinterpret_cast<const bf16*>(Wo), qg, qb, kg, kb, reinterpret_cast<bf16*>(Y),
@@ -155,7 +194,10 @@ int run(int mode, int first_stage, int last_stage, const vggt_attn_shape* shape,
     switch (stage) {
       case VGGT_ATTN_STAGE_PREP: e = launch_prep(plan, a, hs); break;
       case VGGT_ATTN_STAGE_QKV: e = launch_qkv(plan, a, hs); break;
-      case VGGT_ATTN_STAGE_CORE: e = launch_core(plan, a, hs); break;
+      case VGGT_ATTN_STAGE_CORE:
+        if (plan.mode == VGGT_ATTN_MODE_SUBSAMPLED) e = launch_subsample(plan, a, hs);
+        if (e == hipSuccess) e = launch_core(plan, a, hs);
+        break;
       case VGGT_ATTN_STAGE_OUT: e = launch_out(plan, a, hs); break;
     }
     if (e != hipSuccess) return VGGT_ATTN_EHIP;
@@ -169,7 +211,7 @@ extern "C" {
 
 size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape) {
   Plan plan;
-  if (make_plan(mode, shape, &plan) != VGGT_ATTN_OK) return 0;
+  if (make_plan(mode, shape, 1, 1, &plan) != VGGT_ATTN_OK) return 0;
   return plan.total;
 }
 
@@ -181,20 +223,39 @@ size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape) {
   shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream
 
 int vggt_attn_frame(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_FRAME, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_FRAME, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_global(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_GLOBAL, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_GLOBAL, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_global_register(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_REGISTER, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_REGISTER, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {
   if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
-  return run(mode, stage, stage, VGGT_PASS);
+  if (mode == VGGT_ATTN_MODE_SUBSAMPLED) return VGGT_ATTN_EINVAL;  // needs the windows
+  return run(mode, 1, 1, stage, stage, VGGT_PASS);
+}
+
+int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int32_t sub_w,
+                                const void* X, const void* Wqkv, const void* Wo,
+                                const float* q_gamma, const float* q_beta,
+                                const float* k_gamma, const float* k_beta, void* Y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return run(VGGT_ATTN_MODE_SUBSAMPLED, sub_h, sub_w, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT,
+             VGGT_PASS);
+}
+
+int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t sub_h,
+                               int32_t sub_w, const void* X, const void* Wqkv, const void* Wo,
+                               const float* q_gamma, const float* q_beta, const float* k_gamma,
+                               const float* k_beta, void* Y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
+  return run(VGGT_ATTN_MODE_SUBSAMPLED, sub_h, sub_w, stage, stage, VGGT_PASS);
 }
 
 const char* vggt_attn_status_str(int status) {
@@ -205,11 +266,12 @@ const char* vggt_attn_status_str(int status) {
     case VGGT_ATTN_EALIGN: return "misaligned pointer (tensors 16 B, gamma/beta 4 B, workspace 256 B)";
     case VGGT_ATTN_EWORKSPACE: return "workspace smaller than vggt_attn_workspace_bytes()";
     case VGGT_ATTN_EHIP: return "HIP runtime error while enqueueing a kernel";
-    case VGGT_ATTN_ERANGE: return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535";
+    case VGGT_ATTN_ERANGE:
+      return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535, sub_h / sub_w >= 1";
     default: return "unknown status";
   }
 }
 
-int vggt_attn_version(void) { return 10000; }
+int vggt_attn_version(void) { return 10100; }
 
 }  // extern "C"

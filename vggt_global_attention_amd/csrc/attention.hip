@@ -34,8 +34,9 @@
 // condition after each tile.  The row sum accumulates the fp16-rounded
 // probabilities with v_dot2 (the same values the PV MFMA consumes).
 //
-// One kernel, attn_kernel<QB, NW>: NW waves and NW*QB*32 queries per
-// workgroup.  Global sets use 8 waves x 64 queries (512 queries share each
+// One kernel, attn_kernel<QB, NW, SGA>: NW waves and NW*QB*32 queries per
+// workgroup (SGA: the subsampled global set, whose keys are a compact copy of
+// the kept tokens, plus two per-row columns folded in at the end).  Global sets use 8 waves x 64 queries (512 queries share each
 // K/V tile, one workgroup per CU, the -m initialiser kept resident); frame and
 // register sets use 4 waves x 32 queries (small sets, ragged ends).  Measured
 // alternatives that did not pay on gfx950: an 8-wave "ping-pong" split (waves
@@ -53,13 +54,21 @@ constexpr float kPinBelow = 15.f;  // settled rows: reference pinned at bound - 
 constexpr float kSettleGap = 29.f; // settle once bound - m <= kSettleGap (top term stays >= 2^-14)
 
 struct AttnArgs {
-  f16* q;            // [H][rows][64] scaled queries; overwritten with O
-  const f16* k;      // [H][rows][64]
-  const f16* vt;     // [H][64][rows], keys permuted inside aligned 16-groups
-  int64_t rows;
+  f16* q;              // [H][rows][64] scaled queries; overwritten with O
+  const f16* k;        // [H][kv_rows][64] keys of the loop
+  const f16* vt;       // [H][64][kv_rows], keys permuted inside aligned 16-groups
+  int64_t rows;        // query rows per head; set s starts at row s * seq_stride
   int64_t seq_stride;
-  int nseq, L, H, qtiles;
+  int64_t kv_rows;     // key rows per head; set s starts at key s * kv_seq_stride
+  int64_t kv_seq_stride;
+  int nseq, L, Lk, H, qtiles;  // sets, queries and keys per set, heads, query tiles
   const Scalars* sc;
+  // subsampled global set only: every token's key / value (for the diagonal)
+  // and the per-head sums of the discarded keys and values (for the mean)
+  const f16* k_all;    // [H][rows][64]
+  const f16* vt_all;   // [H][64][rows]
+  const float* sums;   // [H][128]
+  int nD, T, gw, sub_h, sub_w;
 };
 
 // LDS tiles are 64 rows x 128 bytes.  The MFMA operand reads take one
@@ -232,6 +241,65 @@ __device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs,
     }
 }
 
+// Subsampled global set: fold into each row's softmax the two columns the
+// key loop does not hold -- the token's own key / value when the token itself
+// was discarded (a kept token's diagonal is already in the loop), and the
+// mean key / value pair of the discarded tokens, which fills the row's other
+// n_i discarded columns (logit + log2 n_i).  Rescales O and l to the new
+// reference like one more online-softmax step, in fp32.
+template <int QB, bool RES>
+__device__ __forceinline__ void sga_columns(Rows<QB, RES>& R, const AttnArgs& p, int hd,
+                                            int qloc0, int j, int h) {
+  const float* sk = p.sums + hd * 128;
+  const float* sv = sk + 64;
+  const float inv = p.nD > 0 ? 1.f / (float)p.nD : 0.f;
+  const f16* kh = p.k_all + (int64_t)hd * p.rows * kDh;
+  const f16* vh = p.vt_all + (int64_t)hd * kDh * p.rows;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qloc0 + qb * 32 + j;  // = token index: one set, identity row map
+    if (row >= p.L) continue;             // lanes j and j + 32 skip together
+    const int t = row % p.T;
+    bool kept = true;
+    if (t >= kSpecial) {
+      const int pidx = t - kSpecial, r = pidx / p.gw, c = pidx - r * p.gw;
+      kept = (r % p.sub_h) == 0 && (c % p.sub_w) == 0;
+    }
+    float sd = 0.f, sm = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      f16x8 kd = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (!kept) kd = *reinterpret_cast<const f16x8*>(kh + (int64_t)row * kDh + dc * 16 + h * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = (float)R.qf[qb][dc][e];
+        sd = fmaf(qv, (float)kd[e], sd);
+        sm = fmaf(qv, sk[dc * 16 + h * 8 + e], sm);
+      }
+    }
+    sd += __shfl_xor(sd, 32);
+    sm += __shfl_xor(sm, 32);
+    const int n = p.nD - (kept ? 0 : 1);
+    const float s_d = kept ? -INFINITY : sd;
+    const float s_m = n > 0 ? sm * inv + __log2f((float)n) : -INFINITY;
+    const float mn = fmaxf(R.m[qb], fmaxf(s_d, s_m));
+    const float al = __builtin_amdgcn_exp2f(R.m[qb] - mn);
+    const float pd = __builtin_amdgcn_exp2f(s_d - mn), pm = __builtin_amdgcn_exp2f(s_m - mn);
+    R.l[qb] = R.l[qb] * al + (h == 0 ? pd + pm : 0.f);
+    const int64_t slot = ((int64_t)row & ~(int64_t)15) | (((row >> 2) & 1) << 3) |
+                         (((row >> 3) & 1) << 2) | (row & 3);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int f = db * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float vd = kept ? 0.f : (float)vh[(int64_t)f * p.rows + slot];
+        R.O[db][qb][r] = fmaf(R.O[db][qb][r], al, fmaf(pd, vd, pm * (sv[f] * inv)));
+      }
+    R.m[qb] = mn;
+  }
+}
+
 // Normalise and store O in place of q, valid rows only.
 template <int QB, bool RES>
 __device__ __forceinline__ void rows_store(const Rows<QB, RES>& R, f16* qh, int64_t seq0, int qloc0,
@@ -274,7 +342,7 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // K / V^T tiles are double buffered in LDS and fetched one tile ahead through
 // registers (global_load -> ds_write after the tile's compute), with one
 // workgroup barrier per tile.
-template <int QB, int NW>
+template <int QB, int NW, bool SGA>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
   constexpr int NT = NW * 64;
@@ -287,12 +355,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 
   const BlockCoord bc = block_coord(p);
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
+  const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
   const int L = p.L;
   const int qloc0 = bc.qt * BQ + wave * QB * 32;
   const bool active = __builtin_amdgcn_readfirstlane(qloc0) < L;
   f16* qh = p.q + (int64_t)bc.h * p.rows * kDh;
-  const f16* kh = p.k + (int64_t)bc.h * p.rows * kDh;
-  const f16* vh = p.vt + (int64_t)bc.h * kDh * p.rows;
+  const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
+  const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
 
   // The -m accumulator initialiser stays resident when the 8-wave tile leaves
   // the registers for it; otherwise it is re-splatted before each QK chain.
@@ -300,8 +369,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   Rows<QB, RES> R;
   rows_init(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
 
-  const int ntiles = (L + 63) / 64;
-  const int last_valid = L - 64 * (ntiles - 1);
+  const int ntiles = (p.Lk + 63) / 64;
+  const int last_valid = p.Lk - 64 * (ntiles - 1);
 
   // 1024 16-byte chunks per K+V tile, CH per thread: chunk c < 512 is K (row
   // c>>3, col c&7), chunk c >= 512 is V^T (feature row, col).
@@ -315,10 +384,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     const int cc = c & 511, row = cc >> 3, col = cc & 7;
     soff[i] = (c >> 9) * (64 * 128) + lds_swz(row, col);
     if (c < 512) {
-      gsrc[i] = kh + (seq0 + row) * kDh + col * 8;
+      gsrc[i] = kh + (kv0 + row) * kDh + col * 8;
       gstep[i] = 64 * kDh;
     } else {
-      gsrc[i] = vh + (int64_t)row * p.rows + seq0 + col * 8;
+      gsrc[i] = vh + (int64_t)row * p.kv_rows + kv0 + col * 8;
       gstep[i] = 64;
     }
   }
@@ -356,35 +425,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     tile_softmax(R, S, pf, ntiles == 1);
     tile_pv(R, smem[buf][1], pf, j, h);
   }
+  if (SGA && active) sga_columns(R, p, bc.h, qloc0, j, h);
   if (active) rows_store(R, qh, seq0, qloc0, L, j, h);
 }
 
-template <int QB, int NW>
+template <int QB, int NW, bool SGA>
 static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   constexpr int BQ = NW * QB * 32;
-  AttnArgs g;
+  AttnArgs g{};
   g.q = ws_q(p, a);
-  g.k = ws_k(p, a);
-  g.vt = ws_v(p, a);
+  g.k = ws_kloop(p, a);
+  g.vt = ws_vloop(p, a);
   g.rows = p.rows;
   g.seq_stride = p.seq_stride;
+  g.kv_rows = p.kv_rows;
+  g.kv_seq_stride = p.kv_seq_stride;
   g.nseq = p.nseq;
   g.L = p.L;
+  g.Lk = p.Lk;
   g.H = p.H;
   g.qtiles = (p.L + BQ - 1) / BQ;
   g.sc = ws_scalars(p, a);
+  if (SGA) {
+    g.k_all = ws_k(p, a);
+    g.vt_all = ws_v(p, a);
+    g.sums = ws_sums(p, a);
+    g.nD = p.nD;
+    g.T = p.T;
+    g.gw = p.gw;
+    g.sub_h = p.sub_h;
+    g.sub_w = p.sub_w;
+  }
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
-  hipLaunchKernelGGL((attn_kernel<QB, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, g);
+  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_core(const Plan& p, const Ptrs& a, hipStream_t st) {
+  if (p.mode == VGGT_ATTN_MODE_SUBSAMPLED) return launch_attn_t<2, 8, true>(p, a, st);
   if (p.attn_waves == 8) {
-    if (p.attn_qb == 2) return launch_attn_t<2, 8>(p, a, st);
-    if (p.attn_qb == 1) return launch_attn_t<1, 8>(p, a, st);
+    if (p.attn_qb == 2) return launch_attn_t<2, 8, false>(p, a, st);
+    if (p.attn_qb == 1) return launch_attn_t<1, 8, false>(p, a, st);
   } else {
-    if (p.attn_qb == 2) return launch_attn_t<2, 4>(p, a, st);
-    if (p.attn_qb == 1) return launch_attn_t<1, 4>(p, a, st);
+    if (p.attn_qb == 2) return launch_attn_t<2, 4, false>(p, a, st);
+    if (p.attn_qb == 1) return launch_attn_t<1, 4, false>(p, a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -31,8 +31,18 @@ struct Plan {
   int rope_npos;       // entries per axis of the RoPE table
   int attn_qb;         // 32-query blocks per wave in the attention kernel
   int attn_waves;      // waves per attention workgroup (4 or 8)
+  // keys / values of the attention sets: the q rows themselves, except in
+  // subsampled mode, where they are a compact gathered copy of the kept
+  // tokens (Lk of them, head stride kv_rows rows)
+  int sub_h, sub_w;    // subsampling windows (1, 1 outside subsampled mode)
+  int Lk;              // keys per set
+  int64_t kv_rows;     // rows per head of the key / value buffers
+  int64_t kv_seq_stride;
+  int nD;              // subsampled mode: discarded tokens (mean-filled columns)
   // workspace carve-up (byte offsets)
-  size_t off_scal, off_rope, off_wo, off_q, off_k, off_v, total;
+  size_t off_scal, off_rope, off_wo, off_q, off_k, off_v;
+  size_t off_kc, off_vc, off_sums, off_part;  // subsampled mode only (else 0)
+  size_t total;
 };
 
 struct Ptrs {
@@ -47,8 +57,10 @@ struct Ptrs {
   char* ws;
 };
 
-// Fills `p`; returns VGGT_ATTN_OK or the shape / range status.
-int make_plan(int mode, const vggt_attn_shape* s, Plan* p);
+// Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  sub_h and
+// sub_w are the subsampling windows of VGGT_ATTN_MODE_SUBSAMPLED (ignored in
+// the other modes).
+int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p);
 
 hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st);
 hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st);
@@ -65,5 +77,19 @@ inline f16* ws_wo(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(
 inline f16* ws_q(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_q); }
 inline f16* ws_k(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_k); }
 inline f16* ws_v(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_v); }
+// keys / values the attention loop streams (compact copies in subsampled mode)
+inline f16* ws_kloop(const Plan& p, const Ptrs& a) {
+  return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_kc : p.off_k));
+}
+inline f16* ws_vloop(const Plan& p, const Ptrs& a) {
+  return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_vc : p.off_v));
+}
+inline float* ws_sums(const Plan& p, const Ptrs& a) {
+  return reinterpret_cast<float*>(a.ws + p.off_sums);
+}
+
+// Subsampled mode: gather the kept tokens' keys / values and sum the
+// discarded ones (first half of the CORE stage).
+hipError_t launch_subsample(const Plan& p, const Ptrs& a, hipStream_t st);
 
 }  // namespace vggt

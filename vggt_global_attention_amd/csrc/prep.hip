@@ -1,6 +1,7 @@
 // Prep-stage kernels (all HBM-bound and small next to the GEMMs and the
 // attention core):
-//   * clear the workspace scalars and tabulate cos/sin of the 2D RoPE angles;
+//   * clear the workspace scalars (and the subsampled mode's sums) and
+//     tabulate cos/sin of the 2D RoPE angles;
 //   * range bounds: max L2 norm of the X rows of the attention set(s), of the
 //     V rows of Wqkv, and max |Wo| -- they pick exact power-of-two scales that
 //     keep V, O and Wo inside fp16 range for the attention and output kernels;
@@ -12,8 +13,12 @@ namespace vggt {
 
 // RoPE table entry (pos, i) = (cos, sin)(pos * base^(-i/16)) for the 16
 // frequencies of a 32-feature half of a 64-wide head; angles in double.
-__global__ void prep_kernel(float* scal, int nscal, float2* rope, int npos, float base) {
+// Also clears `nsums` floats at `sums` (subsampled mode: the discarded-token
+// sums the CORE stage accumulates).
+__global__ void prep_kernel(float* scal, int nscal, float* sums, int nsums, float2* rope, int npos,
+                            float base) {
   for (int i = threadIdx.x; i < nscal; i += blockDim.x) scal[i] = 0.f;
+  for (int i = threadIdx.x; i < nsums; i += blockDim.x) sums[i] = 0.f;
   for (int i = threadIdx.x; i < npos * 16; i += blockDim.x) {
     int pos = i >> 4, f = i & 15;
     double theta = pow((double)base, -(double)f / 16.0);
@@ -133,8 +138,10 @@ static int grid_for(int64_t work, int per_block, int cap) {
 
 hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   Scalars* sc = ws_scalars(p, a);
+  const bool sub = p.mode == VGGT_ATTN_MODE_SUBSAMPLED;
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(sc),
-                     4 + p.H, ws_rope(p, a), p.rope_npos, p.base);
+                     4 + p.H, sub ? ws_sums(p, a) : nullptr, sub ? 128 * p.H : 0, ws_rope(p, a),
+                     p.rope_npos, p.base);
   // X rows of the set(s): walk the workspace rows through the row map.
   hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 16, 2048)), dim3(256), 0, st,
                      a.X, p.rows, p.d, p.map, &sc->xnorm);
