@@ -106,7 +106,8 @@ def token_positions(t_in_frame: np.ndarray, grid_w: int):
     t = np.asarray(t_in_frame, dtype=np.int64)
     is_patch = t >= N_SPECIAL
     p = np.where(is_patch, t - N_SPECIAL, 0)
-    return is_patch, p // grid_w, p % grid_w
+    gw = max(grid_w, 1)  # a grid without patches has only special tokens
+    return is_patch, p // gw, p % gw
 
 
 def rope_angles(pos: np.ndarray, dh: int, base: float) -> np.ndarray:
