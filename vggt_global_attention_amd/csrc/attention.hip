@@ -246,57 +246,88 @@ __device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs,
 // was discarded (a kept token's diagonal is already in the loop), and the
 // mean key / value pair of the discarded tokens, which fills the row's other
 // n_i discarded columns (logit + log2 n_i).  Rescales O and l to the new
-// reference like one more online-softmax step, in fp32.
-template <int QB, bool RES>
-__device__ __forceinline__ void sga_columns(Rows<QB, RES>& R, const AttnArgs& p, int hd,
-                                            int qloc0, int j, int h) {
+// reference like one more online-softmax step, in fp32.  One query block at a
+// time, loads issued before the arithmetic that uses them.
+template <int QB, bool RES, int QBI>
+__device__ __forceinline__ void sga_block(Rows<QB, RES>& R, const AttnArgs& p, int hd, int qloc0,
+                                          int j, int h) {
+  const int row = qloc0 + QBI * 32 + j;  // = token index: one set, identity row map
+  if (row >= p.L) return;                // lanes j and j + 32 leave together
+  const int t = row % p.T;
+  bool kept = true;
+  if (t >= kSpecial) {
+    const int pidx = t - kSpecial, r = pidx / p.gw, c = pidx - r * p.gw;
+    kept = (r % p.sub_h) == 0 && (c % p.sub_w) == 0;
+  }
   const float* sk = p.sums + hd * 128;
   const float* sv = sk + 64;
-  const float inv = p.nD > 0 ? 1.f / (float)p.nD : 0.f;
-  const f16* kh = p.k_all + (int64_t)hd * p.rows * kDh;
-  const f16* vh = p.vt_all + (int64_t)hd * kDh * p.rows;
+  // this lane's 32 features of the token's own key (q layout) and value (O layout)
+  f16x8 kd[4];
+  f16 vd[2][16];
+  if (!kept) {
+    const f16* krow = p.k_all + ((int64_t)hd * p.rows + row) * kDh + h * 8;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qloc0 + qb * 32 + j;  // = token index: one set, identity row map
-    if (row >= p.L) continue;             // lanes j and j + 32 skip together
-    const int t = row % p.T;
-    bool kept = true;
-    if (t >= kSpecial) {
-      const int pidx = t - kSpecial, r = pidx / p.gw, c = pidx - r * p.gw;
-      kept = (r % p.sub_h) == 0 && (c % p.sub_w) == 0;
-    }
-    float sd = 0.f, sm = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      f16x8 kd = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (!kept) kd = *reinterpret_cast<const f16x8*>(kh + (int64_t)row * kDh + dc * 16 + h * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float qv = (float)R.qf[qb][dc][e];
-        sd = fmaf(qv, (float)kd[e], sd);
-        sm = fmaf(qv, sk[dc * 16 + h * 8 + e], sm);
-      }
-    }
-    sd += __shfl_xor(sd, 32);
-    sm += __shfl_xor(sm, 32);
-    const int n = p.nD - (kept ? 0 : 1);
-    const float s_d = kept ? -INFINITY : sd;
-    const float s_m = n > 0 ? sm * inv + __log2f((float)n) : -INFINITY;
-    const float mn = fmaxf(R.m[qb], fmaxf(s_d, s_m));
-    const float al = __builtin_amdgcn_exp2f(R.m[qb] - mn);
-    const float pd = __builtin_amdgcn_exp2f(s_d - mn), pm = __builtin_amdgcn_exp2f(s_m - mn);
-    R.l[qb] = R.l[qb] * al + (h == 0 ? pd + pm : 0.f);
+    for (int dc = 0; dc < 4; ++dc) kd[dc] = *reinterpret_cast<const f16x8*>(krow + dc * 16);
     const int64_t slot = ((int64_t)row & ~(int64_t)15) | (((row >> 2) & 1) << 3) |
                          (((row >> 3) & 1) << 2) | (row & 3);
+    const f16* vcol = p.vt_all + ((int64_t)hd * kDh + 4 * h) * p.rows + slot;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int f = db * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float vd = kept ? 0.f : (float)vh[(int64_t)f * p.rows + slot];
-        R.O[db][qb][r] = fmaf(R.O[db][qb][r], al, fmaf(pd, vd, pm * (sv[f] * inv)));
+      for (int r = 0; r < 16; ++r)
+        vd[db][r] = vcol[(int64_t)(db * 32 + 8 * (r >> 2) + (r & 3)) * p.rows];
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) kd[dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vd[db][r] = (f16)0.f;
+  }
+  float sd = 0.f, sm = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < 4; ++dc) {
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(sk + dc * 16 + h * 8);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(sk + dc * 16 + h * 8 + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qv = (float)R.qf[QBI][dc][e];
+      sd = fmaf(qv, (float)kd[dc][e], sd);
+      sm = fmaf(qv, e < 4 ? k0[e & 3] : k1[e & 3], sm);
+    }
+  }
+  sd += __shfl_xor(sd, 32);
+  sm += __shfl_xor(sm, 32);
+  const float inv = p.nD > 0 ? 1.f / (float)p.nD : 0.f;
+  const int n = p.nD - (kept ? 0 : 1);
+  const float s_d = kept ? -INFINITY : sd;
+  const float s_m = n > 0 ? sm * inv + __log2f((float)n) : -INFINITY;
+  const float mn = fmaxf(R.m[QBI], fmaxf(s_d, s_m));
+  const float al = __builtin_amdgcn_exp2f(R.m[QBI] - mn);
+  const float pd = __builtin_amdgcn_exp2f(s_d - mn), pm = __builtin_amdgcn_exp2f(s_m - mn);
+  R.l[QBI] = R.l[QBI] * al + (h == 0 ? pd + pm : 0.f);
+  const float pmi = pm * inv;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(sv + db * 32 + 8 * rq + 4 * h);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int r = 4 * rq + r4;
+        R.O[db][QBI][r] = fmaf(R.O[db][QBI][r], al, fmaf(pd, (float)vd[db][r], pmi * vb[r4]));
       }
-    R.m[qb] = mn;
+    }
+  R.m[QBI] = mn;
+}
+
+template <int QB, bool RES>
+__device__ __forceinline__ void sga_columns(Rows<QB, RES>& R, const AttnArgs& p, int hd,
+                                            int qloc0, int j, int h) {
+  sga_block<QB, RES, 0>(R, p, hd, qloc0, j, h);
+  if constexpr (QB > 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    sga_block<QB, RES, 1>(R, p, hd, qloc0, j, h);
   }
 }
 

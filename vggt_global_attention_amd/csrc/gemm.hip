@@ -18,7 +18,7 @@
 // other 32 sit in lane l^32, and both RoPE partners (r, r+8) in the lane
 // itself.  LDS tiles are 128-byte rows with the 16-byte chunk index XOR-ed with
 // row bits 0..2 and bit 3 (conflict-free for 32-row operand reads);
-// global->LDS is double buffered through registers.
+// global->LDS goes through registers, each k-step loaded two k-steps ahead.
 #include "plan.h"
 
 namespace vggt {
@@ -108,24 +108,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  // Global -> LDS staging: two register sets, so each k-step's loads are
+  // issued two k-steps before they are stored (the X / O stream comes from
+  // HBM; one k-step of MFMAs does not cover its latency).
+  u32x4 ra[2][4], rb[2][4];
+  auto gload = [&](int kt, u32x4 (&A4)[4], u32x4 (&B4)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + kt * kGemmBK);
+    for (int i = 0; i < 4; ++i) A4[i] = *reinterpret_cast<const u32x4*>(aptr[i] + kt * kGemmBK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (EPI == kEpiQKV) {
-        rb[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + kt * kGemmBK) : u32x4{0, 0, 0, 0};
+        B4[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + kt * kGemmBK) : u32x4{0, 0, 0, 0};
       } else {
-        rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + (int64_t)kt * g.rows * kDh);
+        B4[i] = *reinterpret_cast<const u32x4*>(bptr[i] + (int64_t)kt * g.rows * kDh);
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4 (&A4)[4], const u32x4 (&B4)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][soff[i]]) = ra[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][soff[i]]) = A4[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][1][soff[i]]) = rb[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&smem[buf][1][soff[i]]) = B4[i];
   };
 
   f32x16 acc[2][2];
@@ -136,13 +139,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int nk = g.K / kGemmBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  auto compute = [&](int buf) {
     const char* As = smem[buf][0];
     const char* Bs = smem[buf][1];
 #pragma unroll
@@ -159,7 +156,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32x32x16(af[fb], bfr[tb], acc[fb][tb]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  // nk = K / 64 is even (K is a multiple of 128); the loop is unrolled by two
+  // so that the register sets keep static indices.  At the top of step kt,
+  // LDS buffer kt&1 holds k-step kt and set (kt+1)&1 has k-step kt+1 in flight.
+  const int nk = g.K / kGemmBK;
+  gload(0, ra[0], rb[0]);
+  gload(1, ra[1], rb[1]);
+  sstore(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) gload(kt + 2, ra[0], rb[0]);
+    compute(0);
+    sstore(1, ra[1], rb[1]);
+    __syncthreads();
+    if (kt + 3 < nk) gload(kt + 3, ra[1], rb[1]);
+    compute(1);
+    if (kt + 2 < nk) sstore(0, ra[0], rb[0]);
     __syncthreads();
   }
 
