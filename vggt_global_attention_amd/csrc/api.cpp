@@ -84,7 +84,7 @@ int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p)
   p->sub_w = sub_w;
   if (subsampled) {
     p->Lk = (int)(kept_per_frame(s, sub_h, sub_w) * s->S);
-    p->kv_rows = round_up(p->Lk, kRowAlign);
+    p->kv_rows = round_up(p->Lk, kKvAlign);
     p->kv_seq_stride = round_up(p->Lk, kAttnBK);
     p->nD = (int)(N - p->Lk);
     // the subsampled kernel has a single tile shape

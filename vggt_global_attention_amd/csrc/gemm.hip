@@ -28,6 +28,7 @@ struct GemmArgs {
   const void* B;  // QKV: X bf16 [S*T][d] through `map`; OUT: O fp16 [H][rows][64]
   int64_t rows;   // workspace rows (multiple of 128)
   int Nf, K;
+  int fgroups;    // output-feature groups walked one after the other (divides Nf / 128)
   RowMap map;
   int T, gw, off, d;
   float eps;
@@ -65,20 +66,25 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int wm = wave & 1, wn = wave >> 1;
   const int j = lane & 31, h = lane >> 5;
 
-  // Block order.  Blocks go to the 8 XCDs round-robin.  When the output
-  // features split evenly, XCD x owns feature tiles [x*ntn/8, (x+1)*ntn/8):
-  // that slice of the weights (768 KB of Wqkv, 256 KB of Wo at d = 1024) stays
-  // in the XCD's L2 while token tiles stream past, each reused for the XCD's
-  // few feature tiles back to back.  Otherwise fall back to one contiguous
-  // range of (token tile, feature tile) per XCD.
+  // Block order.  Blocks go to the 8 XCDs round-robin (block b runs on XCD
+  // b % 8).  When the token tiles split evenly, XCD x owns token tiles
+  // [x*ntm/8, (x+1)*ntm/8) -- every X (or O) row is fetched from HBM by one
+  // XCD only -- and walks them once per group of output features, all token
+  // tiles of a group before the next group: the group's slice of the weights
+  // (fgroups is picked on the host so that a slice is about 2 MB) stays in
+  // the XCD's L2 while the token tiles stream past, and X is read fgroups
+  // times in all.  Otherwise fall back to one contiguous range of (token
+  // tile, feature tile) per XCD.
   const int ntn = g.Nf / kGemmBN;
+  const int ntm = gridDim.x / ntn;
   int64_t m0;
   int n0;
-  if (ntn % kXcds == 0) {
-    const int per = ntn / kXcds;
+  if (ntm % kXcds == 0 && ntn % g.fgroups == 0) {
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    m0 = (int64_t)(slot / per) * kGemmBM;
-    n0 = (xcd * per + slot % per) * kGemmBN;
+    const int ntt = ntm / kXcds, pf = ntn / g.fgroups;
+    const int fg = slot / (ntt * pf), rem = slot - fg * ntt * pf;
+    m0 = (int64_t)(xcd * ntt + rem / pf) * kGemmBM;
+    n0 = (fg * pf + rem % pf) * kGemmBN;
   } else {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     m0 = (int64_t)(logical / ntn) * kGemmBM;
@@ -307,6 +313,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// Smallest number of output-feature groups (a divisor of the feature tile
+// count) whose weight slice fits a ~2 MB share of an XCD's 4 MB L2.
+static int feature_groups(int nf, int k, int elem_bytes) {
+  const int ntn = nf / kGemmBN;
+  const int64_t bytes = (int64_t)nf * k * elem_bytes;
+  for (int gcount = 1; gcount < ntn; ++gcount)
+    if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)2 << 20)) return gcount;
+  return ntn;
+}
+
 static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   GemmArgs g{};
   g.rows = p.rows;
@@ -335,6 +351,7 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.B = a.X;
   g.Nf = 3 * p.d;
   g.K = p.d;
+  g.fgroups = feature_groups(g.Nf, g.K, 2);
   const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
   hipLaunchKernelGGL(gemm_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
   return hipGetLastError();
@@ -348,6 +365,7 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.B = ws_q(p, a);  // the attention kernel leaves O in place of q
   g.Nf = p.d;
   g.K = p.d;
+  g.fgroups = feature_groups(g.Nf, g.K, 2);
   const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
   hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
   hipError_t e = hipGetLastError();
