@@ -19,6 +19,8 @@
 // itself.  LDS tiles are 128-byte rows with the 16-byte chunk index XOR-ed with
 // row bits 0..2 and bit 3 (conflict-free for 32-row operand reads);
 // global->LDS goes through registers, each k-step loaded two k-steps ahead.
+#include <stdlib.h>
+
 #include "plan.h"
 
 namespace vggt {
@@ -54,6 +56,140 @@ struct GemmTypes<kEpiOut> {
 
 __device__ __forceinline__ int swz(int row, int col) {
   return row * 128 + ((col ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
+
+// Epilogue of one wave's block: acc[fb][tb][r] holds feature
+// fbase + fb*32 + fo(r) of token (workspace row) mbase + tb*32 + j, with
+// fo(r) = 8*(r/4) + 4*h + r%4; the 64 features are one head (fb = 0 its first
+// half).
+template <int EPI, int TB>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2][TB],
+                                              int64_t mbase, int fbase, int j, int h, int lane) {
+  if (EPI == kEpiQKV) {
+    const int blk = fbase / g.d;  // 0: q, 1: k, 2: v
+    const int hd = (fbase - blk * g.d) / kDh;
+    if (blk < 2) {
+      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
+      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
+      float gm[2][16], bt[2][16];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          gm[fb][r] = gam[f];
+          bt[fb][r] = bet[f];
+        }
+      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
+      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
+      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
+      float kmx = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int64_t w = mbase + tb * 32 + j;
+        const int64_t src = g.map.src(w);
+        float s1 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
+        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
+        float s2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dv = acc[fb][tb][r] - mean;
+            s2 = fmaf(dv, dv, s2);
+          }
+        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
+        const float rstd = 1.f / sqrtf(var + g.eps);
+        float y[2][16];
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
+        if (src >= 0) {
+          const int t = (int)(src % g.T);
+          if (t >= kSpecial) {
+            const int pidx = t - kSpecial;
+            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                // feature i of the half pairs with i + 16: registers r and r + 8
+                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+                const float2 cs = g.rope[pos[fb] * 16 + i];
+                const float a = y[fb][r], b = y[fb][r + 8];
+                y[fb][r] = a * cs.x - b * cs.y;
+                y[fb][r + 8] = b * cs.x + a * cs.y;
+              }
+          }
+        }
+        float n2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            f16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
+              const float back = (float)o[r];
+              n2 = fmaf(back, back, n2);
+            }
+            *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 32 + 8 * rq + 4 * h) = o;
+          }
+        n2 += __shfl_xor(n2, 32);
+        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
+      }
+      if (blk == 1) {
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
+      }
+    } else {
+      const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+      f16* dst = g.vt + (int64_t)hd * kDh * g.rows;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int64_t w = mbase + tb * 32 + j;
+        // Key position inside its aligned group of 16: key 8a + 4c + b is
+        // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
+        // the attention kernel's MFMA consumes probabilities.
+        const int64_t pos = (w & ~(int64_t)15) | (((w >> 2) & 1) << 3) | (((w >> 3) & 1) << 2) | (w & 3);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            dst[(int64_t)e * g.rows + pos] = (f16)ldexpf(acc[fb][tb][r], kv);
+          }
+      }
+    }
+  } else {
+    const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+    const int ws = range_exponent(g.sc->woabs);
+    const float scale = ldexpf(1.f, -(kv + ws));
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t w = mbase + tb * 32 + j;
+      const int64_t src = g.map.src(w);
+      if (src < 0) continue;
+      bf16* dst = g.y + src * g.d + fbase + 4 * h;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][4 * rq + r] * scale);
+          *reinterpret_cast<bf16x4*>(dst + fb * 32 + 8 * rq) = o;
+        }
+    }
+  }
 }
 
 template <int EPI>
@@ -183,134 +319,144 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // acc[fb][tb][r]: feature n0 + wn*64 + fb*32 + fo(r) of token m0 + wm*64 + tb*32 + j,
-  // fo(r) = 8*(r/4) + 4*h + r%4.  Block fb = 0 is the first half of the head.
-  if (EPI == kEpiQKV) {
-    const int fbase = n0 + wn * 64;
-    const int blk = fbase / g.d;  // 0: q, 1: k, 2: v
-    const int hd = (fbase - blk * g.d) / kDh;
-    if (blk < 2) {
-      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
-      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
-      float gm[2][16], bt[2][16];
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          gm[fb][r] = gam[f];
-          bt[fb][r] = bet[f];
-        }
-      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
-      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
-      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
-      float kmx = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int64_t w = m0 + wm * 64 + tb * 32 + j;
-        const int64_t src = g.map.src(w);
-        float s1 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
-        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
-        float s2 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dv = acc[fb][tb][r] - mean;
-            s2 = fmaf(dv, dv, s2);
-          }
-        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
-        const float rstd = 1.f / sqrtf(var + g.eps);
-        float y[2][16];
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
-        if (src >= 0) {
-          const int t = (int)(src % g.T);
-          if (t >= kSpecial) {
-            const int pidx = t - kSpecial;
-            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-              for (int r = 0; r < 8; ++r) {
-                // feature i of the half pairs with i + 16: registers r and r + 8
-                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float2 cs = g.rope[pos[fb] * 16 + i];
-                const float a = y[fb][r], b = y[fb][r + 8];
-                y[fb][r] = a * cs.x - b * cs.y;
-                y[fb][r + 8] = b * cs.x + a * cs.y;
-              }
-          }
-        }
-        float n2 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            f16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
-              const float back = (float)o[r];
-              n2 = fmaf(back, back, n2);
-            }
-            *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 32 + 8 * rq + 4 * h) = o;
-          }
-        n2 += __shfl_xor(n2, 32);
-        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
-      }
-      if (blk == 1) {
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
-      }
-    } else {
-      const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
-      f16* dst = g.vt + (int64_t)hd * kDh * g.rows;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int64_t w = m0 + wm * 64 + tb * 32 + j;
-        // Key position inside its aligned group of 16: key 8a + 4c + b is
-        // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
-        // the attention kernel's MFMA consumes probabilities.
-        const int64_t pos = (w & ~(int64_t)15) | (((w >> 2) & 1) << 3) | (((w >> 3) & 1) << 2) | (w & 3);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            dst[(int64_t)e * g.rows + pos] = (f16)ldexpf(acc[fb][tb][r], kv);
-          }
-      }
-    }
+  gemm_epilogue<EPI, 2>(g, acc, m0 + wm * 64, n0 + wn * 64, j, h, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel: 256 token rows x 128 output features per workgroup, 4 waves of
+// 128 x 64 (one head for 128 tokens; 8 MFMA blocks, 0.75 KB of LDS operand
+// reads per MFMA instead of 1 KB), 32-deep k-steps, operands copied
+// global -> LDS by the load unit itself (global_load_lds, 16 bytes per lane)
+// three k-steps deep, so there is no register staging and no ds_write.  LDS
+// rows are 64 bytes; chunk c of row r sits at chunk c ^ ((r >> 2) & 3), which
+// spreads a 32-row operand read over all 16-byte bank groups.  A DMA
+// instruction fills 16 consecutive rows (1 KB), lane i row i/4 and chunk i%4,
+// so lane i fetches source chunk (i%4) ^ ((i/16) & 3).
+// ---------------------------------------------------------------------------
+constexpr int kDmaBM = 256, kDmaBN = 128, kDmaBK = 32, kDmaStages = 3;
+
+__device__ __forceinline__ int swz64(int row, int col) {
+  return row * 64 + ((col ^ ((row >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
+  typedef typename GemmTypes<EPI>::V8 V8;
+  constexpr int kAB = kDmaBN * 64;  // A stage: 128 feature rows x 64 B
+  constexpr int kBB = kDmaBM * 64;  // B stage: 256 token rows x 64 B
+  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages][kAB + kBB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int j = lane & 31, h = lane >> 5;
+
+  // Block order: as gemm_kernel, with 256-row token tiles.
+  const int ntn = g.Nf / kDmaBN;
+  const int ntm = gridDim.x / ntn;
+  int64_t m0;
+  int n0;
+  if (ntm % kXcds == 0 && ntn % g.fgroups == 0) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int ntt = ntm / kXcds, pf = ntn / g.fgroups;
+    const int fg = slot / (ntt * pf), rem = slot - fg * ntt * pf;
+    m0 = (int64_t)(xcd * ntt + rem / pf) * kDmaBM;
+    n0 = (fg * pf + rem % pf) * kDmaBN;
   } else {
-    const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
-    const int ws = range_exponent(g.sc->woabs);
-    const float scale = ldexpf(1.f, -(kv + ws));
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    m0 = (int64_t)(logical / ntn) * kDmaBM;
+    n0 = (logical % ntn) * kDmaBN;
+  }
+
+  // DMA sources of this lane: A rows (q*4 + wave)*16 + lane/4 (q < 2), B rows
+  // likewise (q < 4); column chunk (lane%4) ^ ((lane/16) & 3).
+  const int lrow = lane >> 2, lcol = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A);
+  const uint16_t* Bb = reinterpret_cast<const uint16_t*>(g.B);
+  const uint16_t* aptr[2];
+  const uint16_t* bptr[4];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int64_t w = m0 + wm * 64 + tb * 32 + j;
+  for (int q = 0; q < 2; ++q)
+    aptr[q] = A + (int64_t)(n0 + (q * 4 + wave) * 16 + lrow) * g.K + lcol * 8;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t w = m0 + (q * 4 + wave) * 16 + lrow;
+    if (EPI == kEpiQKV) {
+      // rows without a token read X row 0: finite values whose outputs are
+      // masked keys or never read
       const int64_t src = g.map.src(w);
-      if (src < 0) continue;
-      bf16* dst = g.y + src * g.d + n0 + wn * 64 + 4 * h;
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][4 * rq + r] * scale);
-          *reinterpret_cast<bf16x4*>(dst + fb * 32 + 8 * rq) = o;
-        }
+      bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
+    } else {
+      bptr[q] = Bb + w * kDh + lcol * 8;
     }
   }
+  auto dma = [&](int kt, int stage) {
+    char* base = &smem[stage][0];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(aptr[q] + kt * kDmaBK, base + (q * 4 + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint16_t* src = EPI == kEpiQKV
+                                ? bptr[q] + kt * kDmaBK
+                                : bptr[q] + (int64_t)(kt >> 1) * g.rows * kDh + (kt & 1) * kDmaBK;
+      dma16(src, base + kAB + (q * 4 + wave) * 1024);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  auto compute = [&](int stage) {
+    const char* As = &smem[stage][0];
+    const char* Bs = As + kAB;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      V8 af[2], bfr[4];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+        af[fb] = *reinterpret_cast<const V8*>(As + swz64(wn * 64 + fb * 32 + j, kc * 2 + h));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz64(wm * 128 + tb * 32 + j, kc * 2 + h));
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mfma32x32x16(af[fb], bfr[tb], acc[fb][tb]);
+    }
+  };
+
+  // Six DMA instructions per wave per k-step.  At the end of step kt, step
+  // kt+1 must have landed; step kt+2 may still be in flight (vmcnt <= 6).
+  // The barrier is the bare s_barrier: a __syncthreads() would also wait for
+  // every outstanding load, in-flight prefetch included.  Reuse is safe: the
+  // buffer step kt+2 overwrites was last read in step kt-1, before the
+  // barrier that closed it.
+  constexpr int kVm6 = 0x0F76, kVm0 = 0x0F70;  // s_waitcnt vmcnt(6) / vmcnt(0)
+  const int nk = g.K / kDmaBK;
+  dma(0, 0);
+  dma(1, 1);
+  __builtin_amdgcn_s_waitcnt(kVm6);
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 2 < nk;
+    if (more) dma(kt + 2, (kt + 2) % kDmaStages);
+    compute(kt % kDmaStages);
+    if (more) __builtin_amdgcn_s_waitcnt(kVm6);
+    else __builtin_amdgcn_s_waitcnt(kVm0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  gemm_epilogue<EPI, 4>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane);
 }
 
 // Smallest number of output-feature groups (a divisor of the feature tile
@@ -321,6 +467,14 @@ static int feature_groups(int nf, int k, int elem_bytes) {
   for (int gcount = 1; gcount < ntn; ++gcount)
     if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)2 << 20)) return gcount;
   return ntn;
+}
+
+// The DMA kernel needs whole 256-row token tiles; VGGT_GEMM=0 forces the
+// register-staged 128 x 128 kernel (a tuning / comparison switch).
+static bool use_dma_gemm(const Plan& p) {
+  if (p.rows % kDmaBM != 0) return false;
+  const char* e = getenv("VGGT_GEMM");
+  return !(e && atoi(e) == 0);
 }
 
 static GemmArgs base_args(const Plan& p, const Ptrs& a) {
@@ -352,8 +506,13 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.Nf = 3 * p.d;
   g.K = p.d;
   g.fgroups = feature_groups(g.Nf, g.K, 2);
-  const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
-  hipLaunchKernelGGL(gemm_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+  if (use_dma_gemm(p)) {
+    const int blocks = (int)(p.rows / kDmaBM) * (g.Nf / kDmaBN);
+    hipLaunchKernelGGL(gemm_dma_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+  } else {
+    const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
+    hipLaunchKernelGGL(gemm_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 
@@ -366,8 +525,13 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.Nf = p.d;
   g.K = p.d;
   g.fgroups = feature_groups(g.Nf, g.K, 2);
-  const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
-  hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+  if (use_dma_gemm(p)) {
+    const int blocks = (int)(p.rows / kDmaBM) * (g.Nf / kDmaBN);
+    hipLaunchKernelGGL(gemm_dma_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+  } else {
+    const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
+    hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.mode == VGGT_ATTN_MODE_REGISTER && a.Y != a.X) return launch_patch_copy(p, a, st);

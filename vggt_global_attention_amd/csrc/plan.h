@@ -15,7 +15,7 @@ constexpr int kGemmBM = 128;        // token rows per GEMM tile
 constexpr int kGemmBN = 128;        // output features per GEMM tile (two heads)
 constexpr int kGemmBK = 64;
 constexpr int kAttnBK = 64;         // keys per attention tile
-constexpr int kRowAlign = 1024;     // workspace rows are padded to this (8 XCDs x 128-row tiles)
+constexpr int kRowAlign = 2048;     // workspace rows are padded to this (8 XCDs x 256-row tiles)
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
 
 struct Plan {
