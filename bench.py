@@ -85,15 +85,20 @@ def gpu_inputs(w):
     return inp, {k: inp[k].to("cuda").contiguous() for k in keys}
 
 
-def time_block(w, mode, d, steps, warmup, sub=(1, 1)):
+def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None):
     """ms per full call and ms per attention-core stage, both with HIP events
-    on the stream the library launches on (torch's current stream)."""
+    on the stream the library launches on (torch's current stream).  rows =
+    (begin, count): the query-row window of the global block instead."""
     import torch
     from vggt_global_attention_amd import api
     from vggt_global_attention_amd import binding as B
-    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
     args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
-    Y = torch.empty_like(d["X"])
+    if rows is not None:
+        blk = api.RowsBlock(d["X"], w.H, w.grid_h, w.grid_w, rows[0], rows[1])
+        Y = torch.empty((rows[1], w.d), dtype=d["X"].dtype, device=d["X"].device)
+    else:
+        blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
+        Y = torch.empty_like(d["X"])
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         blk(*args, Y=Y)
@@ -257,6 +262,15 @@ def main():
             if dd is not d:
                 del dd
             torch.cuda.empty_cache()
+        # one GPU's share of a query-row split over 8 GPUs: N/8 queries, all N keys
+        share = (w.N + 7) // 8
+        print("[bench] extra s100 global rows share 1/8", file=sys.stderr, flush=True)
+        m2, c2 = time_block(w, "global", d, max(3, a.steps // 2), 2, rows=(3 * share, share))
+        attn = 4.0 * share * w.N * w.d
+        gemm = 4.0 * w.N * w.d ** 2 + 4.0 * share * w.d ** 2  # k, v for all; q and Wo for the share
+        extra["s100_global_rows_share1of8"] = {"ms_per_layer": m2, "tflops": (attn + gemm) / m2 / 1e9,
+                                               "core_ms": c2, "core_tflops": attn / c2 / 1e9,
+                                               "query_rows": share, "key_rows": w.N}
         out["extra"] = extra
     if not a.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

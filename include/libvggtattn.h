@@ -25,6 +25,8 @@
  *     a copy of X (patch tokens keep to their own frame in this block).
  *   - vggt_attn_global_subsampled: global mode with AVGGT's subsampled keys and
  *     values (see its declaration).
+ *   - vggt_attn_global_rows: a window of query rows of the global mode (one
+ *     GPU's share of a query-row split; see its declaration).
  *
  * Conventions for every entry point below:
  *   - Tensor pointers are DEVICE pointers on the current HIP device; dense,
@@ -69,7 +71,7 @@ extern "C" {
 #define VGGT_ATTN_EWORKSPACE (-4) /* workspace smaller than vggt_attn_workspace_bytes() */
 #define VGGT_ATTN_EHIP       (-5) /* the HIP runtime rejected a launch */
 #define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of
-                                     range, subsampling window < 1 */
+                                     range, subsampling window < 1, row window outside the set */
 
 /* Block modes. */
 #define VGGT_ATTN_MODE_FRAME    0
@@ -139,6 +141,23 @@ int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int
                                 const float* k_gamma, const float* k_beta, void* Y,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Rows [row_begin, row_begin + row_count) of the global block's output: the
+   queries of those tokens (flat index s*T + t) attend to every token of the
+   set, exactly as in vggt_attn_global.  This is one GPU's share when the
+   global set is split across GPUs by query rows ("HTTM" article, section 02,
+   and the AVGGT summary, technical summary 1: the global set is one long
+   sequence whose keys every query needs); on one GPU it computes keys and
+   values for all tokens and queries, attention and the output projection for
+   the window only.  Y_rows is bf16 [row_count][d] (row i = token
+   row_begin + i).  Requires 0 <= row_begin, 1 <= row_count,
+   row_begin + row_count <= S*T (else VGGT_ATTN_ERANGE).  Workspace:
+   vggt_attn_workspace_bytes(VGGT_ATTN_MODE_GLOBAL).  The rows are bitwise
+   those vggt_attn_global writes for them. */
+int vggt_attn_global_rows(const vggt_attn_shape* shape, int64_t row_begin, int64_t row_count,
+                          const void* X, const void* Wqkv, const void* Wo, const float* q_gamma,
+                          const float* q_beta, const float* k_gamma, const float* k_beta,
+                          void* Y_rows, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One stage of a call in `mode` (VGGT_ATTN_STAGE_*), same arguments and
    checks as the full call.  Running the four stages in order on one stream
    with one workspace is exactly the full call; a stage reads what the
@@ -155,6 +174,13 @@ int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t 
                                const float* q_gamma, const float* q_beta, const float* k_gamma,
                                const float* k_beta, void* Y, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* One stage of vggt_attn_global_rows, as vggt_attn_stage. */
+int vggt_attn_global_rows_stage(int stage, const vggt_attn_shape* shape, int64_t row_begin,
+                                int64_t row_count, const void* X, const void* Wqkv,
+                                const void* Wo, const float* q_gamma, const float* q_beta,
+                                const float* k_gamma, const float* k_beta, void* Y_rows,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* vggt_attn_status_str(int status);

@@ -167,3 +167,33 @@ def test_subsampled_stage_errors():
                                         None) == B.ERANGE
     assert B.vggt_attn_subsampled_stage(B.STAGE_CORE, s, 3, 3, *a, 0x10000000, 16,
                                         None) == B.EWORKSPACE
+
+
+# ----------------------------------------------------------------------------
+# Query-row window of the global block
+# ----------------------------------------------------------------------------
+
+def rows_fn(begin, count):
+    def fn(s, *rest):
+        return B.vggt_attn_global_rows(s, begin, count, *rest)
+    return fn
+
+
+def test_global_rows_errors():
+    s = B.make_shape(**TINY)               # N = 162
+    ws = B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, s)
+    for begin, count in ((-1, 10), (0, 0), (0, -5), (100, 63), (162, 1), (0, 163)):
+        assert call(rows_fn(begin, count), s, ws_bytes=ws) == B.ERANGE, (begin, count)
+    fn = rows_fn(10, 20)
+    assert call(fn, s, ws_bytes=ws, X=0) == B.EINVAL
+    assert call(fn, s, ws_bytes=ws, Y=0x100008) == B.EALIGN
+    assert call(fn, s, ws_bytes=ws - 256) == B.EWORKSPACE
+    # Y holds 20 rows x 256 features x 2 bytes: overlapping X's first bytes is rejected,
+    # ending right before X is fine (the call then fails only later, on the fake pointers,
+    # so check the aliasing verdict through a too-small workspace instead)
+    assert call(fn, s, ws_bytes=ws, Y=0x100000 - 20 * 256 * 2 + 16) == B.EINVAL
+    assert call(fn, s, ws_bytes=16, Y=0x100000 - 20 * 256 * 2) == B.EWORKSPACE
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    assert B.vggt_attn_global_rows_stage(9, s, 0, 10, *a, 0x10000000, ws, None) == B.EINVAL
+    assert B.vggt_attn_global_rows_stage(B.STAGE_CORE, s, 0, 0, *a, 0x10000000, ws,
+                                         None) == B.ERANGE

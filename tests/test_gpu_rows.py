@@ -1,0 +1,75 @@
+"""GPU checks of the query-row window of the global block (one GPU's share of a
+query-row split): the rows are bitwise those of the full global call, and they
+match the fp64 oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vggt_global_attention_amd import api, configs, synth
+from vggt_global_attention_amd import binding as B
+from helpers import assert_parity, f64, oracle_params
+from gpu_common import log, np64, require_gpu, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = configs.WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def rows_call(w, d, begin, count):
+    blk = api.RowsBlock(d["X"], w.H, w.grid_h, w.grid_w, begin, count)
+    y = blk(d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name", ["tiny", "s24"])
+def test_rows_bitwise_equal_global(name):
+    w = W[name]
+    d = to_dev(synth.make_inputs(w))
+    full = run("global", w, d).reshape(-1, w.d)
+    N = w.N
+    windows = [(0, N), (0, (N + 7) // 8), (N // 3, 1), (N - 100, 100), (17, min(513, N - 17)),
+               (N // 2, N // 4)]
+    for begin, count in windows:
+        log(f"[case] {name} rows [{begin}, {begin + count})")
+        y = rows_call(w, d, begin, count)
+        assert y.shape == (count, w.d)
+        assert torch.equal(y, full[begin:begin + count]), (begin, count)
+
+
+def test_rows_s100_share_oracle_and_bitwise():
+    """The 1/8 share of the 100-frame layer (12,888 queries over 103,100 keys)."""
+    w = W["s100"]
+    inp = synth.make_inputs(w)
+    d = to_dev(inp)
+    share = (w.N + 7) // 8
+    begin = 3 * share
+    log(f"[case] s100 rows [{begin}, {begin + share})")
+    y = rows_call(w, d, begin, share)
+    full = run("global", w, d).reshape(-1, w.d)
+    assert torch.equal(y, full[begin:begin + share])
+    rows = np.sort(np.random.default_rng(7).choice(share, 96, replace=False)) + begin
+    ref = oracle.global_attention_rows(f64(inp["X"]), oracle_params(w, inp), rows)
+    assert_parity(np64(y)[rows - begin], ref, "s100/rows-share")
+
+
+def test_rows_stages_equal_full_call():
+    w = W["s24"]
+    d = to_dev(synth.make_inputs(w))
+    blk = api.RowsBlock(d["X"], w.H, w.grid_h, w.grid_w, 1000, 3000)
+    args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+    full = blk(*args).clone()
+    Y = torch.empty_like(full)
+    for st in (B.STAGE_PREP, B.STAGE_QKV, B.STAGE_CORE, B.STAGE_OUT):
+        blk.stage(st, *args, Y)
+    torch.cuda.synchronize()
+    assert torch.equal(full, Y)

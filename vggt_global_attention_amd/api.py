@@ -92,6 +92,38 @@ class Block:
         return Y
 
 
+class RowsBlock:
+    """Rows [row_begin, row_begin + row_count) of the global block (one GPU's
+    share of a query-row split), with its workspace."""
+
+    def __init__(self, X: torch.Tensor, H: int, grid_h: int, grid_w: int, row_begin: int,
+                 row_count: int, rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None):
+        self.inner = Block("global", X, H, grid_h, grid_w, rope_base, ln_eps, pos_offset,
+                           workspace)
+        self.row_begin, self.row_count = int(row_begin), int(row_count)
+
+    def _args(self, X, Wqkv, Wo, qg, qb, kg, kb, Y):
+        return self.inner._args(X, Wqkv, Wo, qg, qb, kg, kb, Y)
+
+    def __call__(self, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y=None, stream=None):
+        if Y is None:
+            Y = torch.empty((self.row_count, X.shape[-1]), dtype=X.dtype, device=X.device)
+        a = self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y)
+        st = B.vggt_attn_global_rows(a[0], self.row_begin, self.row_count, *a[1:],
+                                     _stream_handle(stream))
+        if st != B.OK:
+            raise B.VggtAttnError(st, "vggt_attn_global_rows")
+        return Y
+
+    def stage(self, stage: int, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, stream=None):
+        a = self._args(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y)
+        st = B.vggt_attn_global_rows_stage(stage, a[0], self.row_begin, self.row_count, *a[1:],
+                                           _stream_handle(stream))
+        if st != B.OK:
+            raise B.VggtAttnError(st, "vggt_attn_global_rows_stage")
+        return Y
+
+
 def attention(mode: str, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, H: int, grid_h: int,
               grid_w: int, Y=None, stream=None, sub=(1, 1), **shape_kw):
     """One call of the block in `mode` ('frame', 'global', 'register' or 'subsampled';

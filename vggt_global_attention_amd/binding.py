@@ -18,8 +18,9 @@ MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
          "subsampled": MODE_SUBSAMPLED}
 
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
-           "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_stage",
-           "vggt_attn_subsampled_stage", "vggt_attn_status_str", "vggt_attn_version")
+           "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_global_rows",
+           "vggt_attn_stage", "vggt_attn_subsampled_stage", "vggt_attn_global_rows_stage",
+           "vggt_attn_status_str", "vggt_attn_version")
 
 
 class vggt_attn_shape(ctypes.Structure):
@@ -62,6 +63,11 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.vggt_attn_global_subsampled.argtypes = sub
     L.vggt_attn_subsampled_stage.restype = ctypes.c_int
     L.vggt_attn_subsampled_stage.argtypes = [ctypes.c_int] + sub
+    win = [ctypes.POINTER(vggt_attn_shape), ctypes.c_int64, ctypes.c_int64] + _CALL_ARGS[1:]
+    L.vggt_attn_global_rows.restype = ctypes.c_int
+    L.vggt_attn_global_rows.argtypes = win
+    L.vggt_attn_global_rows_stage.restype = ctypes.c_int
+    L.vggt_attn_global_rows_stage.argtypes = [ctypes.c_int] + win
     L.vggt_attn_status_str.restype = ctypes.c_char_p
     L.vggt_attn_status_str.argtypes = [ctypes.c_int]
     L.vggt_attn_version.restype = ctypes.c_int
@@ -116,6 +122,20 @@ def vggt_attn_subsampled_stage(stage, shape, sub_h, sub_w, X, Wqkv, Wo, q_gamma,
                                k_gamma, k_beta, Y, workspace, workspace_bytes, stream) -> int:
     return _call("vggt_attn_subsampled_stage", stage, ctypes.byref(shape), sub_h, sub_w, X, Wqkv,
                  Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global_rows(shape, row_begin, row_count, X, Wqkv, Wo, q_gamma, q_beta, k_gamma,
+                          k_beta, Y_rows, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_global_rows", ctypes.byref(shape), row_begin, row_count, X, Wqkv, Wo,
+                 q_gamma, q_beta, k_gamma, k_beta, Y_rows, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global_rows_stage(stage, shape, row_begin, row_count, X, Wqkv, Wo, q_gamma,
+                                q_beta, k_gamma, k_beta, Y_rows, workspace, workspace_bytes,
+                                stream) -> int:
+    return _call("vggt_attn_global_rows_stage", stage, ctypes.byref(shape), row_begin, row_count,
+                 X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y_rows, workspace,
+                 workspace_bytes, stream)
 
 
 def status_str(status: int) -> str:

@@ -16,7 +16,8 @@ static int64_t kept_per_frame(const vggt_attn_shape* s, int sub_h, int sub_w) {
   return kSpecial + (int64_t)((s->grid_h + sub_h - 1) / sub_h) * ((s->grid_w + sub_w - 1) / sub_w);
 }
 
-int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p) {
+int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
+  int sub_h = o.sub_h, sub_w = o.sub_w;
   if (!s || !p) return VGGT_ATTN_EINVAL;
   if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
       mode != VGGT_ATTN_MODE_REGISTER && mode != VGGT_ATTN_MODE_SUBSAMPLED)
@@ -33,6 +34,11 @@ int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p)
   const bool subsampled = mode == VGGT_ATTN_MODE_SUBSAMPLED;
   if (!subsampled) sub_h = sub_w = 1;
   if (sub_h < 1 || sub_w < 1) return VGGT_ATTN_ERANGE;
+  const bool window = o.q_count >= 0;
+  if (window) {
+    if (mode != VGGT_ATTN_MODE_GLOBAL) return VGGT_ATTN_EINVAL;
+    if (o.q_begin < 0 || o.q_count < 1 || o.q_begin + o.q_count > N) return VGGT_ATTN_ERANGE;
+  }
 
   memset(p, 0, sizeof(*p));
   p->mode = mode;
@@ -91,17 +97,26 @@ int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p)
     p->attn_qb = 2;
     p->attn_waves = 8;
   } else {
-    p->Lk = p->L;
+    p->Lk = p->L;  // (a query window below moves L, never the keys)
     p->kv_rows = p->rows;
     p->kv_seq_stride = p->seq_stride;
     p->nD = 0;
   }
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled) {
-    p->map = RowMap{p->rows, 0, (int32_t)N, 1};
+    p->map = RowMap{p->rows, 0, (int32_t)N, 1, 0};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
-    p->map = RowMap{p->seq_stride, s->T, s->T, s->S};
+    p->map = RowMap{p->seq_stride, s->T, s->T, s->S, 0};
   } else {
-    p->map = RowMap{kSpecial, s->T, kSpecial, s->S};
+    p->map = RowMap{kSpecial, s->T, kSpecial, s->S, 0};
+  }
+  p->out_map = p->map;
+  p->q0 = 0;
+  p->window = window;
+  if (window) {
+    // keys: every token; queries and outputs: rows [q_begin, q_begin + q_count)
+    p->q0 = (int)o.q_begin;
+    p->L = (int)(o.q_begin + o.q_count);
+    p->out_map = RowMap{p->rows, 0, (int32_t)o.q_count, 1, o.q_begin};
   }
   p->rope_npos = (s->grid_h > s->grid_w ? s->grid_h : s->grid_w) + s->pos_offset;
   if (p->rope_npos < 1) p->rope_npos = 1;
@@ -149,10 +164,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-int check_call(int mode, const vggt_attn_shape* shape, int sub_h, int sub_w, const void* X,
+int check_call(int mode, const vggt_attn_shape* shape, const CallOpts& o, const void* X,
                const void* Wqkv, const void* Wo, const float* qg, const float* qb, const float* kg,
                const float* kb, void* Y, void* ws, size_t ws_bytes, Plan* plan) {
-  int st = make_plan(mode, shape, sub_h, sub_w, plan);
+  int st = make_plan(mode, shape, o, plan);
   if (st != VGGT_ATTN_OK) return st;
   if (!X || !Wqkv || !Wo || !qg || !qb || !kg || !kb || !Y || !ws) return VGGT_ATTN_EINVAL;
   if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(Wqkv, 16) || !aligned(Wo, 16) ||
@@ -160,13 +175,14 @@ int check_call(int mode, const vggt_attn_shape* shape, int sub_h, int sub_w, con
     return VGGT_ATTN_EALIGN;
   if (ws_bytes < plan->total) return VGGT_ATTN_EWORKSPACE;
   const size_t nx = (size_t)plan->S * plan->T * plan->d * 2;
+  const size_t ny = plan->window ? (size_t)(plan->L - plan->q0) * plan->d * 2 : nx;
   const size_t nw = (size_t)3 * plan->d * plan->d * 2, no = (size_t)plan->d * plan->d * 2;
   const size_t ng = (size_t)plan->H * kDh * 4;
   const bool in_place = (mode == VGGT_ATTN_MODE_REGISTER && Y == X);
-  if (!in_place && overlap(Y, nx, X, nx)) return VGGT_ATTN_EINVAL;
-  if (overlap(Y, nx, Wqkv, nw) || overlap(Y, nx, Wo, no) || overlap(Y, nx, qg, ng) ||
-      overlap(Y, nx, qb, ng) || overlap(Y, nx, kg, ng) || overlap(Y, nx, kb, ng) ||
-      overlap(Y, nx, ws, plan->total))
+  if (!in_place && overlap(Y, ny, X, nx)) return VGGT_ATTN_EINVAL;
+  if (overlap(Y, ny, Wqkv, nw) || overlap(Y, ny, Wo, no) || overlap(Y, ny, qg, ng) ||
+      overlap(Y, ny, qb, ng) || overlap(Y, ny, kg, ng) || overlap(Y, ny, kb, ng) ||
+      overlap(Y, ny, ws, plan->total))
     return VGGT_ATTN_EINVAL;
   // The workspace is written by the library: it must not hold any input.
   if (overlap(ws, plan->total, X, nx) || overlap(ws, plan->total, Wqkv, nw) ||
@@ -177,13 +193,12 @@ int check_call(int mode, const vggt_attn_shape* shape, int sub_h, int sub_w, con
   return VGGT_ATTN_OK;
 }
 
-int run(int mode, int sub_h, int sub_w, int first_stage, int last_stage,
+int run(int mode, const CallOpts& o, int first_stage, int last_stage,
         const vggt_attn_shape* shape, const void* X, const void* Wqkv, const void* Wo,
         const float* qg, const float* qb, const float* kg, const float* kb, void* Y, void* ws,
         size_t ws_bytes, void* stream) {
   Plan plan;
-  int st = check_call(mode, shape, sub_h, sub_w, X, Wqkv, Wo, qg, qb, kg, kb, Y, ws, ws_bytes,
-                      &plan);
+  int st = check_call(mode, shape, o, X, Wqkv, Wo, qg, qb, kg, kb, Y, ws, ws_bytes, &plan);
   if (st != VGGT_ATTN_OK) return st;
   Ptrs a{reinterpret_cast<const bf16*>(X), reinterpret_cast<const bf16*>(Wqkv),
          reinterpret_cast<const bf16*>(Wo), qg, qb, kg, kb, reinterpret_cast<bf16*>(Y),
@@ -211,7 +226,7 @@ extern "C" {
 
 size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape) {
   Plan plan;
-  if (make_plan(mode, shape, 1, 1, &plan) != VGGT_ATTN_OK) return 0;
+  if (make_plan(mode, shape, CallOpts(), &plan) != VGGT_ATTN_OK) return 0;
   return plan.total;
 }
 
@@ -223,21 +238,21 @@ size_t vggt_attn_workspace_bytes(int mode, const vggt_attn_shape* shape) {
   shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream
 
 int vggt_attn_frame(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_FRAME, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_FRAME, CallOpts(), VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_global(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_GLOBAL, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_GLOBAL, CallOpts(), VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_global_register(VGGT_ARGS) {
-  return run(VGGT_ATTN_MODE_REGISTER, 1, 1, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(VGGT_ATTN_MODE_REGISTER, CallOpts(), VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {
   if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
   if (mode == VGGT_ATTN_MODE_SUBSAMPLED) return VGGT_ATTN_EINVAL;  // needs the windows
-  return run(mode, 1, 1, stage, stage, VGGT_PASS);
+  return run(mode, CallOpts(), stage, stage, VGGT_PASS);
 }
 
 int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int32_t sub_w,
@@ -245,8 +260,10 @@ int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int
                                 const float* q_gamma, const float* q_beta,
                                 const float* k_gamma, const float* k_beta, void* Y,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(VGGT_ATTN_MODE_SUBSAMPLED, sub_h, sub_w, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT,
-             VGGT_PASS);
+  CallOpts o;
+  o.sub_h = sub_h;
+  o.sub_w = sub_w;
+  return run(VGGT_ATTN_MODE_SUBSAMPLED, o, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
 }
 
 int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t sub_h,
@@ -255,7 +272,34 @@ int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t 
                                const float* k_beta, void* Y, void* workspace,
                                size_t workspace_bytes, void* stream) {
   if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
-  return run(VGGT_ATTN_MODE_SUBSAMPLED, sub_h, sub_w, stage, stage, VGGT_PASS);
+  CallOpts o;
+  o.sub_h = sub_h;
+  o.sub_w = sub_w;
+  return run(VGGT_ATTN_MODE_SUBSAMPLED, o, stage, stage, VGGT_PASS);
+}
+
+int vggt_attn_global_rows(const vggt_attn_shape* shape, int64_t row_begin, int64_t row_count,
+                          const void* X, const void* Wqkv, const void* Wo, const float* q_gamma,
+                          const float* q_beta, const float* k_gamma, const float* k_beta,
+                          void* Y_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  CallOpts o;
+  o.q_begin = row_begin;
+  o.q_count = row_count < 0 ? 0 : row_count;  // negative counts are out of range, not "all"
+  void* Y = Y_rows;
+  return run(VGGT_ATTN_MODE_GLOBAL, o, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_global_rows_stage(int stage, const vggt_attn_shape* shape, int64_t row_begin,
+                                int64_t row_count, const void* X, const void* Wqkv, const void* Wo,
+                                const float* q_gamma, const float* q_beta, const float* k_gamma,
+                                const float* k_beta, void* Y_rows, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
+  CallOpts o;
+  o.q_begin = row_begin;
+  o.q_count = row_count < 0 ? 0 : row_count;
+  void* Y = Y_rows;
+  return run(VGGT_ATTN_MODE_GLOBAL, o, stage, stage, VGGT_PASS);
 }
 
 const char* vggt_attn_status_str(int status) {
@@ -267,7 +311,8 @@ const char* vggt_attn_status_str(int status) {
     case VGGT_ATTN_EWORKSPACE: return "workspace smaller than vggt_attn_workspace_bytes()";
     case VGGT_ATTN_EHIP: return "HIP runtime error while enqueueing a kernel";
     case VGGT_ATTN_ERANGE:
-      return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535, sub_h / sub_w >= 1";
+      return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535, sub_h / sub_w >= 1, "
+             "row window inside the set";
     default: return "unknown status";
   }
 }

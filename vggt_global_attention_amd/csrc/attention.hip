@@ -61,7 +61,8 @@ struct AttnArgs {
   int64_t seq_stride;
   int64_t kv_rows;     // key rows per head; set s starts at key s * kv_seq_stride
   int64_t kv_seq_stride;
-  int nseq, L, Lk, H, qtiles;  // sets, queries and keys per set, heads, query tiles
+  int nseq, L, Lk, H, qtiles;  // sets, query end and keys per set, heads, query tiles
+  int q0;                      // first query row of a set (a window of the global set), else 0
   const Scalars* sc;
   // subsampled global set only: every token's key / value (for the diagonal)
   // and the per-head sums of the discarded keys and values (for the mean)
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
   const int L = p.L;
-  const int qloc0 = bc.qt * BQ + wave * QB * 32;
+  const int qloc0 = p.q0 + bc.qt * BQ + wave * QB * 32;
   const bool active = __builtin_amdgcn_readfirstlane(qloc0) < L;
   f16* qh = p.q + (int64_t)bc.h * p.rows * kDh;
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
@@ -475,7 +476,8 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.L = p.L;
   g.Lk = p.Lk;
   g.H = p.H;
-  g.qtiles = (p.L + BQ - 1) / BQ;
+  g.q0 = p.q0;
+  g.qtiles = (p.L - p.q0 + BQ - 1) / BQ;
   g.sc = ws_scalars(p, a);
   if (SGA) {
     g.k_all = ws_k(p, a);

@@ -23,20 +23,25 @@ constexpr int kSpecial = 17;   // 1 camera + 16 register tokens per frame
 constexpr int kDh = 64;        // head width supported by the kernels
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, one L2 each
 
-// Workspace row -> X row map.  Rows are grouped: group g = w / grp_stride,
-// slot t = w % grp_stride; the row is a real token iff t < grp_valid and
-// g < ngroups, and then reads X row g * src_stride + t.
+// Workspace row -> X row map.  With v = w - base (no row if v < 0), rows are
+// grouped: group g = v / grp_stride, slot t = v % grp_stride; the row is a
+// real token iff t < grp_valid and g < ngroups, and then reads X row
+// g * src_stride + t.
 //   global:   one group of N rows           (grp_stride = rows, src_stride = 0)
 //   frame:    S groups of T rows, padded to a multiple of 64
 //   register: S groups of the 17 special rows, packed
+//   a window of global rows [base, base + n) -> output rows 0..n-1
 struct RowMap {
   int64_t grp_stride;
   int64_t src_stride;
   int32_t grp_valid;
   int32_t ngroups;
+  int64_t base;
   __device__ __forceinline__ int64_t src(int64_t w) const {
-    int64_t g = w / grp_stride;
-    int64_t t = w - g * grp_stride;
+    const int64_t v = w - base;
+    if (v < 0) return -1;
+    int64_t g = v / grp_stride;
+    int64_t t = v - g * grp_stride;
     return (t < grp_valid && g < ngroups) ? g * src_stride + t : -1;
   }
 };

@@ -31,7 +31,9 @@ struct GemmArgs {
   int64_t rows;   // workspace rows (multiple of 128)
   int Nf, K;
   int fgroups;    // output-feature groups walked one after the other (divides Nf / 128)
-  RowMap map;
+  int64_t m_first;       // first workspace row of the token tiles (a multiple of the tile)
+  int64_t q_lo, q_hi;    // QKV: q is needed only for rows [q_lo, q_hi)
+  RowMap map;            // QKV: workspace row -> X row; OUT: workspace row -> Y row
   int T, gw, off, d;
   float eps;
   const float *qg, *qb, *kg, *kb;
@@ -226,6 +228,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     m0 = (int64_t)(logical / ntn) * kGemmBM;
     n0 = (logical % ntn) * kGemmBN;
   }
+  m0 += g.m_first;
+  // query rows outside the window need no q (whole workgroup leaves)
+  if (EPI == kEpiQKV && n0 < g.d && (m0 + kGemmBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (int64_t)n0 * g.K;
   const uint16_t* Bbase = reinterpret_cast<const uint16_t*>(g.B);
@@ -372,6 +377,9 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
     m0 = (int64_t)(logical / ntn) * kDmaBM;
     n0 = (logical % ntn) * kDmaBN;
   }
+  m0 += g.m_first;
+  // query rows outside the window need no q (whole workgroup leaves)
+  if (EPI == kEpiQKV && n0 < g.d && (m0 + kDmaBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   // DMA sources of this lane: A rows (q*4 + wave)*16 + lane/4 (q < 2), B rows
   // likewise (q < 4); column chunk (lane%4) ^ ((lane/16) & 3).
@@ -496,6 +504,9 @@ static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   g.k = ws_k(p, a);
   g.vt = ws_v(p, a);
   g.y = a.Y;
+  g.m_first = 0;
+  g.q_lo = p.q0;
+  g.q_hi = p.window ? p.L : p.rows;
   return g;
 }
 
@@ -525,11 +536,17 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.Nf = p.d;
   g.K = p.d;
   g.fgroups = feature_groups(g.Nf, g.K, 2);
-  if (use_dma_gemm(p)) {
-    const int blocks = (int)(p.rows / kDmaBM) * (g.Nf / kDmaBN);
+  g.map = p.out_map;
+  // token tiles covering the output rows: all rows, or the query window
+  const bool dma = use_dma_gemm(p);
+  const int64_t bm = dma ? kDmaBM : kGemmBM;
+  const int64_t lo = p.window ? p.q0 / bm * bm : 0;
+  const int64_t hi = p.window ? (p.L + bm - 1) / bm * bm : p.rows;
+  g.m_first = lo;
+  const int blocks = (int)((hi - lo) / bm) * (g.Nf / kGemmBN);
+  if (dma) {
     hipLaunchKernelGGL(gemm_dma_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
   } else {
-    const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
     hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
   }
   hipError_t e = hipGetLastError();

@@ -18,6 +18,13 @@ constexpr int kAttnBK = 64;         // keys per attention tile
 constexpr int kRowAlign = 2048;     // workspace rows are padded to this (8 XCDs x 256-row tiles)
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
 
+// Options of the extended entry points.
+struct CallOpts {
+  int sub_h = 1, sub_w = 1;  // subsampled mode: windows
+  int64_t q_begin = 0;       // global mode: first query row computed
+  int64_t q_count = -1;      // global mode: query rows computed (-1: every row)
+};
+
 struct Plan {
   int mode;
   int S, T, d, H, gh, gw, off;
@@ -25,10 +32,13 @@ struct Plan {
   // attention sets: nseq sequences of L tokens, sequence s starting at
   // workspace row s * seq_stride
   int nseq;
-  int L;
+  int L;               // query rows of a set end here (= q0 + query count)
+  int q0;              // first query row (a window of the global set), else 0
   int64_t seq_stride;
   int64_t rows;        // workspace rows held by q/k/v (multiple of kRowAlign)
   RowMap map;          // workspace row -> X row
+  RowMap out_map;      // workspace row -> Y row (the window's rows only, when windowed)
+  bool window;         // global mode restricted to query rows [q0, L)
   int rope_npos;       // entries per axis of the RoPE table
   int attn_qb;         // 32-query blocks per wave in the attention kernel
   int attn_waves;      // waves per attention workgroup (4 or 8)
@@ -58,10 +68,10 @@ struct Ptrs {
   char* ws;
 };
 
-// Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  sub_h and
-// sub_w are the subsampling windows of VGGT_ATTN_MODE_SUBSAMPLED (ignored in
-// the other modes).
-int make_plan(int mode, const vggt_attn_shape* s, int sub_h, int sub_w, Plan* p);
+// Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  `o` carries
+// the subsampling windows (VGGT_ATTN_MODE_SUBSAMPLED) or the query-row
+// window (VGGT_ATTN_MODE_GLOBAL); defaults mean neither.
+int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p);
 
 hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st);
 hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st);
