@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--sub", default="3x3", help="subsampled mode: windows sub_h x sub_w")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other modes / sizes")
-    ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
     ap.add_argument("--copy-calibration", action="store_true",
