@@ -449,7 +449,10 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
   // every outstanding load, in-flight prefetch included.  Reuse is safe: the
   // buffer step kt+2 overwrites was last read in step kt-1, before the
   // barrier that closed it.
-  constexpr int kVm6 = 0x0F76, kVm0 = 0x0F70;  // s_waitcnt vmcnt(6) / vmcnt(0)
+  // The waits also cover this wave's LDS reads (lgkmcnt(0)): the compiler may
+  // sink the last MFMAs below the barrier, and no read of a stage may still be
+  // in flight when another wave starts refilling it.
+  constexpr int kVm6 = 0x0076, kVm0 = 0x0070;  // s_waitcnt vmcnt(6|0) lgkmcnt(0)
   const int nk = g.K / kDmaBK;
   dma(0, 0);
   dma(1, 1);
@@ -467,22 +470,156 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
   gemm_epilogue<EPI, 4>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel (output features a multiple of 256): 256 token rows x 256
+// output features per workgroup, 8 waves of 128 x 64 (2 x 4), 64-deep
+// k-steps in two LDS stages of 64 KB.  A DMA instruction moves 8 whole
+// 128-byte rows (8 cache lines, all bytes used), and the 256 x 256 tile moves
+// half the bytes per FLOP of the 256 x 128 one.  LDS rows use the 128-byte
+// swizzle chunk ^ (row & 7) ^ ((row >> 3) & 1); lane i of a DMA instruction
+// writes row i/8, chunk position i%8, so it fetches source chunk
+// (i%8) ^ (i/8) ^ ((R0 >> 3) & 1) for the instruction's first row R0.
+// (Measured alternatives at the s500 frame QKV shape: 32-deep k-steps in four
+// stages, 4.60 ms; a per-tile rotation of the k order, no change; 4.40 ms
+// here.)
+// ---------------------------------------------------------------------------
+constexpr int kWBM = 256, kWBN = 256, kWBK = 64;
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
+  typedef typename GemmTypes<EPI>::V8 V8;
+  constexpr int kAB = kWBN * 128;  // A stage: 256 feature rows x 128 B
+  constexpr int kBB = kWBM * 128;  // B stage: 256 token rows x 128 B
+  __shared__ __attribute__((aligned(1024))) char smem[2][kAB + kBB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;  // 2 token halves x 4 feature quarters
+  const int j = lane & 31, h = lane >> 5;
+
+  const int ntn = g.Nf / kWBN;
+  const int ntm = gridDim.x / ntn;
+  int64_t m0;
+  int n0;
+  if (ntm % kXcds == 0 && ntn % g.fgroups == 0) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int ntt = ntm / kXcds, pf = ntn / g.fgroups;
+    const int fg = slot / (ntt * pf), rem = slot - fg * ntt * pf;
+    m0 = (int64_t)(xcd * ntt + rem / pf) * kWBM;
+    n0 = (fg * pf + rem % pf) * kWBN;
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    m0 = (int64_t)(logical / ntn) * kWBM;
+    n0 = (logical % ntn) * kWBN;
+  }
+  m0 += g.m_first;
+  if (EPI == kEpiQKV && n0 < g.d && (m0 + kWBM <= g.q_lo || m0 >= g.q_hi)) return;
+
+  // DMA: instruction q of wave w covers rows (q*8 + w)*8 .. +7 (q < 4) of A
+  // and of B; lane row lane/8.
+  const int lrow = lane >> 3;
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A);
+  const uint16_t* Bb = reinterpret_cast<const uint16_t*>(g.B);
+  const uint16_t* aptr[4];
+  const uint16_t* bptr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = (q * 8 + wave) * 8;
+    const int lcol = (lane & 7) ^ lrow ^ ((r0 >> 3) & 1);
+    aptr[q] = A + (int64_t)(n0 + r0 + lrow) * g.K + lcol * 8;
+    const int64_t w = m0 + r0 + lrow;
+    if (EPI == kEpiQKV) {
+      const int64_t src = g.map.src(w);  // rows without a token read X row 0 (finite, unused)
+      bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
+    } else {
+      bptr[q] = Bb + w * kDh + lcol * 8;
+    }
+  }
+  auto dma = [&](int kt, int stage) {
+    char* base = &smem[stage][0];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(aptr[q] + kt * kWBK, base + (q * 8 + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint16_t* src = EPI == kEpiQKV ? bptr[q] + kt * kWBK
+                                           : bptr[q] + (int64_t)kt * g.rows * kDh;
+      dma16(src, base + kAB + (q * 8 + wave) * 1024);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  auto compute = [&](int stage) {
+    const char* As = &smem[stage][0];
+    const char* Bs = As + kAB;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      V8 af[2], bfr[4];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+        af[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 32 + j, kc * 2 + h));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 128 + tb * 32 + j, kc * 2 + h));
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mfma32x32x16(af[fb], bfr[tb], acc[fb][tb]);
+    }
+  };
+
+  // Eight DMA instructions per wave per k-step; stage kt+1 is fetched while
+  // stage kt is computed.  Bare s_barrier after an explicit wait that also
+  // covers this wave's LDS reads (lgkmcnt(0), as in gemm_dma_kernel): the
+  // stage overwritten next was last read before the previous barrier.
+  constexpr int kVm0 = 0x0070;  // s_waitcnt vmcnt(0) lgkmcnt(0)
+  const int nk = g.K / kWBK;
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(kVm0);
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) dma(kt + 1, (kt + 1) & 1);
+    compute(kt & 1);
+    __builtin_amdgcn_s_waitcnt(kVm0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  gemm_epilogue<EPI, 4>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane);
+}
+
 // Smallest number of output-feature groups (a divisor of the feature tile
 // count) whose weight slice fits a ~2 MB share of an XCD's 4 MB L2.
-static int feature_groups(int nf, int k, int elem_bytes) {
-  const int ntn = nf / kGemmBN;
+static int feature_groups(int nf, int k, int elem_bytes, int bn) {
+  const int ntn = nf / bn;
+  if (const char* e = getenv("VGGT_GEMM_FGROUPS")) {  // tuning override (must divide the tile count)
+    const int v = atoi(e);
+    if (v >= 1 && ntn % v == 0) return v;
+  }
   const int64_t bytes = (int64_t)nf * k * elem_bytes;
   for (int gcount = 1; gcount < ntn; ++gcount)
     if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)2 << 20)) return gcount;
   return ntn;
 }
 
-// The DMA kernel needs whole 256-row token tiles; VGGT_GEMM=0 forces the
-// register-staged 128 x 128 kernel (a tuning / comparison switch).
-static bool use_dma_gemm(const Plan& p) {
-  if (p.rows % kDmaBM != 0) return false;
-  const char* e = getenv("VGGT_GEMM");
-  return !(e && atoi(e) == 0);
+// Kernel choice: 2 = wide (256 x 256, output features a multiple of 256),
+// 1 = DMA 256 x 128, 0 = register-staged 128 x 128.  The DMA kernels need
+// whole 256-row token tiles.  VGGT_GEMM = 0 | 1 | 2 caps the choice (a tuning
+// / comparison switch).
+static int gemm_kind(const Plan& p, int nf) {
+  int kind = 2;
+  if (const char* e = getenv("VGGT_GEMM")) {
+    const int v = atoi(e);
+    if (v >= 0 && v < 2) kind = v;
+  }
+  if (kind == 2 && nf % kWBN != 0) kind = 1;
+  if (kind >= 1 && p.rows % kDmaBM != 0) kind = 0;
+  return kind;
 }
 
 static GemmArgs base_args(const Plan& p, const Ptrs& a) {
@@ -516,8 +653,12 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.B = a.X;
   g.Nf = 3 * p.d;
   g.K = p.d;
-  g.fgroups = feature_groups(g.Nf, g.K, 2);
-  if (use_dma_gemm(p)) {
+  const int kind = gemm_kind(p, g.Nf);
+  g.fgroups = feature_groups(g.Nf, g.K, 2, kind == 2 ? kWBN : kGemmBN);
+  if (kind == 2) {
+    const int blocks = (int)(p.rows / kWBM) * (g.Nf / kWBN);
+    hipLaunchKernelGGL(gemm_wide_kernel<kEpiQKV>, dim3(blocks), dim3(512), 0, st, g);
+  } else if (kind == 1) {
     const int blocks = (int)(p.rows / kDmaBM) * (g.Nf / kDmaBN);
     hipLaunchKernelGGL(gemm_dma_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
   } else {
@@ -535,16 +676,19 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.B = ws_q(p, a);  // the attention kernel leaves O in place of q
   g.Nf = p.d;
   g.K = p.d;
-  g.fgroups = feature_groups(g.Nf, g.K, 2);
+  const int kind = gemm_kind(p, g.Nf);
+  const int bn = kind == 2 ? kWBN : kGemmBN;
+  g.fgroups = feature_groups(g.Nf, g.K, 2, bn);
   g.map = p.out_map;
   // token tiles covering the output rows: all rows, or the query window
-  const bool dma = use_dma_gemm(p);
-  const int64_t bm = dma ? kDmaBM : kGemmBM;
+  const int64_t bm = kind == 2 ? kWBM : kind == 1 ? kDmaBM : kGemmBM;
   const int64_t lo = p.window ? p.q0 / bm * bm : 0;
   const int64_t hi = p.window ? (p.L + bm - 1) / bm * bm : p.rows;
   g.m_first = lo;
-  const int blocks = (int)((hi - lo) / bm) * (g.Nf / kGemmBN);
-  if (dma) {
+  const int blocks = (int)((hi - lo) / bm) * (g.Nf / bn);
+  if (kind == 2) {
+    hipLaunchKernelGGL(gemm_wide_kernel<kEpiOut>, dim3(blocks), dim3(512), 0, st, g);
+  } else if (kind == 1) {
     hipLaunchKernelGGL(gemm_dma_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
   } else {
     hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
