@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
+    ap.add_argument("--schedule", default=None, metavar="S_LIST",
+                    help="instead of the layer: time the 24-layer attention-only schedule and "
+                         "record its peak device memory at these frame counts, e.g. 1,25,100")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -143,6 +146,68 @@ def loop_stage(w, mode, d, stage, steps, sub=(1, 1)):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def schedule_forward(w, spec, steps, warmup, ls=1e-5):
+    """ms per attention-only forward of `spec` and the peak device memory of
+    the run (torch's allocator high-water mark: input, state, kept states,
+    workspace and the weights of every block)."""
+    import torch
+    from vggt_global_attention_amd import schedule as S
+    from vggt_global_attention_amd import synth
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    blocks = [{k: v.to("cuda") for k, v in b.items()}
+              for b in synth.make_block_weights(w, 2 * spec.n_layers, ls)]
+    wbytes = sum(t.numel() * t.element_size() for b in blocks for t in b.values())
+    X = synth.make_inputs(w)["X"].to("cuda")
+    sch = S.Schedule(X, w.H, w.grid_h, w.grid_w, blocks, spec)
+    caches = sch.alloc_caches(X)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sch(X, state=X, caches=caches)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        sch(X, state=X, caches=caches)     # in place: the state overwrites the input
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    peak = torch.cuda.max_memory_allocated() - base
+    flop = 0.0
+    for l in range(spec.n_layers):
+        flop += w.flop("frame") + w.flop(spec.inter_mode(l), spec.sub)
+    out = {"S": w.S, "N": w.N, "ms_per_forward": ms, "tflops": flop / ms / 1e9,
+           "peak_bytes": peak, "peak_gb": peak / 1e9, "weights_bytes": wbytes,
+           "state_bytes": X.numel() * 2, "caches_bytes": caches.numel() * 2,
+           "workspace_bytes": sch.workspace.numel(), "flop_per_forward": flop,
+           "inter_modes": [spec.inter_mode(l) for l in range(spec.n_layers)]}
+    del sch, caches, X, blocks
+    torch.cuda.empty_cache()
+    return out
+
+
+def schedule_sweep(frames, steps, warmup):
+    from vggt_global_attention_amd import configs
+    from vggt_global_attention_amd import schedule as S
+    variants = {"vggt": S.ScheduleSpec(),
+                # AVGGT: the first third of the layers as frame attention, the
+                # remaining global layers subsampled with 3 x 3 windows
+                "avggt_early8_sub3x3": S.ScheduleSpec(early_frame=8, sub=(3, 3))}
+    rows = []
+    for n in frames:
+        w = configs.custom(f"s{n}", S=n, grid_h=26, grid_w=39, d=1024, H=16, cid=70)
+        for vname, spec in variants.items():
+            print(f"[bench] schedule {vname} S={n}", file=sys.stderr, flush=True)
+            st = steps if n <= 100 else 1
+            r = schedule_forward(w, spec, st, min(warmup, 1) if n > 100 else warmup)
+            r["variant"] = vname
+            rows.append(r)
+            print(f"[bench]   {r['ms_per_forward']:.1f} ms, peak {r['peak_gb']:.2f} GB",
+                  file=sys.stderr, flush=True)
+    return rows
+
+
 def cpu_baseline(w, inp, n_rows):
     """The fp64 oracle on a bounded sample of the same layer: k/v for all N
     tokens, then q, attention and output projection for n_rows query rows."""
@@ -195,6 +260,14 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n,
                           "bytes_written_per_copy": n, "copies": 3}))
+        return
+    if a.schedule:
+        frames = [int(x) for x in a.schedule.split(",")]
+        rows = schedule_sweep(frames, a.steps, a.warmup)
+        print(json.dumps({"schedule_sweep": rows, "layers": 24,
+                          "register_layers": [2, 6, 9, 14, 20], "cached_layers": [4, 11, 17, 23],
+                          "shape": "T=1031 (26x39 patches + 17), d=1024, H=16, bf16 state",
+                          "data": "synthetic (seeded; no trained weights)"}), flush=True)
         return
     w = configs.WORKLOADS[a.workload]
     sub = tuple(int(x) for x in a.sub.lower().split("x")) if a.mode == "subsampled" else (1, 1)
@@ -271,6 +344,13 @@ def main():
         extra["s100_global_rows_share1of8"] = {"ms_per_layer": m2, "tflops": (attn + gemm) / m2 / 1e9,
                                                "core_ms": c2, "core_tflops": attn / c2 / 1e9,
                                                "query_rows": share, "key_rows": w.N}
+        from vggt_global_attention_amd import schedule as S
+        print("[bench] extra s100 24-layer attention-only forward", file=sys.stderr, flush=True)
+        del d
+        torch.cuda.empty_cache()
+        r = schedule_forward(w, S.ScheduleSpec(), 2, 1)
+        extra["s100_schedule24"] = {k: r[k] for k in ("ms_per_forward", "tflops", "peak_gb",
+                                                      "flop_per_forward")}
         out["extra"] = extra
     if not a.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

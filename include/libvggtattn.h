@@ -182,6 +182,81 @@ int vggt_attn_global_rows_stage(int stage, const vggt_attn_shape* shape, int64_t
                                 const float* k_gamma, const float* k_beta, void* Y_rows,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+   Layer schedule.  "VGGT-Omega Aggregator explainer", section 三: the
+   Aggregator is 24 layers deep and every layer runs a frame block and then an
+   inter-frame block, each a residual branch scaled by LayerScale; the
+   inter-frame block is in register mode at layers [2, 6, 9, 14, 20] (read as
+   0-based layer indices, global mode at the others); section 四: the token
+   states after the frame block and after the inter-frame block of layers 4,
+   11, 17, 23 are kept, concatenated along channels (2d features).  AVGGT
+   summary, technical summary 2B: early global layers may run as frame
+   attention, the remaining ones as subsampled global attention.
+   --------------------------------------------------------------------------- */
+
+/* Residual update: for rows r with r % period < active,
+   Z[r][c] = X[r][c] + gamma[c] * Y[r][c] (fp32 fused multiply-add of the bf16
+   inputs, rounded once to bf16); other rows Z = X (register layers pass
+   period = T, active = 17, so patch rows keep their state).  X, Y, Z: bf16
+   [rows][d]; gamma: fp32 [d] (the LayerScale vector); all device pointers,
+   16-byte aligned, d % 8 == 0.  Z may be X (in place) but must not overlap Y
+   or gamma.  If C is not NULL, Z is also written to C + r * c_stride (bf16
+   elements; c_stride >= d, a multiple of 8), e.g. one half of a [rows][2d]
+   cache; C must not overlap the other buffers.  Errors: EINVAL (null X / Y /
+   Z / gamma, overlap), ESHAPE (rows < 0, d, period < 1, active < 0,
+   c_stride), EALIGN; nothing is launched on error. */
+int vggt_attn_residual(const void* X, const void* Y, void* Z, int64_t rows, int32_t d,
+                       const float* gamma, int32_t period, int32_t active, void* C,
+                       int64_t c_stride, void* stream);
+
+/* Weights of one block of the schedule (device pointers, layouts as for the
+   block calls above). */
+typedef struct vggt_attn_block_weights {
+  const void* Wqkv;          /* bf16 [3d][d] */
+  const void* Wo;            /* bf16 [d][d] */
+  const float* q_gamma;      /* fp32 [H][Dh] */
+  const float* q_beta;
+  const float* k_gamma;
+  const float* k_beta;
+  const float* layer_scale;  /* fp32 [d], 16-byte aligned: LayerScale of the residual branch */
+} vggt_attn_block_weights;
+
+typedef struct vggt_attn_schedule {
+  int32_t n_layers;          /* 1..64 (24 in the model) */
+  int32_t early_frame;       /* inter-frame blocks of layers l < early_frame that are not
+                                register layers run as frame blocks (AVGGT); 0: none */
+  uint64_t register_layers;  /* bit l: layer l's inter-frame block is in register mode */
+  uint64_t cached_layers;    /* bit l: layer l's two states are kept */
+  int32_t sub_h, sub_w;      /* 1, 1: the remaining inter-frame blocks are global; else they
+                                are subsampled global blocks with these windows */
+} vggt_attn_schedule;
+
+/* Workspace of vggt_attn_schedule_run: the block output buffer plus the
+   largest block workspace the schedule uses; 0 if the shape or the schedule
+   is not supported. */
+size_t vggt_attn_schedule_workspace_bytes(const vggt_attn_shape* shape,
+                                          const vggt_attn_schedule* sched);
+
+/* The attention part of the Aggregator's forward pass.  With x = X:
+     for l in 0 .. n_layers-1:
+       a = x + ls_f * frame_l(x)                    (all rows)
+       x = a + ls_i * inter_l(a)                    (register mode: the 17 special
+                                                      rows of every frame only)
+       if bit l of cached_layers: cache[k] = [a | x], k counting cached layers
+   where frame_l / inter_l are the block calls above with the weights
+   blocks[2l] / blocks[2l+1] (a HOST array of 2 * n_layers entries holding
+   device pointers), ls_f / ls_i their layer_scale vectors, and every block
+   output and state is bf16.  state receives the final x (bf16 [S][T][d]; it
+   may be X itself, else it must not overlap X).  caches: NULL (nothing kept)
+   or bf16 [popcount(cached_layers)][S][T][2d], channels [0, d) the state after
+   the frame block, [d, 2d) the state after the inter-frame block.  Masks with
+   bits at or above n_layers, early_frame outside 0..n_layers or windows < 1
+   give VGGT_ATTN_ERANGE; every block and residual call is checked before the
+   first launch, so on any error nothing is enqueued. */
+int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedule* sched,
+                           const vggt_attn_block_weights* blocks, const void* X, void* state,
+                           void* caches, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* vggt_attn_status_str(int status);
 

@@ -42,7 +42,7 @@ def metrics(y, ref) -> dict:
     }
 
 
-# Tolerance fixed by the benchmark spec for the bf16-in / fp32-accumulate path:
+# Parity bar of the bf16-in / fp32-accumulate path:
 # max|err| <= 1e-2 * max|ref| and mean relative error (read as relL1) <= 2e-3.
 TOL_MAX = 1e-2
 TOL_RELL1 = 2e-3

@@ -197,3 +197,105 @@ def test_global_rows_errors():
     assert B.vggt_attn_global_rows_stage(9, s, 0, 10, *a, 0x10000000, ws, None) == B.EINVAL
     assert B.vggt_attn_global_rows_stage(B.STAGE_CORE, s, 0, 0, *a, 0x10000000, ws,
                                          None) == B.ERANGE
+
+
+# ----------------------------------------------------------------------------
+# Residual update and layer schedule
+# ----------------------------------------------------------------------------
+
+RES = dict(X=0x100000, Y=0x200000, Z=0x300000, rows=64, d=256, gamma=0x400000, period=1,
+           active=1, C=0, c_stride=256)
+
+
+def res(**over):
+    a = dict(RES)
+    a.update(over)
+    return B.vggt_attn_residual(a["X"], a["Y"], a["Z"], a["rows"], a["d"], a["gamma"],
+                                a["period"], a["active"], a["C"] or None, a["c_stride"], None)
+
+
+def test_residual_errors():
+    assert res(rows=0) == B.OK                   # nothing to do, nothing launched
+    assert res(rows=0, X=0) == B.EINVAL
+    assert res(gamma=0) == B.EINVAL
+    assert res(d=12) == B.ESHAPE
+    assert res(period=0) == B.ESHAPE
+    assert res(active=-1) == B.ESHAPE
+    assert res(rows=-1) == B.ESHAPE
+    assert res(X=0x100008) == B.EALIGN
+    assert res(gamma=0x400004) == B.EALIGN
+    assert res(Z=0x200000 + 512) == B.EINVAL     # Z overlaps Y
+    assert res(Z=0x100000 + 512) == B.EINVAL     # partial overlap with X (Z == X is fine)
+    assert res(C=0x100000 + 1024, c_stride=512) == B.EINVAL   # cache overlaps X
+    assert res(C=0x600000, c_stride=200) == B.ESHAPE
+    assert res(C=0x600000, c_stride=260) == B.ESHAPE           # not a multiple of 8
+    assert res(C=0x600008, c_stride=512) == B.EALIGN
+
+
+def sched(n=24, reg=(2, 6, 9, 14, 20), cache=(4, 11, 17, 23), early=0, sub=(1, 1)):
+    m = lambda ls: sum(1 << l for l in ls)  # noqa: E731
+    return B.vggt_attn_schedule(n, early, m(reg), m(cache), sub[0], sub[1])
+
+
+def test_schedule_workspace_bytes():
+    s = B.make_shape(**TINY)
+    ybytes = -(-2 * 81 * 256 * 2 // 256) * 256
+    f = B.vggt_attn_workspace_bytes(B.MODE_FRAME, s)
+    g = B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, s)
+    u = B.vggt_attn_workspace_bytes(B.MODE_SUBSAMPLED, s)
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched()) == ybytes + max(f, g)
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(sub=(3, 3))) == ybytes + max(f, u)
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(reg=(), early=24)) == ybytes + f
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(n=0)) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(n=65)) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(n=4, reg=(5,))) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(B.make_shape(**dict(TINY, T=80)), sched()) == 0
+
+
+def fake_blocks(n_blocks, **bad):
+    arr = (B.vggt_attn_block_weights * n_blocks)()
+    for b in range(n_blocks):
+        base = 0x40000000 + b * 0x100000
+        f = dict(Wqkv=base, Wo=base + 0x80000, q_gamma=base + 0xC0000, q_beta=base + 0xC1000,
+                 k_gamma=base + 0xC2000, k_beta=base + 0xC3000, layer_scale=base + 0xC4000)
+        if b == n_blocks - 1:
+            f.update(bad)
+        arr[b] = B.vggt_attn_block_weights(**f)
+    return arr
+
+
+def run_sched(sc=None, blocks=None, X=0x100000, state=0x500000, caches=0x20000000,
+              ws=0x10000000, ws_bytes=1 << 28, shape=None):
+    sc = sc or sched()
+    if blocks is None:
+        blocks = fake_blocks(2 * sc.n_layers)
+    return B.vggt_attn_schedule_run(shape or B.make_shape(**TINY), sc, blocks, X, state,
+                                    caches, ws, ws_bytes, None)
+
+
+def test_schedule_errors():
+    assert run_sched(sc=sched(n=0)) == B.ESHAPE
+    assert run_sched(sc=sched(n=65)) == B.ESHAPE
+    assert run_sched(sc=sched(n=4, reg=(4,), cache=())) == B.ERANGE
+    assert run_sched(sc=sched(n=4, reg=(), cache=(7,))) == B.ERANGE
+    assert run_sched(sc=sched(early=25)) == B.ERANGE
+    assert run_sched(sc=sched(early=-1)) == B.ERANGE
+    assert run_sched(sc=sched(sub=(0, 2))) == B.ERANGE
+    assert run_sched(shape=B.make_shape(**dict(TINY, T=80))) == B.ESHAPE
+    assert B.vggt_attn_schedule_run(B.make_shape(**TINY), sched(), None, 0x100000, 0x500000,
+                                    None, 0x10000000, 1 << 28, None) == B.EINVAL
+    assert run_sched(X=0) == B.EINVAL
+    assert run_sched(state=0) == B.EINVAL
+    assert run_sched(ws=0x10000080) == B.EALIGN
+    assert run_sched(ws_bytes=4096) == B.EWORKSPACE
+    assert run_sched(state=0x100000 + 4096) == B.EINVAL          # state overlaps X partially
+    assert run_sched(state=0x10000000 + 4096) == B.EINVAL        # state inside the workspace
+    assert run_sched(caches=0x10000000 + 4096) == B.EINVAL       # caches inside the workspace
+    assert run_sched(caches=0x500000 + 4096) == B.EINVAL         # caches overlap the state
+    assert run_sched(caches=0x20000008) == B.EALIGN
+    assert run_sched(blocks=fake_blocks(48, Wo=0)) == B.EINVAL
+    assert run_sched(blocks=fake_blocks(48, layer_scale=0)) == B.EINVAL
+    assert run_sched(blocks=fake_blocks(48, layer_scale=0x40000000 + 47 * 0x100000 + 0xC4004)) \
+        == B.EALIGN
+    assert run_sched(blocks=fake_blocks(48, Wqkv=0x500000)) == B.EINVAL   # weight is the state
+    assert run_sched(blocks=fake_blocks(48, q_gamma=0x20000000)) == B.EINVAL  # inside caches

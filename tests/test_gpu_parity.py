@@ -1,8 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
-Bar (the benchmark's tolerance for bf16 inputs / fp32 accumulation):
-max|err| <= 1e-2 * max|ref| and relL1 = sum|err| / sum|ref| <= 2e-3, the
-reading of "mean relative error" the design notes justify.  Sizes: the tiny
+Bar (the parity tolerance for bf16 inputs / fp32 accumulation):
+max|err| <= 1e-2 * max|ref| and relL1 = sum|err| / sum|ref| <= 2e-3 ("mean
+relative error" read as the L1 ratio, which stays defined where ref is near 0).  Sizes: the tiny
 alternating block and ragged shapes with the full oracle, the 24-frame layer
 with the full oracle, and the 100/300/500-frame layers on seeded row samples
 plus closed forms that hold at full size.

@@ -20,6 +20,7 @@ MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_global_rows",
            "vggt_attn_stage", "vggt_attn_subsampled_stage", "vggt_attn_global_rows_stage",
+           "vggt_attn_residual", "vggt_attn_schedule_workspace_bytes", "vggt_attn_schedule_run",
            "vggt_attn_status_str", "vggt_attn_version")
 
 
@@ -28,6 +29,18 @@ class vggt_attn_shape(ctypes.Structure):
                 ("H", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("ln_eps", ctypes.c_float),
                 ("pos_offset", ctypes.c_int32)]
+
+
+class vggt_attn_block_weights(ctypes.Structure):
+    _fields_ = [("Wqkv", ctypes.c_void_p), ("Wo", ctypes.c_void_p), ("q_gamma", ctypes.c_void_p),
+                ("q_beta", ctypes.c_void_p), ("k_gamma", ctypes.c_void_p),
+                ("k_beta", ctypes.c_void_p), ("layer_scale", ctypes.c_void_p)]
+
+
+class vggt_attn_schedule(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("early_frame", ctypes.c_int32),
+                ("register_layers", ctypes.c_uint64), ("cached_layers", ctypes.c_uint64),
+                ("sub_h", ctypes.c_int32), ("sub_w", ctypes.c_int32)]
 
 
 class VggtAttnError(RuntimeError):
@@ -68,6 +81,20 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.vggt_attn_global_rows.argtypes = win
     L.vggt_attn_global_rows_stage.restype = ctypes.c_int
     L.vggt_attn_global_rows_stage.argtypes = [ctypes.c_int] + win
+    L.vggt_attn_residual.restype = ctypes.c_int
+    L.vggt_attn_residual.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    L.vggt_attn_schedule_workspace_bytes.restype = ctypes.c_size_t
+    L.vggt_attn_schedule_workspace_bytes.argtypes = [ctypes.POINTER(vggt_attn_shape),
+                                                     ctypes.POINTER(vggt_attn_schedule)]
+    L.vggt_attn_schedule_run.restype = ctypes.c_int
+    L.vggt_attn_schedule_run.argtypes = [ctypes.POINTER(vggt_attn_shape),
+                                         ctypes.POINTER(vggt_attn_schedule),
+                                         ctypes.POINTER(vggt_attn_block_weights), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
     L.vggt_attn_status_str.restype = ctypes.c_char_p
     L.vggt_attn_status_str.argtypes = [ctypes.c_int]
     L.vggt_attn_version.restype = ctypes.c_int
@@ -136,6 +163,21 @@ def vggt_attn_global_rows_stage(stage, shape, row_begin, row_count, X, Wqkv, Wo,
     return _call("vggt_attn_global_rows_stage", stage, ctypes.byref(shape), row_begin, row_count,
                  X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y_rows, workspace,
                  workspace_bytes, stream)
+
+
+def vggt_attn_residual(X, Y, Z, rows, d, gamma, period, active, C, c_stride, stream) -> int:
+    return _call("vggt_attn_residual", X, Y, Z, rows, d, gamma, period, active, C, c_stride, stream)
+
+
+def vggt_attn_schedule_workspace_bytes(shape, sched) -> int:
+    return lib().vggt_attn_schedule_workspace_bytes(ctypes.byref(shape), ctypes.byref(sched))
+
+
+def vggt_attn_schedule_run(shape, sched, blocks, X, state, caches, workspace, workspace_bytes,
+                           stream) -> int:
+    """`blocks` is a ctypes array of vggt_attn_block_weights (2 * n_layers)."""
+    return _call("vggt_attn_schedule_run", ctypes.byref(shape), ctypes.byref(sched), blocks, X,
+                 state, caches, workspace, workspace_bytes, stream)
 
 
 def status_str(status: int) -> str:

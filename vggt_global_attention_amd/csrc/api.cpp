@@ -4,7 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "plan.h"
+#include "entry.h"
 
 namespace vggt {
 
@@ -153,9 +153,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
 
 }  // namespace vggt
 
-using namespace vggt;
-
-namespace {
+namespace vggt {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
@@ -220,7 +218,30 @@ int run(int mode, const CallOpts& o, int first_stage, int last_stage,
   return VGGT_ATTN_OK;
 }
 
-}  // namespace
+int check_residual(const void* X, const void* Y, const void* Z, int64_t rows, int d,
+                   const float* gamma, int period, int active, const void* C, int64_t c_stride) {
+  if (!X || !Y || !Z || !gamma) return VGGT_ATTN_EINVAL;
+  if (rows < 0 || d < 8 || d % 8 != 0 || period < 1 || active < 0) return VGGT_ATTN_ESHAPE;
+  if (C && (c_stride < d || c_stride % 8 != 0)) return VGGT_ATTN_ESHAPE;
+  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(Z, 16) || !aligned(gamma, 16) ||
+      (C && !aligned(C, 16)))
+    return VGGT_ATTN_EALIGN;
+  const size_t n = (size_t)rows * d * 2, ng = (size_t)d * 4;
+  // Z may be X itself; no other overlap between the buffers
+  if (overlap(Z, n, Y, n) || overlap(Z, n, gamma, ng) || (Z != X && overlap(Z, n, X, n)))
+    return VGGT_ATTN_EINVAL;
+  if (C) {
+    const size_t nc = rows ? ((size_t)(rows - 1) * c_stride + d) * 2 : 0;
+    if (overlap(C, nc, X, n) || overlap(C, nc, Y, n) || overlap(C, nc, Z, n) ||
+        overlap(C, nc, gamma, ng))
+      return VGGT_ATTN_EINVAL;
+  }
+  return VGGT_ATTN_OK;
+}
+
+}  // namespace vggt
+
+using namespace vggt;
 
 extern "C" {
 
@@ -300,6 +321,18 @@ int vggt_attn_global_rows_stage(int stage, const vggt_attn_shape* shape, int64_t
   o.q_count = row_count < 0 ? 0 : row_count;
   void* Y = Y_rows;
   return run(VGGT_ATTN_MODE_GLOBAL, o, stage, stage, VGGT_PASS);
+}
+
+int vggt_attn_residual(const void* X, const void* Y, void* Z, int64_t rows, int32_t d,
+                       const float* gamma, int32_t period, int32_t active, void* C,
+                       int64_t c_stride, void* stream) {
+  const int st = check_residual(X, Y, Z, rows, d, gamma, period, active, C, c_stride);
+  if (st != VGGT_ATTN_OK || rows == 0) return st;
+  hipError_t e = launch_residual(reinterpret_cast<const bf16*>(X), reinterpret_cast<const bf16*>(Y),
+                                 reinterpret_cast<bf16*>(Z), rows, d, gamma, period, active,
+                                 reinterpret_cast<bf16*>(C), c_stride,
+                                 reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VGGT_ATTN_OK : VGGT_ATTN_EHIP;
 }
 
 const char* vggt_attn_status_str(int status) {

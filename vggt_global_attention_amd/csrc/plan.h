@@ -99,6 +99,11 @@ inline float* ws_sums(const Plan& p, const Ptrs& a) {
   return reinterpret_cast<float*>(a.ws + p.off_sums);
 }
 
+// Residual update of a layer schedule (prep.hip).
+hipError_t launch_residual(const bf16* X, const bf16* Y, bf16* Z, int64_t rows, int d,
+                           const float* gamma, int period, int active, bf16* C, int64_t c_stride,
+                           hipStream_t st);
+
 // Subsampled mode: gather the kept tokens' keys / values and sum the
 // discarded ones (first half of the CORE stage).
 hipError_t launch_subsample(const Plan& p, const Ptrs& a, hipStream_t st);

@@ -130,6 +130,35 @@ __global__ __launch_bounds__(256) void patch_copy_kernel(const bf16* X, bf16* Y,
   }
 }
 
+// Residual update between the blocks of a layer schedule: for rows whose
+// index modulo `period` is below `active`, Z = X + gamma * Y per channel (fp32
+// fma, one rounding to bf16); other rows Z = X.  Optionally also writes Z into
+// a strided cache (row r at C + r * c_stride).  Eight channels per step.
+__global__ __launch_bounds__(256) void residual_kernel(const bf16* X, const bf16* Y, bf16* Z,
+                                                       int64_t rows, int d, const float* gamma,
+                                                       int period, int active, bf16* C,
+                                                       int64_t c_stride) {
+  const int per_row = d / 8;
+  const int64_t total = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row;
+    const int c = (int)(i - r * per_row) * 8;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(X + r * d + c);
+    bf16x8 z = x;
+    if ((int)(r % period) < active) {
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(Y + r * d + c);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + c);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + c + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        z[e] = (bf16)fmaf(e < 4 ? g0[e & 3] : g1[e & 3], (float)y[e], (float)x[e]);
+    }
+    *reinterpret_cast<bf16x8*>(Z + r * d + c) = z;
+    if (C) *reinterpret_cast<bf16x8*>(C + r * c_stride + c) = z;
+  }
+}
+
 static int grid_for(int64_t work, int per_block, int cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -162,6 +191,15 @@ hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st) {
   const int64_t work = (frame - skip) / 8 * p.S;
   hipLaunchKernelGGL(patch_copy_kernel, dim3(grid_for(work, 1024, 4096)), dim3(256), 0, st, a.X,
                      a.Y, p.S, frame, skip);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual(const bf16* X, const bf16* Y, bf16* Z, int64_t rows, int d,
+                           const float* gamma, int period, int active, bf16* C, int64_t c_stride,
+                           hipStream_t st) {
+  const int64_t work = rows * (d / 8);
+  hipLaunchKernelGGL(residual_kernel, dim3(grid_for(work, 256, 8192)), dim3(256), 0, st, X, Y, Z,
+                     rows, d, gamma, period, active, C, c_stride);
   return hipGetLastError();
 }
 

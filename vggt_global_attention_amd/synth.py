@@ -67,6 +67,39 @@ def make_inputs(w: Workload, fp32: bool = False) -> dict:
     return out
 
 
+BLOCK_TENSORS = ("Wqkv", "Wo", "q_gamma", "q_beta", "k_gamma", "k_beta", "layer_scale")
+
+
+def make_block_weights(w: Workload, n_blocks: int, ls: float = 1e-5) -> list:
+    """Weights of `n_blocks` blocks for a layer schedule, as CPU tensors.
+
+    Block b, tensor i draws from its own generator seeded with
+    10_000_000 + 1000 * cid + 10 * b + i (b < 100).  Same value recipe as
+    make_inputs; the LayerScale vector is ls * (1 + N(0, 0.01)) per channel,
+    fp32.  Returns a list of dicts with the keys of BLOCK_TENSORS.
+    """
+    if n_blocks > 100:
+        raise ValueError("at most 100 blocks")
+    d, H, Dh = w.d, w.H, w.Dh
+    sd = math.sqrt(0.1)
+    out = []
+    for b in range(n_blocks):
+        def gen(name):
+            g = torch.Generator(device="cpu")
+            g.manual_seed(10_000_000 + 1000 * w.cid + 10 * b + BLOCK_TENSORS.index(name))
+            return g
+        out.append({
+            "Wqkv": _normal((3 * d, d), 1.0 / math.sqrt(d), gen("Wqkv"), torch.bfloat16),
+            "Wo": _normal((d, d), 1.0 / math.sqrt(d), gen("Wo"), torch.bfloat16),
+            "q_gamma": 1.0 + _normal((H, Dh), sd, gen("q_gamma")),
+            "q_beta": _normal((H, Dh), sd, gen("q_beta")),
+            "k_gamma": 1.0 + _normal((H, Dh), sd, gen("k_gamma")),
+            "k_beta": _normal((H, Dh), sd, gen("k_beta")),
+            "layer_scale": ls * (1.0 + _normal((d,), 0.1, gen("layer_scale"))),
+        })
+    return out
+
+
 def sample_rows(w: Workload, n_rows: int, seed: int = 7) -> torch.Tensor:
     """A seeded sample of flat row indices (s*T + t) for row-sampled parity.
 
