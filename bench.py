@@ -146,6 +146,53 @@ def loop_stage(w, mode, d, stage, steps, sub=(1, 1)):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def time_descriptor(w, d, per_frame, steps, warmup):
+    """Descriptor attention: the S*T tokens attend to per_frame * S cached
+    descriptors.  Times the append of all descriptors (one chunk), the full
+    attend call and its attention-core stage (HIP events on the call's
+    stream)."""
+    import torch
+    from vggt_global_attention_amd import binding as B
+    from vggt_global_attention_amd import synth
+    from vggt_global_attention_amd.descriptor import DescriptorCache
+    M = per_frame * w.S
+    D = synth.make_descriptors(w, M, 0).to("cuda")
+    cache = DescriptorCache(w.d, w.H, M)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    wts = (d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"])
+    Y = torch.empty_like(d["X"])
+    for _ in range(warmup):
+        cache.reset()
+        cache.append(D, d["Wqkv"], d["k_gamma"], d["k_beta"])
+        cache.attend(d["X"], w.grid_h, w.grid_w, *wts, Y=Y)
+    torch.cuda.synchronize()
+    app = att = core = 0.0
+    for _ in range(steps):
+        cache.reset()
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        cache.append(D, d["Wqkv"], d["k_gamma"], d["k_beta"])
+        e1.record(stream)
+        cache.attend(d["X"], w.grid_h, w.grid_w, *wts, Y=Y)
+        e2.record(stream)
+        cache.attend_stage(B.STAGE_QKV, d["X"], w.grid_h, w.grid_w, *wts, Y)
+        c0, c1 = ev(), ev()
+        c0.record(stream)
+        cache.attend_stage(B.STAGE_CORE, d["X"], w.grid_h, w.grid_w, *wts, Y)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        app += e0.elapsed_time(e1)
+        att += e1.elapsed_time(e2)
+        core += c0.elapsed_time(c1)
+    app, att, core = app / steps, att / steps, core / steps
+    attn_flop = 4.0 * w.N * M * w.d
+    gemm_flop = 4.0 * M * w.d ** 2 + 4.0 * w.N * w.d ** 2   # K, V of the descriptors; q, Wo
+    return {"descriptors": M, "per_frame": per_frame, "append_ms": app, "attend_ms": att,
+            "core_ms": core, "core_tflops": attn_flop / core / 1e9,
+            "tflops": (attn_flop + gemm_flop) / (app + att) / 1e9}
+
+
 def schedule_forward(w, spec, steps, warmup, ls=1e-5):
     """ms per attention-only forward of `spec` and the peak device memory of
     the run (torch's allocator high-water mark: input, state, kept states,
@@ -344,6 +391,8 @@ def main():
         extra["s100_global_rows_share1of8"] = {"ms_per_layer": m2, "tflops": (attn + gemm) / m2 / 1e9,
                                                "core_ms": c2, "core_tflops": attn / c2 / 1e9,
                                                "query_rows": share, "key_rows": w.N}
+        print("[bench] extra s100 descriptor attention, 64 per frame", file=sys.stderr, flush=True)
+        extra["s100_descriptor64"] = time_descriptor(w, d, 64, max(3, a.steps // 2), 2)
         from vggt_global_attention_amd import schedule as S
         print("[bench] extra s100 24-layer attention-only forward", file=sys.stderr, flush=True)
         del d

@@ -71,13 +71,15 @@ extern "C" {
 #define VGGT_ATTN_EWORKSPACE (-4) /* workspace smaller than vggt_attn_workspace_bytes() */
 #define VGGT_ATTN_EHIP       (-5) /* the HIP runtime rejected a launch */
 #define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of
-                                     range, subsampling window < 1, row window outside the set */
+                                     range, subsampling window < 1, row window outside the set,
+                                     descriptor count outside the cache */
 
 /* Block modes. */
 #define VGGT_ATTN_MODE_FRAME    0
 #define VGGT_ATTN_MODE_GLOBAL   1
 #define VGGT_ATTN_MODE_REGISTER 2
 #define VGGT_ATTN_MODE_SUBSAMPLED 3 /* global mode, AVGGT subsampled keys / values */
+#define VGGT_ATTN_MODE_DESCRIPTOR 4 /* every token attends to a descriptor key / value cache */
 
 /* Stages of one call, in order (see vggt_attn_stage). */
 #define VGGT_ATTN_STAGE_PREP 0 /* range bounds, RoPE table, fp16 copy of Wo */
@@ -180,6 +182,62 @@ int vggt_attn_global_rows_stage(int stage, const vggt_attn_shape* shape, int64_t
                                 int64_t row_count, const void* X, const void* Wqkv,
                                 const void* Wo, const float* q_gamma, const float* q_beta,
                                 const float* k_gamma, const float* k_beta, void* Y_rows,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+   Descriptor attention ("FlashVGGT: Efficient and Scalable Visual Geometry
+   Transformers with Compressed Descriptor Attention", chatpaper.ai, abstract):
+   the global step is cross-attention from every image token to a compact set
+   of descriptor tokens, and long sequences run chunk by chunk, reusing the
+   cached descriptors of earlier chunks.  How descriptors are made is not
+   described there: they are the caller's tokens (bf16 [m][d], the model's
+   token width).  Their keys and values go through the layer's Wqkv (K and V
+   rows) and the key LayerNorm (k_gamma, k_beta); they have no place on the
+   patch grid and are not rotated.  The keys / values live in a caller-owned
+   device cache that grows by appends; the caller keeps the fill count.
+   One cache belongs to one layer: every append must pass the same Wqkv,
+   k_gamma and k_beta.
+   --------------------------------------------------------------------------- */
+
+/* Bytes of a descriptor cache for `capacity` descriptors (1 <= capacity <
+   2^31) at the shape's H; 0 if unsupported.  Host arithmetic only. */
+size_t vggt_attn_desc_cache_bytes(const vggt_attn_shape* shape, int64_t capacity);
+
+/* Makes `cache` (256-byte aligned, >= vggt_attn_desc_cache_bytes bytes) an
+   empty cache: every stored key / value zero, no bounds yet.  Required once
+   before the first append. */
+int vggt_attn_desc_cache_init(const vggt_attn_shape* shape, int64_t capacity, void* cache,
+                              size_t cache_bytes, void* stream);
+
+/* Appends the m descriptor tokens D (bf16 [m][d], 16-byte aligned) at
+   positions count .. count + m - 1 of the cache (count = descriptors already
+   appended; 0 <= count, 1 <= m, count + m <= capacity, else
+   VGGT_ATTN_ERANGE).  The stored values carry one power-of-two scale for the
+   whole cache, chosen from the largest descriptor norm seen so far; when an
+   append raises that bound, the values already stored are rescaled (exactly,
+   by a power of two) before the new ones are written.  D must not overlap the
+   cache. */
+int vggt_attn_desc_append(const vggt_attn_shape* shape, int64_t capacity, int64_t count,
+                          const void* D, int64_t m, const void* Wqkv, const float* k_gamma,
+                          const float* k_beta, void* cache, size_t cache_bytes, void* stream);
+
+/* Y = softmax(q k^T / sqrt(Dh)) v Wo^T per head, heads concatenated, for
+   every token of X (bf16 [S][T][d]): q from X exactly as in the global block
+   (LayerNorm with q_gamma / q_beta, 2D RoPE on patch tokens), keys / values
+   the first `count` cached descriptors (1 <= count <= capacity).
+   Workspace: vggt_attn_workspace_bytes(VGGT_ATTN_MODE_DESCRIPTOR).  Y must
+   not overlap X, the weights, the cache or the workspace; the cache is only
+   read. */
+int vggt_attn_desc_attend(const vggt_attn_shape* shape, int64_t capacity, int64_t count,
+                          const void* cache, size_t cache_bytes, const void* X, const void* Wqkv,
+                          const void* Wo, const float* q_gamma, const float* q_beta, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* One stage of vggt_attn_desc_attend, as vggt_attn_stage. */
+int vggt_attn_desc_attend_stage(int stage, const vggt_attn_shape* shape, int64_t capacity,
+                                int64_t count, const void* cache, size_t cache_bytes,
+                                const void* X, const void* Wqkv, const void* Wo,
+                                const float* q_gamma, const float* q_beta, void* Y,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

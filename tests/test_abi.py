@@ -299,3 +299,84 @@ def test_schedule_errors():
         == B.EALIGN
     assert run_sched(blocks=fake_blocks(48, Wqkv=0x500000)) == B.EINVAL   # weight is the state
     assert run_sched(blocks=fake_blocks(48, q_gamma=0x20000000)) == B.EINVAL  # inside caches
+
+
+# ----------------------------------------------------------------------------
+# Descriptor cache and attention
+# ----------------------------------------------------------------------------
+
+def test_descriptor_sizes():
+    s = B.make_shape(**TINY)   # d = 256, H = 4
+    n = B.vggt_attn_desc_cache_bytes(s, 100)
+    assert n == 256 + 2 * 4 * 256 * 64 * 2          # header + keys + values, 256 rows
+    assert B.vggt_attn_desc_cache_bytes(s, 257) == 256 + 2 * 4 * 512 * 64 * 2
+    assert B.vggt_attn_desc_cache_bytes(s, 0) == 0
+    assert B.vggt_attn_desc_cache_bytes(s, 1 << 31) == 0
+    assert B.vggt_attn_desc_cache_bytes(B.make_shape(**dict(TINY, d=192, H=3)), 10) == 0
+    # the attend workspace holds queries only
+    g = B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, s)
+    dws = B.vggt_attn_workspace_bytes(B.MODE_DESCRIPTOR, s)
+    assert 0 < dws < g
+
+
+CACHE = 0x20000000
+
+
+def test_descriptor_init_errors():
+    s = B.make_shape(**TINY)
+    n = B.vggt_attn_desc_cache_bytes(s, 100)
+    assert B.vggt_attn_desc_cache_init(s, 0, CACHE, n, None) == B.ERANGE
+    assert B.vggt_attn_desc_cache_init(s, 100, 0, n, None) == B.EINVAL
+    assert B.vggt_attn_desc_cache_init(s, 100, CACHE + 16, n, None) == B.EALIGN
+    assert B.vggt_attn_desc_cache_init(s, 100, CACHE, n - 1, None) == B.EWORKSPACE
+
+
+def app(count=0, m=10, D=0x100000, W=0x200000, kg=0x400000, kb=0x400100, cache=CACHE,
+        nbytes=None, cap=100):
+    s = B.make_shape(**TINY)
+    n = B.vggt_attn_desc_cache_bytes(s, cap) if nbytes is None else nbytes
+    return B.vggt_attn_desc_append(s, cap, count, D, m, W, kg, kb, cache, n, None)
+
+
+def test_descriptor_append_errors():
+    assert app(count=95, m=6) == B.ERANGE
+    assert app(m=0) == B.ERANGE
+    assert app(count=-1) == B.ERANGE
+    assert app(cap=0) == B.ERANGE
+    assert app(D=0) == B.EINVAL
+    assert app(kb=0) == B.EINVAL
+    assert app(D=0x100008) == B.EALIGN
+    assert app(kg=0x400002) == B.EALIGN
+    assert app(cache=CACHE + 128) == B.EALIGN
+    assert app(nbytes=1024) == B.EWORKSPACE
+    assert app(D=CACHE + 4096) == B.EINVAL          # descriptors inside the cache
+    assert app(W=CACHE - 0x1000) == B.EINVAL        # weights run into the cache
+
+
+def att(count=10, cap=100, cache=CACHE, nbytes=None, Y=0x500000, ws=0x10000000, wsb=1 << 28,
+        stage=None):
+    s = B.make_shape(**TINY)
+    n = B.vggt_attn_desc_cache_bytes(s, cap) if nbytes is None else nbytes
+    args = (s, cap, count, cache, n, 0x100000, 0x200000, 0x300000, 0x400000, 0x400100, Y, ws,
+            wsb, None)
+    if stage is None:
+        return B.vggt_attn_desc_attend(*args)
+    return B.vggt_attn_desc_attend_stage(stage, *args)
+
+
+def test_descriptor_attend_errors():
+    assert att(count=0) == B.ERANGE
+    assert att(count=101) == B.ERANGE
+    assert att(cap=0, count=0, nbytes=1 << 20) == B.ERANGE
+    assert att(cache=0) == B.EINVAL
+    assert att(cache=CACHE + 64) == B.EALIGN
+    assert att(nbytes=4096) == B.EWORKSPACE
+    assert att(Y=CACHE + 1024) == B.EINVAL          # Y inside the cache
+    assert att(ws=CACHE) == B.EINVAL                # workspace is the cache
+    assert att(wsb=4096) == B.EWORKSPACE
+    assert att(stage=9) == B.EINVAL
+    assert att(stage=B.STAGE_CORE, count=0) == B.ERANGE
+    s = B.make_shape(**TINY)
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    assert B.vggt_attn_stage(B.MODE_DESCRIPTOR, B.STAGE_CORE, s, *a, 0x10000000, 1 << 30,
+                             None) == B.EINVAL

@@ -12,14 +12,16 @@ import os
 from .build import LIB
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
-MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED = 0, 1, 2, 3
+MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR = 0, 1, 2, 3, 4
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
 MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
-         "subsampled": MODE_SUBSAMPLED}
+         "subsampled": MODE_SUBSAMPLED, "descriptor": MODE_DESCRIPTOR}
 
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_global_rows",
            "vggt_attn_stage", "vggt_attn_subsampled_stage", "vggt_attn_global_rows_stage",
+           "vggt_attn_desc_cache_bytes", "vggt_attn_desc_cache_init", "vggt_attn_desc_append",
+           "vggt_attn_desc_attend", "vggt_attn_desc_attend_stage",
            "vggt_attn_residual", "vggt_attn_schedule_workspace_bytes", "vggt_attn_schedule_run",
            "vggt_attn_status_str", "vggt_attn_version")
 
@@ -81,6 +83,18 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.vggt_attn_global_rows.argtypes = win
     L.vggt_attn_global_rows_stage.restype = ctypes.c_int
     L.vggt_attn_global_rows_stage.argtypes = [ctypes.c_int] + win
+    P, VP, I64, SZ = ctypes.POINTER(vggt_attn_shape), ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.vggt_attn_desc_cache_bytes.restype = ctypes.c_size_t
+    L.vggt_attn_desc_cache_bytes.argtypes = [P, I64]
+    L.vggt_attn_desc_cache_init.restype = ctypes.c_int
+    L.vggt_attn_desc_cache_init.argtypes = [P, I64, VP, SZ, VP]
+    L.vggt_attn_desc_append.restype = ctypes.c_int
+    L.vggt_attn_desc_append.argtypes = [P, I64, I64, VP, I64, VP, VP, VP, VP, SZ, VP]
+    attend = [P, I64, I64, VP, SZ, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+    L.vggt_attn_desc_attend.restype = ctypes.c_int
+    L.vggt_attn_desc_attend.argtypes = attend
+    L.vggt_attn_desc_attend_stage.restype = ctypes.c_int
+    L.vggt_attn_desc_attend_stage.argtypes = [ctypes.c_int] + attend
     L.vggt_attn_residual.restype = ctypes.c_int
     L.vggt_attn_residual.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
@@ -162,6 +176,34 @@ def vggt_attn_global_rows_stage(stage, shape, row_begin, row_count, X, Wqkv, Wo,
                                 stream) -> int:
     return _call("vggt_attn_global_rows_stage", stage, ctypes.byref(shape), row_begin, row_count,
                  X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y_rows, workspace,
+                 workspace_bytes, stream)
+
+
+def vggt_attn_desc_cache_bytes(shape, capacity) -> int:
+    return lib().vggt_attn_desc_cache_bytes(ctypes.byref(shape), capacity)
+
+
+def vggt_attn_desc_cache_init(shape, capacity, cache, cache_bytes, stream) -> int:
+    return _call("vggt_attn_desc_cache_init", ctypes.byref(shape), capacity, cache, cache_bytes,
+                 stream)
+
+
+def vggt_attn_desc_append(shape, capacity, count, D, m, Wqkv, k_gamma, k_beta, cache,
+                          cache_bytes, stream) -> int:
+    return _call("vggt_attn_desc_append", ctypes.byref(shape), capacity, count, D, m, Wqkv,
+                 k_gamma, k_beta, cache, cache_bytes, stream)
+
+
+def vggt_attn_desc_attend(shape, capacity, count, cache, cache_bytes, X, Wqkv, Wo, q_gamma,
+                          q_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_desc_attend", ctypes.byref(shape), capacity, count, cache,
+                 cache_bytes, X, Wqkv, Wo, q_gamma, q_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_desc_attend_stage(stage, shape, capacity, count, cache, cache_bytes, X, Wqkv, Wo,
+                                q_gamma, q_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_desc_attend_stage", stage, ctypes.byref(shape), capacity, count,
+                 cache, cache_bytes, X, Wqkv, Wo, q_gamma, q_beta, Y, workspace,
                  workspace_bytes, stream)
 
 

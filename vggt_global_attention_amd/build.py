@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvggtattn.so")
 SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip", "subsample.hip",
-           "schedule.cpp"]
+           "desc.hip", "schedule.cpp"]
 
 # Packed fp32 VALU ops are kept out of every kernel on purpose.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -20,7 +20,8 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   int sub_h = o.sub_h, sub_w = o.sub_w;
   if (!s || !p) return VGGT_ATTN_EINVAL;
   if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
-      mode != VGGT_ATTN_MODE_REGISTER && mode != VGGT_ATTN_MODE_SUBSAMPLED)
+      mode != VGGT_ATTN_MODE_REGISTER && mode != VGGT_ATTN_MODE_SUBSAMPLED &&
+      mode != VGGT_ATTN_MODE_DESCRIPTOR)
     return VGGT_ATTN_EINVAL;
   if (s->S < 1 || s->H < 1 || s->d < 1 || s->grid_h < 0 || s->grid_w < 0) return VGGT_ATTN_ESHAPE;
   if (s->d != s->H * kDh || s->d % kGemmBN != 0) return VGGT_ATTN_ESHAPE;
@@ -32,6 +33,10 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   if (!(isfinite(s->ln_eps) && s->ln_eps > 0.f)) return VGGT_ATTN_ERANGE;
   if (s->pos_offset < 0 || s->pos_offset > 65535) return VGGT_ATTN_ERANGE;
   const bool subsampled = mode == VGGT_ATTN_MODE_SUBSAMPLED;
+  const bool desc = mode == VGGT_ATTN_MODE_DESCRIPTOR;
+  if (desc && (o.desc_capacity < 0 || o.desc_capacity >= ((int64_t)1 << 31) ||
+               o.desc_count < 0 || o.desc_count > o.desc_capacity))
+    return VGGT_ATTN_ERANGE;
   if (!subsampled) sub_h = sub_w = 1;
   if (sub_h < 1 || sub_w < 1) return VGGT_ATTN_ERANGE;
   const bool window = o.q_count >= 0;
@@ -53,7 +58,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   p->eps = s->ln_eps;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
-  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc) {
     p->nseq = 1;
     p->L = (int)N;
     p->seq_stride = round_up(N, kAttnBK);
@@ -96,13 +101,20 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     // the subsampled kernel has a single tile shape
     p->attn_qb = 2;
     p->attn_waves = 8;
+  } else if (desc) {
+    // keys / values: the first desc_count entries of the caller's cache
+    p->desc = desc_layout(s->H, o.desc_capacity > 0 ? o.desc_capacity : 1);
+    p->Lk = (int)o.desc_count;
+    p->kv_rows = p->desc.cap_rows;
+    p->kv_seq_stride = round_up(o.desc_count, kAttnBK);
+    p->nD = 0;
   } else {
     p->Lk = p->L;  // (a query window below moves L, never the keys)
     p->kv_rows = p->rows;
     p->kv_seq_stride = p->seq_stride;
     p->nD = 0;
   }
-  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc) {
     p->map = RowMap{p->rows, 0, (int32_t)N, 1, 0};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->map = RowMap{p->seq_stride, s->T, s->T, s->S, 0};
@@ -131,10 +143,15 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   const size_t qkv = (size_t)s->H * (size_t)p->rows * kDh * 2;
   p->off_q = off;
   off += qkv;
-  p->off_k = off;
-  off += qkv;
-  p->off_v = off;
-  off += qkv;
+  if (desc) {
+    // queries only: keys and values come from the cache
+    p->off_k = p->off_v = p->off_q;
+  } else {
+    p->off_k = off;
+    off += qkv;
+    p->off_v = off;
+    off += qkv;
+  }
   if (subsampled) {
     // compact keys / values sized for the largest kept set (sub_h = sub_w = 1:
     // every token), so the workspace size does not depend on the windows
@@ -167,7 +184,16 @@ int check_call(int mode, const vggt_attn_shape* shape, const CallOpts& o, const 
                const float* kb, void* Y, void* ws, size_t ws_bytes, Plan* plan) {
   int st = make_plan(mode, shape, o, plan);
   if (st != VGGT_ATTN_OK) return st;
-  if (!X || !Wqkv || !Wo || !qg || !qb || !kg || !kb || !Y || !ws) return VGGT_ATTN_EINVAL;
+  const bool desc = mode == VGGT_ATTN_MODE_DESCRIPTOR;
+  // descriptor mode: keys come from the cache, so no key affine is passed
+  if (!X || !Wqkv || !Wo || !qg || !qb || (!desc && (!kg || !kb)) || !Y || !ws)
+    return VGGT_ATTN_EINVAL;
+  if (desc) {
+    if (!o.cache) return VGGT_ATTN_EINVAL;
+    if (o.desc_capacity < 1 || o.desc_count < 1) return VGGT_ATTN_ERANGE;
+    if (!aligned(o.cache, 256)) return VGGT_ATTN_EALIGN;
+    if (o.cache_bytes < plan->desc.total) return VGGT_ATTN_EWORKSPACE;
+  }
   if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(Wqkv, 16) || !aligned(Wo, 16) ||
       !aligned(qg, 4) || !aligned(qb, 4) || !aligned(kg, 4) || !aligned(kb, 4) || !aligned(ws, 256))
     return VGGT_ATTN_EALIGN;
@@ -181,6 +207,9 @@ int check_call(int mode, const vggt_attn_shape* shape, const CallOpts& o, const 
   if (overlap(Y, ny, Wqkv, nw) || overlap(Y, ny, Wo, no) || overlap(Y, ny, qg, ng) ||
       overlap(Y, ny, qb, ng) || overlap(Y, ny, kg, ng) || overlap(Y, ny, kb, ng) ||
       overlap(Y, ny, ws, plan->total))
+    return VGGT_ATTN_EINVAL;
+  if (desc && (overlap(Y, ny, o.cache, plan->desc.total) ||
+               overlap(ws, plan->total, o.cache, plan->desc.total)))
     return VGGT_ATTN_EINVAL;
   // The workspace is written by the library: it must not hold any input.
   if (overlap(ws, plan->total, X, nx) || overlap(ws, plan->total, Wqkv, nw) ||
@@ -200,7 +229,7 @@ int run(int mode, const CallOpts& o, int first_stage, int last_stage,
   if (st != VGGT_ATTN_OK) return st;
   Ptrs a{reinterpret_cast<const bf16*>(X), reinterpret_cast<const bf16*>(Wqkv),
          reinterpret_cast<const bf16*>(Wo), qg, qb, kg, kb, reinterpret_cast<bf16*>(Y),
-         reinterpret_cast<char*>(ws)};
+         reinterpret_cast<char*>(ws), reinterpret_cast<char*>(const_cast<void*>(o.cache))};
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   for (int stage = first_stage; stage <= last_stage; ++stage) {
     hipError_t e = hipSuccess;
@@ -272,7 +301,9 @@ int vggt_attn_global_register(VGGT_ARGS) {
 
 int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {
   if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
-  if (mode == VGGT_ATTN_MODE_SUBSAMPLED) return VGGT_ATTN_EINVAL;  // needs the windows
+  // these modes need the windows / the cache: they have stage entries of their own
+  if (mode == VGGT_ATTN_MODE_SUBSAMPLED || mode == VGGT_ATTN_MODE_DESCRIPTOR)
+    return VGGT_ATTN_EINVAL;
   return run(mode, CallOpts(), stage, stage, VGGT_PASS);
 }
 
@@ -333,6 +364,85 @@ int vggt_attn_residual(const void* X, const void* Y, void* Z, int64_t rows, int3
                                  reinterpret_cast<bf16*>(C), c_stride,
                                  reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? VGGT_ATTN_OK : VGGT_ATTN_EHIP;
+}
+
+size_t vggt_attn_desc_cache_bytes(const vggt_attn_shape* shape, int64_t capacity) {
+  Plan plan;
+  CallOpts o;
+  o.desc_capacity = capacity;
+  if (capacity < 1 || make_plan(VGGT_ATTN_MODE_DESCRIPTOR, shape, o, &plan) != VGGT_ATTN_OK)
+    return 0;
+  return plan.desc.total;
+}
+
+int vggt_attn_desc_cache_init(const vggt_attn_shape* shape, int64_t capacity, void* cache,
+                              size_t cache_bytes, void* stream) {
+  Plan plan;
+  CallOpts o;
+  o.desc_capacity = capacity;
+  int st = make_plan(VGGT_ATTN_MODE_DESCRIPTOR, shape, o, &plan);
+  if (st != VGGT_ATTN_OK) return st;
+  if (capacity < 1) return VGGT_ATTN_ERANGE;
+  if (!cache) return VGGT_ATTN_EINVAL;
+  if (!aligned(cache, 256)) return VGGT_ATTN_EALIGN;
+  if (cache_bytes < plan.desc.total) return VGGT_ATTN_EWORKSPACE;
+  hipError_t e = launch_desc_init(reinterpret_cast<char*>(cache), plan.desc, plan.H,
+                                  reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VGGT_ATTN_OK : VGGT_ATTN_EHIP;
+}
+
+int vggt_attn_desc_append(const vggt_attn_shape* shape, int64_t capacity, int64_t count,
+                          const void* D, int64_t m, const void* Wqkv, const float* k_gamma,
+                          const float* k_beta, void* cache, size_t cache_bytes, void* stream) {
+  Plan plan;
+  CallOpts o;
+  o.desc_capacity = capacity;
+  int st = make_plan(VGGT_ATTN_MODE_DESCRIPTOR, shape, o, &plan);
+  if (st != VGGT_ATTN_OK) return st;
+  if (capacity < 1 || count < 0 || m < 1 || count > capacity - m) return VGGT_ATTN_ERANGE;
+  if (!D || !Wqkv || !k_gamma || !k_beta || !cache) return VGGT_ATTN_EINVAL;
+  if (!aligned(D, 16) || !aligned(Wqkv, 16) || !aligned(k_gamma, 4) || !aligned(k_beta, 4) ||
+      !aligned(cache, 256))
+    return VGGT_ATTN_EALIGN;
+  if (cache_bytes < plan.desc.total) return VGGT_ATTN_EWORKSPACE;
+  const size_t nc = plan.desc.total, nd = (size_t)m * plan.d * 2;
+  const size_t nw = (size_t)3 * plan.d * plan.d * 2, ng = (size_t)plan.H * kDh * 4;
+  if (overlap(cache, nc, D, nd) || overlap(cache, nc, Wqkv, nw) ||
+      overlap(cache, nc, k_gamma, ng) || overlap(cache, nc, k_beta, ng))
+    return VGGT_ATTN_EINVAL;
+  hipError_t e = launch_desc_append(reinterpret_cast<char*>(cache), plan.desc, plan.H, plan.d,
+                                    plan.eps, count, reinterpret_cast<const bf16*>(D), m,
+                                    reinterpret_cast<const bf16*>(Wqkv), k_gamma, k_beta,
+                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VGGT_ATTN_OK : VGGT_ATTN_EHIP;
+}
+
+#define VGGT_DESC_ARGS                                                                      \
+  const vggt_attn_shape *shape, int64_t capacity, int64_t count, const void *cache,         \
+      size_t cache_bytes, const void *X, const void *Wqkv, const void *Wo,                  \
+      const float *q_gamma, const float *q_beta, void *Y, void *workspace,                  \
+      size_t workspace_bytes, void *stream
+
+static CallOpts desc_opts(int64_t capacity, int64_t count, const void* cache, size_t cache_bytes) {
+  CallOpts o;
+  o.cache = cache;
+  o.cache_bytes = cache_bytes;
+  o.desc_capacity = capacity;
+  o.desc_count = count;
+  return o;
+}
+
+int vggt_attn_desc_attend(VGGT_DESC_ARGS) {
+  return run(VGGT_ATTN_MODE_DESCRIPTOR, desc_opts(capacity, count, cache, cache_bytes),
+             VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, shape, X, Wqkv, Wo, q_gamma, q_beta,
+             nullptr, nullptr, Y, workspace, workspace_bytes, stream);
+}
+
+int vggt_attn_desc_attend_stage(int stage, VGGT_DESC_ARGS) {
+  if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
+  return run(VGGT_ATTN_MODE_DESCRIPTOR, desc_opts(capacity, count, cache, cache_bytes), stage,
+             stage, shape, X, Wqkv, Wo, q_gamma, q_beta, nullptr, nullptr, Y, workspace,
+             workspace_bytes, stream);
 }
 
 const char* vggt_attn_status_str(int status) {

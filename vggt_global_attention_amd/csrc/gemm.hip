@@ -33,6 +33,9 @@ struct GemmArgs {
   int fgroups;    // output-feature groups walked one after the other (divides Nf / 128)
   int64_t m_first;       // first workspace row of the token tiles (a multiple of the tile)
   int64_t q_lo, q_hi;    // QKV: q is needed only for rows [q_lo, q_hi)
+  int f_off;             // QKV: feature index (in [q|k|v]) of A's first row
+  int64_t dst_off;       // QKV: workspace row w is stored at row w + dst_off
+  int real_only;         // QKV: rows without a token write nothing
   RowMap map;            // QKV: workspace row -> X row; OUT: workspace row -> Y row
   int T, gw, off, d;
   float eps;
@@ -68,8 +71,9 @@ template <int EPI, int TB>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2][TB],
                                               int64_t mbase, int fbase, int j, int h, int lane) {
   if (EPI == kEpiQKV) {
-    const int blk = fbase / g.d;  // 0: q, 1: k, 2: v
-    const int hd = (fbase - blk * g.d) / kDh;
+    const int fq = fbase + g.f_off;
+    const int blk = fq / g.d;  // 0: q, 1: k, 2: v
+    const int hd = (fq - blk * g.d) / kDh;
     if (blk < 2) {
       const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
       const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
@@ -131,6 +135,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
           }
         }
         float n2 = 0.f;
+        const bool store = !g.real_only || src >= 0;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
@@ -142,7 +147,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
               const float back = (float)o[r];
               n2 = fmaf(back, back, n2);
             }
-            *reinterpret_cast<f16x4*>(dst + w * kDh + fb * 32 + 8 * rq + 4 * h) = o;
+            if (store)
+              *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) = o;
           }
         n2 += __shfl_xor(n2, 32);
         if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
@@ -158,10 +164,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
+        if (g.real_only && g.map.src(w) < 0) continue;
+        const int64_t x = w + g.dst_off;
         // Key position inside its aligned group of 16: key 8a + 4c + b is
         // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
         // the attention kernel's MFMA consumes probabilities.
-        const int64_t pos = (w & ~(int64_t)15) | (((w >> 2) & 1) << 3) | (((w >> 3) & 1) << 2) | (w & 3);
+        const int64_t pos = (x & ~(int64_t)15) | (((x >> 2) & 1) << 3) | (((x >> 3) & 1) << 2) | (x & 3);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
   m0 += g.m_first;
   // query rows outside the window need no q (whole workgroup leaves)
-  if (EPI == kEpiQKV && n0 < g.d && (m0 + kGemmBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kGemmBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (int64_t)n0 * g.K;
   const uint16_t* Bbase = reinterpret_cast<const uint16_t*>(g.B);
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
   }
   m0 += g.m_first;
   // query rows outside the window need no q (whole workgroup leaves)
-  if (EPI == kEpiQKV && n0 < g.d && (m0 + kDmaBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kDmaBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   // DMA sources of this lane: A rows (q*4 + wave)*16 + lane/4 (q < 2), B rows
   // likewise (q < 4); column chunk (lane%4) ^ ((lane/16) & 3).
@@ -513,7 +521,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     n0 = (logical % ntn) * kWBN;
   }
   m0 += g.m_first;
-  if (EPI == kEpiQKV && n0 < g.d && (m0 + kWBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kWBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   // DMA: instruction q of wave w covers rows (q*8 + w)*8 .. +7 (q < 4) of A
   // and of B; lane row lane/8.
@@ -651,7 +659,8 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   GemmArgs g = base_args(p, a);
   g.A = a.Wqkv;
   g.B = a.X;
-  g.Nf = 3 * p.d;
+  // descriptor mode: queries only (the keys / values are in the cache)
+  g.Nf = p.mode == VGGT_ATTN_MODE_DESCRIPTOR ? p.d : 3 * p.d;
   g.K = p.d;
   const int kind = gemm_kind(p, g.Nf);
   g.fgroups = feature_groups(g.Nf, g.K, 2, kind == 2 ? kWBN : kGemmBN);
@@ -669,6 +678,64 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
 }
 
 hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st);
+
+hipError_t launch_desc_kv(char* cache, const DescLayout& L, int H, int d, float eps,
+                          int64_t count, const bf16* D, int64_t m, const bf16* Wqkv,
+                          const float* kg, const float* kb, hipStream_t st) {
+  // K and V rows of Wqkv over the m descriptor rows; tile rows past m read
+  // row 0 and store nothing.  Descriptors carry no grid position: with T = 1
+  // every row is token 0 of its "frame", which is never rotated.
+  const int64_t tiles = (m + kWBM - 1) / kWBM;
+  GemmArgs g{};
+  g.A = Wqkv + (int64_t)d * d;
+  g.B = D;
+  g.rows = L.cap_rows;  // head stride of the cache arrays
+  g.Nf = 2 * d;
+  g.K = d;
+  g.m_first = 0;
+  g.q_lo = 0;
+  g.q_hi = tiles * kWBM;
+  g.f_off = d;
+  g.dst_off = count;
+  g.real_only = 1;
+  g.map = RowMap{tiles * kWBM, 0, (int32_t)m, 1, 0};
+  g.T = 1;
+  g.gw = 1;
+  g.off = 0;
+  g.d = d;
+  g.eps = eps;
+  g.qg = nullptr;
+  g.qb = nullptr;
+  g.kg = kg;
+  g.kb = kb;
+  g.rope = nullptr;
+  g.sc = reinterpret_cast<Scalars*>(cache);
+  g.q = nullptr;
+  g.k = reinterpret_cast<f16*>(cache + L.off_k);
+  g.vt = reinterpret_cast<f16*>(cache + L.off_v);
+  g.y = nullptr;
+  int kind = 2;
+  if (const char* e = getenv("VGGT_GEMM")) {
+    const int v = atoi(e);
+    if (v >= 0 && v < 2) kind = v;
+  }
+  if (kind == 2 && g.Nf % kWBN != 0) kind = 1;
+  const int bn = kind == 2 ? kWBN : kind == 1 ? kDmaBN : kGemmBN;
+  g.fgroups = feature_groups(g.Nf, g.K, 2, bn);
+  if (kind == 2) {
+    hipLaunchKernelGGL(gemm_wide_kernel<kEpiQKV>, dim3((unsigned)(tiles * (g.Nf / kWBN))), dim3(512),
+                       0, st, g);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL(gemm_dma_kernel<kEpiQKV>,
+                       dim3((unsigned)(tiles * (kWBM / kDmaBM) * (g.Nf / kDmaBN))), dim3(256), 0, st,
+                       g);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<kEpiQKV>,
+                       dim3((unsigned)(tiles * (kWBM / kGemmBM) * (g.Nf / kGemmBN))), dim3(256), 0,
+                       st, g);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   GemmArgs g = base_args(p, a);

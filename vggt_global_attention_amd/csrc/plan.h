@@ -23,7 +23,34 @@ struct CallOpts {
   int sub_h = 1, sub_w = 1;  // subsampled mode: windows
   int64_t q_begin = 0;       // global mode: first query row computed
   int64_t q_count = -1;      // global mode: query rows computed (-1: every row)
+  // descriptor mode: the caller's key / value cache and its fill
+  const void* cache = nullptr;
+  size_t cache_bytes = 0;
+  int64_t desc_capacity = 0;
+  int64_t desc_count = 0;
 };
+
+// Descriptor key / value cache (caller-owned device buffer, 256-byte
+// aligned): a Scalars header (xnorm = max norm of the appended descriptor
+// rows, wvnorm = max norm of the V rows of Wqkv, pad = the power-of-two
+// exponent the stored values carry, as int bits; kmax[H] = max key norm per
+// head), then keys fp16 [H][cap_rows][64] and values fp16 [H][64][cap_rows]
+// (keys permuted inside aligned groups of 16, as in the workspace).
+struct DescLayout {
+  int64_t cap_rows;
+  size_t off_k, off_v, total;
+};
+inline DescLayout desc_layout(int H, int64_t capacity) {
+  DescLayout L;
+  L.cap_rows = (capacity + kKvAlign - 1) / kKvAlign * kKvAlign;
+  const size_t hdr = ((sizeof(float) * (4 + H)) + 255) / 256 * 256;
+  const size_t arr = (size_t)H * L.cap_rows * kDh * 2;
+  L.off_k = hdr;
+  L.off_v = hdr + arr;
+  L.total = hdr + 2 * arr;
+  return L;
+}
+constexpr int kDescEmpty = 127;  // exponent of an empty cache: above every real one
 
 struct Plan {
   int mode;
@@ -53,6 +80,7 @@ struct Plan {
   // workspace carve-up (byte offsets)
   size_t off_scal, off_rope, off_wo, off_q, off_k, off_v;
   size_t off_kc, off_vc, off_sums, off_part;  // subsampled mode only (else 0)
+  DescLayout desc;     // descriptor mode: layout of the key / value cache
   size_t total;
 };
 
@@ -66,6 +94,7 @@ struct Ptrs {
   const float* kb;
   bf16* Y;
   char* ws;
+  char* cache;  // descriptor mode: the key / value cache (read-only there)
 };
 
 // Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  `o` carries
@@ -90,9 +119,11 @@ inline f16* ws_k(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a
 inline f16* ws_v(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_v); }
 // keys / values the attention loop streams (compact copies in subsampled mode)
 inline f16* ws_kloop(const Plan& p, const Ptrs& a) {
+  if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return reinterpret_cast<f16*>(a.cache + p.desc.off_k);
   return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_kc : p.off_k));
 }
 inline f16* ws_vloop(const Plan& p, const Ptrs& a) {
+  if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return reinterpret_cast<f16*>(a.cache + p.desc.off_v);
   return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_vc : p.off_v));
 }
 inline float* ws_sums(const Plan& p, const Ptrs& a) {
@@ -103,6 +134,23 @@ inline float* ws_sums(const Plan& p, const Ptrs& a) {
 hipError_t launch_residual(const bf16* X, const bf16* Y, bf16* Z, int64_t rows, int d,
                            const float* gamma, int period, int active, bf16* C, int64_t c_stride,
                            hipStream_t st);
+
+// Descriptor cache (desc.hip): fill an empty cache; append m descriptor
+// tokens D [m][d] at position `count` (norm bounds, rescale of the stored
+// values when the bound grows, then the K / V projection); copy the cache's
+// bounds into a call's scalars (prep stage of the descriptor mode).
+hipError_t launch_desc_init(char* cache, const DescLayout& L, int H, hipStream_t st);
+hipError_t launch_desc_append(char* cache, const DescLayout& L, int H, int d, float eps,
+                              int64_t count, const bf16* D, int64_t m, const bf16* Wqkv,
+                              const float* kg, const float* kb, hipStream_t st);
+hipError_t launch_desc_load(const Plan& p, const Ptrs& a, hipStream_t st);
+// K / V projection of descriptor rows into the cache (gemm.hip).
+hipError_t launch_desc_kv(char* cache, const DescLayout& L, int H, int d, float eps,
+                          int64_t count, const bf16* D, int64_t m, const bf16* Wqkv,
+                          const float* kg, const float* kb, hipStream_t st);
+// Max row norm of `rows` rows of X (through `map`) into *out (atomic max; prep.hip).
+hipError_t launch_rownorm_max(const bf16* X, int64_t rows, int d, RowMap map, float* out,
+                              hipStream_t st);
 
 // Subsampled mode: gather the kept tokens' keys / values and sum the
 // discarded ones (first half of the CORE stage).

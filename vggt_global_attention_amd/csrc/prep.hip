@@ -171,17 +171,29 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(sc),
                      4 + p.H, sub ? ws_sums(p, a) : nullptr, sub ? 128 * p.H : 0, ws_rope(p, a),
                      p.rope_npos, p.base);
-  // X rows of the set(s): walk the workspace rows through the row map.
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 16, 2048)), dim3(256), 0, st,
-                     a.X, p.rows, p.d, p.map, &sc->xnorm);
-  RowMap ident{INT64_MAX / 2, 0, p.d, 1};
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 16, 2048)), dim3(256), 0, st,
-                     a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
+  // Descriptor mode: no values are projected here; the bounds of the cached
+  // values are copied in after the Wo conversion (launch_desc_load).
+  if (p.mode != VGGT_ATTN_MODE_DESCRIPTOR) {
+    // X rows of the set(s): walk the workspace rows through the row map.
+    hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 16, 2048)), dim3(256), 0, st,
+                       a.X, p.rows, p.d, p.map, &sc->xnorm);
+    RowMap ident{INT64_MAX / 2, 0, p.d, 1};
+    hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 16, 2048)), dim3(256), 0, st,
+                       a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
+  }
   const int64_t n8 = (int64_t)p.d * p.d / 8;
   hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 1024, 256)), dim3(256), 0, st, a.Wo, n8,
                      &sc->woabs);
   hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
                      n8, (const Scalars*)sc, ws_wo(p, a));
+  if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return launch_desc_load(p, a, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_max(const bf16* X, int64_t rows, int d, RowMap map, float* out,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(rows, 16, 2048)), dim3(256), 0, st, X, rows,
+                     d, map, out);
   return hipGetLastError();
 }
 

@@ -100,6 +100,15 @@ def make_block_weights(w: Workload, n_blocks: int, ls: float = 1e-5) -> list:
     return out
 
 
+def make_descriptors(w: Workload, M: int, salt: int = 0, scale: float = 1.0) -> torch.Tensor:
+    """M descriptor tokens [M, d], bf16: scale * N(0, 1), the value recipe of X
+    (descriptors are token states of the model's width).  Seed
+    20_000_000 + 1000 * cid + salt."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(20_000_000 + 1000 * w.cid + salt)
+    return _normal((M, w.d), scale, g).to(torch.bfloat16)
+
+
 def sample_rows(w: Workload, n_rows: int, seed: int = 7) -> torch.Tensor:
     """A seeded sample of flat row indices (s*T + t) for row-sampled parity.
 
