@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
+    ap.add_argument("--descriptors", type=int, default=0, metavar="PER_FRAME",
+                    help="instead of the layer: descriptor attention of the workload's tokens "
+                         "against PER_FRAME cached descriptors per frame")
     ap.add_argument("--schedule", default=None, metavar="S_LIST",
                     help="instead of the layer: time the 24-layer attention-only schedule and "
                          "record its peak device memory at these frame counts, e.g. 1,25,100")
@@ -320,6 +323,11 @@ def main():
     sub = tuple(int(x) for x in a.sub.lower().split("x")) if a.mode == "subsampled" else (1, 1)
     print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
     inp, d = gpu_inputs(w)
+    if a.descriptors:
+        r = time_descriptor(w, d, a.descriptors, a.steps, a.warmup)
+        r["workload"] = w.name
+        print(json.dumps({"descriptor_attention": r}), flush=True)
+        return
     if a.only_stage:
         ms = loop_stage(w, a.mode, d, a.only_stage, a.steps, sub)
         print(json.dumps({"stage": a.only_stage, "mode": a.mode, "workload": w.name,
