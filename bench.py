@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
+    ap.add_argument("--hbm", action="store_true",
+                    help="instead of the layer: HBM-bound kernels (register-mode patch copy, "
+                         "residual update) at 500 frames, warm and after a 512 MB cache scrub")
     ap.add_argument("--descriptors", type=int, default=0, metavar="PER_FRAME",
                     help="instead of the layer: descriptor attention of the workload's tokens "
                          "against PER_FRAME cached descriptors per frame")
@@ -196,6 +199,63 @@ def time_descriptor(w, d, per_frame, steps, warmup):
             "tflops": (attn_flop + gemm_flop) / (app + att) / 1e9}
 
 
+def hbm_kernels(steps):
+    """GB/s of the HBM-bound kernels at 500 frames (X: 1.06 GB): the register
+    block's patch copy (the call with Y != X minus the in-place call) and the
+    residual update, each timed warm (back to back) and cold (a 512 MB write,
+    twice the 256 MB Infinity Cache, before every call)."""
+    import torch
+    from vggt_global_attention_amd import api, configs, synth
+    from vggt_global_attention_amd import schedule as S
+    w = configs.WORKLOADS["s500"]
+    inp, d = gpu_inputs(w)
+    stream = torch.cuda.current_stream()
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, cold):
+        tot = 0.0
+        for _ in range(steps):
+            if cold:
+                scrub.fill_(1)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / steps
+
+    args = [d[k] for k in ("Wqkv", "Wo", "q_gamma", "q_beta", "k_gamma", "k_beta")]
+    blk = api.Block("register", d["X"], w.H, w.grid_h, w.grid_w)
+    Xi = d["X"].clone()
+    Y = torch.empty_like(d["X"])
+    out = {}
+    copy_bytes = 2.0 * w.S * (w.T - 17) * w.d * 2
+    for cold in (False, True):
+        blk(d["X"], *args, Y=Y)
+        blk(Xi, *args, Y=Xi)
+        torch.cuda.synchronize()
+        full = timed(lambda: blk(d["X"], *args, Y=Y), cold)
+        inplace = timed(lambda: blk(Xi, *args, Y=Xi), cold)
+        ms = full - inplace
+        out[f"patch_copy_s500_{'cold' if cold else 'warm'}"] = {
+            "bytes": copy_bytes, "ms": ms, "gbs": copy_bytes / ms / 1e6,
+            "register_call_ms": full, "register_call_inplace_ms": inplace}
+    del Xi, Y
+    gamma = torch.full((w.d,), 0.5, dtype=torch.float32, device="cuda")
+    Yr = d["X"].flip(0).contiguous()
+    Z = torch.empty_like(d["X"])
+    res_bytes = 3.0 * w.N * w.d * 2
+    for cold in (False, True):
+        S.residual(d["X"], Yr, gamma, Z=Z)
+        torch.cuda.synchronize()
+        ms = timed(lambda: S.residual(d["X"], Yr, gamma, Z=Z), cold)
+        out[f"residual_s500_{'cold' if cold else 'warm'}"] = {
+            "bytes": res_bytes, "ms": ms, "gbs": res_bytes / ms / 1e6}
+    return out
+
+
 def schedule_forward(w, spec, steps, warmup, ls=1e-5):
     """ms per attention-only forward of `spec` and the peak device memory of
     the run (torch's allocator high-water mark: input, state, kept states,
@@ -258,6 +318,28 @@ def schedule_sweep(frames, steps, warmup):
     return rows
 
 
+def host_info():
+    """CPU model, logical CPUs and NumPy's BLAS, for the oracle timing."""
+    import platform
+    import numpy as np
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "blas": blas}
+
+
 def cpu_baseline(w, inp, n_rows):
     """The fp64 oracle on a bounded sample of the same layer: k/v for all N
     tokens, then q, attention and output projection for n_rows query rows."""
@@ -282,6 +364,7 @@ def cpu_baseline(w, inp, n_rows):
     flop = 4.0 * n * d * d + len(rows) * (2.0 * d * d + 4.0 * n * d + 2.0 * d * d)
     full_s = dt * (w.flop("global") / flop)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host": host_info(),
             "sample": f"{w.name} global layer: k/v for all {n} tokens + {len(rows)} sampled query "
                       f"rows (q, attention over all keys, Wo); {flop / 1e12:.3f} TFLOP in {dt:.1f} s; "
                       f"full layer extrapolates to {full_s / 60:.0f} min",
@@ -310,6 +393,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n,
                           "bytes_written_per_copy": n, "copies": 3}))
+        return
+    if a.hbm:
+        print(json.dumps({"hbm_kernels": hbm_kernels(a.steps), "peak_gbs": PEAK_HBM_GBS}),
+              flush=True)
         return
     if a.schedule:
         frames = [int(x) for x in a.schedule.split(",")]
