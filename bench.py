@@ -243,6 +243,16 @@ def hbm_kernels(steps):
             "bytes": copy_bytes, "ms": ms, "gbs": copy_bytes / ms / 1e6,
             "register_call_ms": full, "register_call_inplace_ms": inplace}
     del Xi, Y
+    # reference: the runtime's own device-to-device copy of the same tensor
+    Xc = torch.empty_like(d["X"])
+    xbytes = 2.0 * w.N * w.d * 2
+    for cold in (False, True):
+        Xc.copy_(d["X"])
+        torch.cuda.synchronize()
+        ms = timed(lambda: Xc.copy_(d["X"]), cold)
+        out[f"torch_copy_s500_{'cold' if cold else 'warm'}"] = {
+            "bytes": xbytes, "ms": ms, "gbs": xbytes / ms / 1e6}
+    del Xc
     gamma = torch.full((w.d,), 0.5, dtype=torch.float32, device="cuda")
     Yr = d["X"].flip(0).contiguous()
     Z = torch.empty_like(d["X"])
