@@ -46,6 +46,21 @@ struct GemmArgs {
   bf16* y;
 };
 
+// RowMap::src in 32-bit arithmetic: every workspace row and token index of a
+// call is below 2^31 (checked on the host), so the 64-bit divisions of the
+// generic map (a long instruction sequence each) become 32-bit ones.
+__device__ __forceinline__ int64_t row_src(const RowMap& m, int64_t w64) {
+  const int v = (int)(w64 - m.base);
+  if (v < 0) return -1;
+  int grp = 0, t = v;
+  if (m.grp_stride <= 0x7fffffff) {
+    const unsigned gs = (unsigned)m.grp_stride;
+    grp = (int)((unsigned)v / gs);
+    t = v - grp * (int)gs;
+  }
+  return (t < m.grp_valid && grp < m.ngroups) ? (int64_t)(grp * (int)m.src_stride + t) : -1;
+}
+
 enum { kEpiQKV = 0, kEpiOut = 1 };
 
 template <int EPI>
@@ -93,7 +108,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
-        const int64_t src = g.map.src(w);
+        const int64_t src = row_src(g.map, w);
         float s1 = 0.f;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
@@ -117,7 +132,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
           for (int r = 0; r < 16; ++r)
             y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
         if (src >= 0) {
-          const int t = (int)(src % g.T);
+          const int t = (int)src % g.T;
           if (t >= kSpecial) {
             const int pidx = t - kSpecial;
             const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
@@ -164,7 +179,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
-        if (g.real_only && g.map.src(w) < 0) continue;
+        if (g.real_only && row_src(g.map, w) < 0) continue;
         const int64_t x = w + g.dst_off;
         // Key position inside its aligned group of 16: key 8a + 4c + b is
         // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
@@ -186,7 +201,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int64_t w = mbase + tb * 32 + j;
-      const int64_t src = g.map.src(w);
+      const int64_t src = row_src(g.map, w);
       if (src < 0) continue;
       bf16* dst = g.y + src * g.d + fbase + 4 * h;
 #pragma unroll
@@ -198,6 +213,181 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
           for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][4 * rq + r] * scale);
           *reinterpret_cast<bf16x4*>(dst + fb * 32 + 8 * rq) = o;
         }
+    }
+  }
+}
+
+// Epilogue of the 256 x 256 kernel, staged through LDS: each wave first
+// writes its finished 128-token x 64-feature block into its own 16 KB of the
+// (by then idle) operand buffers, then stores it with 16-byte lanes along
+// whole 128-byte rows -- q / k / O rows token-major, v^T feature-major --
+// instead of the 8- and 2-byte scattered stores of gemm_epilogue, whose
+// instruction count dominated the epilogue.  Token-major rows are swizzled
+// by chunk ^ (token & 7), feature-major rows by chunk ^ (4 * bit 2 of the
+// feature), which keeps both the writes and the reads free of bank conflicts.
+// The descriptor append path (rows without a token must not be stored, keys
+// not aligned to 16) keeps the direct stores for v^T.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (&acc)[2][4],
+                                                     int64_t mbase, int fbase, int j, int h,
+                                                     int lane, char* lds) {
+  constexpr int TB = 4;
+  if (EPI == kEpiQKV) {
+    const int fq = fbase + g.f_off;
+    const int blk = fq / g.d;  // 0: q, 1: k, 2: v
+    const int hd = (fq - blk * g.d) / kDh;
+    if (blk == 2 && (g.real_only || (g.dst_off & 15) != 0)) {
+      gemm_epilogue<EPI, TB>(g, acc, mbase, fbase, j, h, lane);
+      return;
+    }
+    if (blk < 2) {
+      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
+      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
+      float gm[2][16], bt[2][16];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          gm[fb][r] = gam[f];
+          bt[fb][r] = bet[f];
+        }
+      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
+      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
+      float kmx = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int tl = tb * 32 + j;
+        const int64_t src = row_src(g.map, mbase + tl);
+        float s1 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
+        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
+        float s2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dv = acc[fb][tb][r] - mean;
+            s2 = fmaf(dv, dv, s2);
+          }
+        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
+        const float rstd = 1.f / sqrtf(var + g.eps);
+        float y[2][16];
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
+        if (src >= 0) {
+          const int t = (int)src % g.T;
+          if (t >= kSpecial) {
+            const int pidx = t - kSpecial;
+            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+                const float2 cs = g.rope[pos[fb] * 16 + i];
+                const float a = y[fb][r], b = y[fb][r + 8];
+                y[fb][r] = a * cs.x - b * cs.y;
+                y[fb][r + 8] = b * cs.x + a * cs.y;
+              }
+          }
+        }
+        float n2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            f16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
+              const float back = (float)o[r];
+              n2 = fmaf(back, back, n2);
+            }
+            // features fb*32 + 8*rq + 4*h .. +3: 16-byte chunk fb*4 + rq, half h
+            *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) = o;
+          }
+        n2 += __shfl_xor(n2, 32);
+        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
+      }
+      if (blk == 1) {
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
+      }
+      lds_wave_sync();
+      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * 128 + ((c ^ (tl & 7)) << 4));
+        const int64_t w = mbase + tl;
+        if (!g.real_only || row_src(g.map, w) >= 0)
+          *reinterpret_cast<u32x4*>(dst + (w + g.dst_off) * kDh + c * 8) = v;
+      }
+    } else {
+      const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int tl = tb * 32 + j;
+        // slot of token tl inside its aligned group of 16 (bits 2 and 3 swapped)
+        const int slot = (tl & ~15) | (((tl >> 2) & 1) << 3) | (((tl >> 3) & 1) << 2) | (tl & 3);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int chunk = (slot >> 3) ^ (((e >> 2) & 1) << 2);
+            *reinterpret_cast<f16*>(lds + e * 256 + (chunk << 4) + (slot & 7) * 2) =
+                (f16)ldexpf(acc[fb][tb][r], kv);
+          }
+      }
+      lds_wave_sync();
+      f16* dst = g.vt + (int64_t)hd * kDh * g.rows + mbase + g.dst_off;
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, e = q >> 4, c = q & 15;
+        const u32x4 v =
+            *reinterpret_cast<const u32x4*>(lds + e * 256 + ((c ^ (((e >> 2) & 1) << 2)) << 4));
+        *reinterpret_cast<u32x4*>(dst + (int64_t)e * g.rows + c * 8) = v;
+      }
+    }
+  } else {
+    const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+    const int ws = range_exponent(g.sc->woabs);
+    const float scale = ldexpf(1.f, -(kv + ws));
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int tl = tb * 32 + j;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)(acc[fb][tb][4 * rq + r] * scale);
+          *reinterpret_cast<bf16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) = o;
+        }
+    }
+    lds_wave_sync();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
+      const int64_t src = row_src(g.map, mbase + tl);
+      if (src < 0) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * 128 + ((c ^ (tl & 7)) << 4));
+      *reinterpret_cast<u32x4*>(g.y + src * g.d + fbase + c * 8) = v;
     }
   }
 }
@@ -254,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     soff[i] = swz(row, col);
     aptr[i] = A + (int64_t)row * g.K + col * 8;
     if (EPI == kEpiQKV) {
-      const int64_t src = g.map.src(m0 + row);
+      const int64_t src = row_src(g.map, m0 + row);
       bval[i] = src >= 0;
       bptr[i] = Bbase + (bval[i] ? src : 0) * g.K + col * 8;
     } else {
@@ -363,6 +553,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
   constexpr int kAB = kDmaBN * 64;  // A stage: 128 feature rows x 64 B
   constexpr int kBB = kDmaBM * 64;  // B stage: 256 token rows x 64 B
   __shared__ __attribute__((aligned(1024))) char smem[kDmaStages][kAB + kBB];
+  static_assert(sizeof(smem) >= 4 * 16384, "staged epilogue: 16 KB of LDS per wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -405,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
     if (EPI == kEpiQKV) {
       // rows without a token read X row 0: finite values whose outputs are
       // masked keys or never read
-      const int64_t src = g.map.src(w);
+      const int64_t src = row_src(g.map, w);
       bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
     } else {
       bptr[q] = Bb + w * kDh + lcol * 8;
@@ -475,7 +666,9 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();
   }
 
-  gemm_epilogue<EPI, 4>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane);
+  // the loop's last barrier: no wave reads the operand stages any more
+  gemm_epilogue_staged<EPI>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane,
+                            &smem[0][0] + wave * 16384);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,6 +692,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
   constexpr int kAB = kWBN * 128;  // A stage: 256 feature rows x 128 B
   constexpr int kBB = kWBM * 128;  // B stage: 256 token rows x 128 B
   __shared__ __attribute__((aligned(1024))) char smem[2][kAB + kBB];
+  static_assert(sizeof(smem) >= 8 * 16384, "staged epilogue: 16 KB of LDS per wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -537,7 +731,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     aptr[q] = A + (int64_t)(n0 + r0 + lrow) * g.K + lcol * 8;
     const int64_t w = m0 + r0 + lrow;
     if (EPI == kEpiQKV) {
-      const int64_t src = g.map.src(w);  // rows without a token read X row 0 (finite, unused)
+      const int64_t src = row_src(g.map, w);  // rows without a token read X row 0 (finite, unused)
       bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
     } else {
       bptr[q] = Bb + w * kDh + lcol * 8;
@@ -598,7 +792,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();
   }
 
-  gemm_epilogue<EPI, 4>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane);
+  // the loop's last barrier: no wave reads the operand stages any more
+  gemm_epilogue_staged<EPI>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane,
+                            &smem[0][0] + wave * 16384);
 }
 
 // Smallest number of output-feature groups (a divisor of the feature tile
