@@ -62,6 +62,13 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     path = path or LIB
+    # torch wheels bundle their own HIP runtime: load it first so that the
+    # library binds to the same runtime as torch's streams and allocations
+    # (loaded the other way round, two runtimes coexist and launches fail).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(f"libvggtattn not built ({path} missing): run __graft_entry__.build()")
     L = ctypes.CDLL(path)

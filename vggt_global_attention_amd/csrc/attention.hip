@@ -395,9 +395,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
 
-  // The -m accumulator initialiser stays resident when the 8-wave tile leaves
-  // the registers for it; otherwise it is re-splatted before each QK chain.
-  constexpr bool RES = NW == 8;
+  // The -m accumulator initialiser stays resident where the registers allow
+  // it (8-wave tiles, and one query block per wave); otherwise it is
+  // re-splatted before each QK chain.
+  constexpr bool RES = NW == 8 || QB == 1;
   Rows<QB, RES> R;
   rows_init(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
 
