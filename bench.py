@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
     ap.add_argument("--only-stage", default=None, choices=["prep", "qkv", "core", "out"],
                     help="time one stage in a loop (for profilers) and print its ms")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="instead of the layer: time the fp64 oracle on whole workloads "
+                         "(tiny, s24, s500, s100; s300 on a row sample) on this host")
     ap.add_argument("--hbm", action="store_true",
                     help="instead of the layer: HBM-bound kernels (register-mode patch copy, "
                          "residual update) at 500 frames, warm and after a 512 MB cache scrub")
@@ -381,6 +384,44 @@ def cpu_baseline(w, inp, n_rows):
             "ms_per_step_extrapolated": full_s * 1e3}
 
 
+def cpu_full():
+    """Wall time of the fp64 oracle (all host threads) on whole workloads:
+    tiny and s24 in frame and global mode, s500 in frame and register mode,
+    the s100 global layer, and s300 global on 1,024 sampled query rows
+    (extrapolated linearly in the rows)."""
+    import oracle
+    import torch
+    from vggt_global_attention_amd import configs, synth
+    threads = max(1, os.cpu_count() or 1)
+    os.environ["ORACLE_THREADS"] = str(threads)
+    runs = []
+    for name, mode in (("tiny", "frame"), ("tiny", "global"), ("s24", "frame"), ("s24", "global"),
+                       ("s500", "frame"), ("s500", "register"), ("s100", "global"),
+                       ("s300", "global_rows")):
+        w = configs.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        p = oracle.OracleParams(
+            Wqkv=inp["Wqkv"].to(torch.float64).numpy(), Wo=inp["Wo"].to(torch.float64).numpy(),
+            q_gamma=inp["q_gamma"].double().numpy(), q_beta=inp["q_beta"].double().numpy(),
+            k_gamma=inp["k_gamma"].double().numpy(), k_beta=inp["k_beta"].double().numpy(),
+            H=w.H, grid_h=w.grid_h, grid_w=w.grid_w)
+        X = inp["X"].to(torch.float64).numpy()
+        print(f"[bench] oracle {name} {mode}", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        if mode == "global_rows":
+            rows = synth.sample_rows(w, 1024).numpy()
+            oracle.global_attention_rows(X, p, rows, threads=threads)
+            dt = time.perf_counter() - t0
+            runs.append({"workload": name, "mode": "global", "seconds": dt,
+                         "sample_rows": int(len(rows)),
+                         "seconds_extrapolated": dt * w.N / len(rows)})
+        else:
+            getattr(oracle, f"{mode}_attention")(X, p, threads=threads)
+            runs.append({"workload": name, "mode": mode, "seconds": time.perf_counter() - t0})
+        print(f"[bench]   {runs[-1]['seconds']:.1f} s", file=sys.stderr, flush=True)
+    return {"oracle_full": runs, "threads": threads, "host": host_info()}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -407,6 +448,9 @@ def main():
     if a.hbm:
         print(json.dumps({"hbm_kernels": hbm_kernels(a.steps), "peak_gbs": PEAK_HBM_GBS}),
               flush=True)
+        return
+    if a.cpu_full:
+        print(json.dumps(cpu_full()), flush=True)
         return
     if a.schedule:
         frames = [int(x) for x in a.schedule.split(",")]
