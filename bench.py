@@ -425,7 +425,7 @@ def cpu_full():
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
                           "requested_gpus": a.gpus}))
         sys.exit(2)
     import torch
