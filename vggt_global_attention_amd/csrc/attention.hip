@@ -45,6 +45,8 @@
 // queries per wave (spills).  With random fp16 operands this loop is
 // power-bound: the shader clock settles near 1.9 GHz, so lowering the energy
 // per FLOP (LDS bytes, non-MFMA instructions) matters as much as issue slots.
+#include <type_traits>
+
 #include "plan.h"
 
 namespace vggt {
@@ -436,24 +438,54 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 
   f32x16 S[2][QB];
   f16x8 pf[QB][4];
+  // One tile from LDS buffer BUF while the next tile moves into BUF ^ 1.  The
+  // loop is unrolled by two so that BUF is a constant and every LDS address
+  // is a lane offset plus an immediate; a scheduling barrier keeps the two
+  // halves from being interleaved (which would only add live registers).
+  auto step = [&](auto buf_c, int t) {
+    constexpr int BUF = decltype(buf_c)::value;
+    gload(t + 1);
+    if (active) {
+      tile_qk<QB, RES, false>(R, smem[BUF][0], j, h, 64, S);
+      tile_softmax(R, S, pf, t == 0);
+      tile_pv(R, smem[BUF][1], pf, j, h);
+    }
+    sstore(BUF ^ 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
   gload(0);
   sstore(0);
   __syncthreads();
   // all tiles but the last: no mask
-  for (int t = 0; t < ntiles - 1; ++t) {
-    const int buf = t & 1;
-    gload(t + 1);
-    if (active) {
-      tile_qk<QB, RES, false>(R, smem[buf][0], j, h, 64, S);
-      tile_softmax(R, S, pf, t == 0);
-      tile_pv(R, smem[buf][1], pf, j, h);
+  int t = 0;
+  if constexpr (NW == 8) {
+    for (; t + 2 < ntiles; t += 2) {
+      step(std::integral_constant<int, 0>(), t);
+      step(std::integral_constant<int, 1>(), t + 1);
     }
-    sstore(buf ^ 1);
-    __syncthreads();
+    if (t < ntiles - 1) {
+      step(std::integral_constant<int, 0>(), t);
+      ++t;
+    }
+  } else {
+    // 4-wave tiles keep the rolled loop: unrolled, the extra registers cost
+    // a wave of occupancy
+    for (; t < ntiles - 1; ++t) {
+      const int buf = t & 1;
+      gload(t + 1);
+      if (active) {
+        tile_qk<QB, RES, false>(R, smem[buf][0], j, h, 64, S);
+        tile_softmax(R, S, pf, t == 0);
+        tile_pv(R, smem[buf][1], pf, j, h);
+      }
+      sstore(buf ^ 1);
+      __syncthreads();
+    }
   }
-  // last tile: keys past the end of the set masked
+  // last tile (t = ntiles - 1): keys past the end of the set masked
   if (active) {
-    const int buf = (ntiles - 1) & 1;
+    const int buf = t & 1;
     tile_qk<QB, RES, true>(R, smem[buf][0], j, h, last_valid, S);
     tile_softmax(R, S, pf, ntiles == 1);
     tile_pv(R, smem[buf][1], pf, j, h);
