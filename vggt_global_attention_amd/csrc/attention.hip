@@ -139,15 +139,17 @@ __device__ __forceinline__ void rows_init(Rows<QB, RES>& R, const f16* qh, int64
 // S^T = K Q^T - m for one 64-key tile in LDS.  MASK: keys at or beyond
 // `valid` (the last tile of a set) start from -inf instead of -m, so their
 // probability is exactly 0.
+// `la` holds this lane's four LDS row offsets lds_swz(j, 2 * c + h) (the
+// 32-row block kb adds kb * 4096: the swizzle only uses row bits 0..3).
 template <int QB, bool RES, bool MASK>
-__device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, int j, int h,
-                                        int valid, f32x16 (&S)[2][QB]) {
+__device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, const int (&la)[4],
+                                        int h, int valid, f32x16 (&S)[2][QB]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f16x8 kf[4];
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc)
-      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + lds_swz(kb * 32 + j, dc * 2 + h));
+      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + la[dc] + kb * 4096);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 c = RES ? R.negm[RES ? qb : 0] : splat16(-R.m[qb]);
@@ -163,12 +165,7 @@ __device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, 
   }
 }
 
-template <int QB, bool RES>
-__device__ __forceinline__ void tile_qk_any(const Rows<QB, RES>& R, const char* Ks, int j, int h,
-                                            bool last, int last_valid, f32x16 (&S)[2][QB]) {
-  if (last && last_valid < 64) tile_qk<QB, RES, true>(R, Ks, j, h, last_valid, S);
-  else tile_qk<QB, RES, false>(R, Ks, j, h, 64, S);
-}
+
 
 // Softmax of one tile: on the first tile, or while a row is unsettled, take
 // the row max and move / pin the reference; then P = 2^S in fp16 and the row
@@ -232,13 +229,13 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
 
 // O^T += V^T P^T for one tile in LDS.
 template <int QB, bool RES>
-__device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs,
-                                        const f16x8 (&pf)[QB][4], int j, int h) {
+__device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs, const int (&la)[4],
+                                        const f16x8 (&pf)[QB][4]) {
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + lds_swz(db * 32 + j, c * 2 + h));
+      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + la[c] + db * 4096);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) R.O[db][qb] = mfma32x32x16(vf, pf[qb][c], R.O[db][qb]);
     }
@@ -438,6 +435,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 
   f32x16 S[2][QB];
   f16x8 pf[QB][4];
+  int la[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) la[c] = lds_swz(j, 2 * c + h);
   // One tile from LDS buffer BUF while the next tile moves into BUF ^ 1.  The
   // loop is unrolled by two so that BUF is a constant and every LDS address
   // is a lane offset plus an immediate; a scheduling barrier keeps the two
@@ -446,9 +446,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     constexpr int BUF = decltype(buf_c)::value;
     gload(t + 1);
     if (active) {
-      tile_qk<QB, RES, false>(R, smem[BUF][0], j, h, 64, S);
+      tile_qk<QB, RES, false>(R, smem[BUF][0], la, h, 64, S);
       tile_softmax(R, S, pf, t == 0);
-      tile_pv(R, smem[BUF][1], pf, j, h);
+      tile_pv(R, smem[BUF][1], la, pf);
     }
     sstore(BUF ^ 1);
     __syncthreads();
@@ -469,26 +469,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       ++t;
     }
   } else {
-    // 4-wave tiles keep the rolled loop: unrolled, the extra registers cost
-    // a wave of occupancy
+    // 4-wave tiles keep the rolled loop (unrolled, the extra registers cost
+    // a wave of occupancy); the lane offsets carry the buffer bit instead,
+    // flipped once per tile.
+    int lb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lb[c] = la[c];
     for (; t < ntiles - 1; ++t) {
-      const int buf = t & 1;
       gload(t + 1);
       if (active) {
-        tile_qk<QB, RES, false>(R, smem[buf][0], j, h, 64, S);
+        tile_qk<QB, RES, false>(R, smem[0][0], lb, h, 64, S);
         tile_softmax(R, S, pf, t == 0);
-        tile_pv(R, smem[buf][1], pf, j, h);
+        tile_pv(R, smem[0][1], lb, pf);
       }
-      sstore(buf ^ 1);
+      sstore((t & 1) ^ 1);
       __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lb[c] ^= 2 * 64 * 128;  // the other buffer
     }
   }
   // last tile (t = ntiles - 1): keys past the end of the set masked
   if (active) {
-    const int buf = t & 1;
-    tile_qk<QB, RES, true>(R, smem[buf][0], j, h, last_valid, S);
+    int lb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lb[c] = la[c] ^ ((t & 1) * 2 * 64 * 128);
+    tile_qk<QB, RES, true>(R, smem[0][0], lb, h, last_valid, S);
     tile_softmax(R, S, pf, ntiles == 1);
-    tile_pv(R, smem[buf][1], pf, j, h);
+    tile_pv(R, smem[0][1], lb, pf);
   }
   if (SGA && active) sga_columns(R, p, bc.h, qloc0, j, h);
   if (active) rows_store(R, qh, seq0, qloc0, L, j, h);
