@@ -141,11 +141,12 @@ __device__ __forceinline__ void rows_init(Rows<QB, RES>& R, const f16* qh, int64
 // probability is exactly 0.
 // `la` holds this lane's four LDS row offsets lds_swz(j, 2 * c + h) (the
 // 32-row block kb adds kb * 4096: the swizzle only uses row bits 0..3).
-template <int QB, bool RES, bool MASK>
+// KB = 1: only keys 0..31 of the tile (a short last tile).
+template <int QB, bool RES, bool MASK, int KB = 2>
 __device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, const int (&la)[4],
                                         int h, int valid, f32x16 (&S)[2][QB]) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     f16x8 kf[4];
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc)
@@ -170,7 +171,9 @@ __device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, 
 // Softmax of one tile: on the first tile, or while a row is unsettled, take
 // the row max and move / pin the reference; then P = 2^S in fp16 and the row
 // sums.  pf[qb][c] is the B operand of the PV product for keys 16c..16c+15.
-template <int QB, bool RES>
+// A short last tile passes KB = 1 (keys 0..31 only) and NC = the number of
+// 16-key groups that hold any valid key: the other probabilities are zero.
+template <int QB, bool RES, int KB = 2, int NC = 4>
 __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB],
                                              f16x8 (&pf)[QB][4], bool first) {
   if (first || R.track) {
@@ -179,7 +182,7 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
     for (int qb = 0; qb < QB; ++qb) {
       float mt = S[0][qb][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(S[kb][qb][r], S[kb][qb][r + 1]));
       mt = fmaxf(mt, __shfl_xor(mt, 32));  // row max of this tile, relative to m (m = 0 before the first)
@@ -192,7 +195,7 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
       const float dl = mn - R.m[qb];
       if (dl != 0.f) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) S[kb][qb][r] -= dl;
         // O and l are still zero before the first tile: leave them alone
@@ -212,7 +215,7 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       f16x8 v;
 #pragma unroll
       for (int r = 0; r < 8; r += 2) {
@@ -227,14 +230,14 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
     }
 }
 
-// O^T += V^T P^T for one tile in LDS.
-template <int QB, bool RES>
+// O^T += V^T P^T for one tile in LDS (the first NC groups of 16 keys).
+template <int QB, bool RES, int NC = 4>
 __device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs, const int (&la)[4],
                                         const f16x8 (&pf)[QB][4]) {
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + la[c] + db * 4096);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) R.O[db][qb] = mfma32x32x16(vf, pf[qb][c], R.O[db][qb]);
@@ -488,14 +491,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       for (int c = 0; c < 4; ++c) lb[c] ^= 2 * 64 * 128;  // the other buffer
     }
   }
-  // last tile (t = ntiles - 1): keys past the end of the set masked
+  // last tile (t = ntiles - 1): keys past the end of the set masked.  Small
+  // sets (4-wave tiles, one query block per wave: frames, register sets)
+  // often end in a short tile -- 7 of 64 keys for a 26 x 39 frame -- whose
+  // empty 32- and 16-key groups are skipped (their probabilities are exactly
+  // zero, so the result is the same bit for bit).
   if (active) {
     int lb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) lb[c] = la[c] ^ ((t & 1) * 2 * 64 * 128);
-    tile_qk<QB, RES, true>(R, smem[0][0], lb, h, last_valid, S);
-    tile_softmax(R, S, pf, ntiles == 1);
-    tile_pv(R, smem[0][1], lb, pf);
+    if (NW == 4 && QB == 1 && last_valid <= 16) {
+      tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
+      tile_softmax<QB, RES, 1, 1>(R, S, pf, ntiles == 1);
+      tile_pv<QB, RES, 1>(R, smem[0][1], lb, pf);
+    } else if (NW == 4 && QB == 1 && last_valid <= 32) {
+      tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
+      tile_softmax<QB, RES, 1, 2>(R, S, pf, ntiles == 1);
+      tile_pv<QB, RES, 2>(R, smem[0][1], lb, pf);
+    } else {
+      tile_qk<QB, RES, true>(R, smem[0][0], lb, h, last_valid, S);
+      tile_softmax(R, S, pf, ntiles == 1);
+      tile_pv(R, smem[0][1], lb, pf);
+    }
   }
   if (SGA && active) sga_columns(R, p, bc.h, qloc0, j, h);
   if (active) rows_store(R, qh, seq0, qloc0, L, j, h);
