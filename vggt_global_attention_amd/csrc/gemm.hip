@@ -21,9 +21,36 @@
 // global->LDS goes through registers, each k-step loaded two k-steps ahead.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace vggt {
+
+// Exact floor(n / d) for 0 <= n < 2^31 and 1 <= d < 2^31 by one multiply:
+// m = ceil(2^k / d) with k = 31 + l, l = ceil(log2 d).  The excess e = m d - 2^k
+// is below d, so n m / 2^k = n / d + n e / (d 2^k) with n e / (d 2^k) < 2^-l <= 1/d,
+// which never reaches the next multiple of 1/d (division by invariant integers
+// using multiplication, after Granlund and Montgomery).  m <= 2^32 and
+// n m < 2^64.
+struct FastDiv {
+  uint64_t m;
+  int k;
+  int d;
+};
+
+static FastDiv fast_div(int64_t d) {
+  if (d < 1) d = 1;
+  if (d > 0x7fffffff) d = 0x7fffffff;  // every numerator is below d then: quotient 0
+  int l = 0;
+  while (((int64_t)1 << l) < d) ++l;
+  const int k = 31 + l;
+  return FastDiv{(((uint64_t)1 << k) + (uint64_t)d - 1) / (uint64_t)d, k, (int)d};
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+  return (int)(((uint64_t)(uint32_t)n * f.m) >> f.k);
+}
 
 struct GemmArgs {
   const void* A;  // weights [Nf][K], row-major (bf16 for QKV, fp16 for OUT)
@@ -37,6 +64,7 @@ struct GemmArgs {
   int64_t dst_off;       // QKV: workspace row w is stored at row w + dst_off
   int real_only;         // QKV: rows without a token write nothing
   RowMap map;            // QKV: workspace row -> X row; OUT: workspace row -> Y row
+  FastDiv dgrp, dT, dgw; // division by map.grp_stride, T and gw
   int T, gw, off, d;
   float eps;
   const float *qg, *qb, *kg, *kb;
@@ -47,18 +75,108 @@ struct GemmArgs {
 };
 
 // RowMap::src in 32-bit arithmetic: every workspace row and token index of a
-// call is below 2^31 (checked on the host), so the 64-bit divisions of the
-// generic map (a long instruction sequence each) become 32-bit ones.
-__device__ __forceinline__ int64_t row_src(const RowMap& m, int64_t w64) {
+// call is below 2^31 (checked on the host), so the 64-bit division of the
+// generic map becomes one multiply by the precomputed FastDiv.
+__device__ __forceinline__ int64_t row_src(const GemmArgs& g, int64_t w64) {
+  const RowMap& m = g.map;
   const int v = (int)(w64 - m.base);
   if (v < 0) return -1;
-  int grp = 0, t = v;
-  if (m.grp_stride <= 0x7fffffff) {
-    const unsigned gs = (unsigned)m.grp_stride;
-    grp = (int)((unsigned)v / gs);
-    t = v - grp * (int)gs;
-  }
+  const int grp = fdiv(v, g.dgrp);
+  const int t = v - grp * g.dgrp.d;
   return (t < m.grp_valid && grp < m.ngroups) ? (int64_t)(grp * (int)m.src_stride + t) : -1;
+}
+
+// Grid position of X row `src` for the RoPE of q and k: (row, column) plus the
+// position offset for patch tokens, row -1 for the special tokens and for
+// workspace rows without a token (no rotation).
+__device__ __forceinline__ int2 rope_pos(const GemmArgs& g, int64_t src) {
+  int2 pos = make_int2(-1, 0);
+  if (src >= 0) {
+    const int s32 = (int)src;
+    const int t = s32 - fdiv(s32, g.dT) * g.T;
+    if (t >= kSpecial) {
+      const int pidx = t - kSpecial, r = fdiv(pidx, g.dgw);
+      pos = make_int2(r + g.off, pidx - r * g.gw + g.off);
+    }
+  }
+  return pos;
+}
+
+// q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
+constexpr float kQScale = 0.18033688011112042f;
+
+// LayerNorm of one (token, head) over its 64 features -- this lane's 32 in
+// a0 (features 8*(r/4) + 4*h + r%4) and a1 (the same + 32), the other 32 in
+// lane l ^ 32 -- then the per-feature affine map (gm / bt, which carry q's
+// softmax scale), 2D RoPE for patch tokens (pos.x >= 0: feature i of each
+// half pairs with i + 16, registers r and r + 8 of the lane) and fp16
+// conversion into o[fb][rq] = features fb*32 + 8*rq + 4*h .. +3.  NORM: also
+// the squared L2 norm of the fp16 vector, summed over the lane pair.
+template <bool NORM>
+__device__ __forceinline__ void ln_rope_f16(const f32x16& a0, const f32x16& a1,
+                                            const float (&gm)[2][16], const float (&bt)[2][16],
+                                            float eps, const float2* rope, int2 pos, int h,
+                                            f16x4 (&o)[2][4], float& n2) {
+  float y[2][16];
+  float s1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s1 += a0[r] + a1[r];
+  const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
+  float s2 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    y[0][r] = a0[r] - mean;
+    y[1][r] = a1[r] - mean;
+    s2 = fmaf(y[0][r], y[0][r], s2);
+    s2 = fmaf(y[1][r], y[1][r], s2);
+  }
+  const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
+  const float rstd = __builtin_amdgcn_rsqf(var + eps);
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[fb][r] = fmaf(y[fb][r] * rstd, gm[fb][r], bt[fb][r]);
+  if (pos.x >= 0) {
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      const float2* cs_row = rope + (fb == 0 ? pos.x : pos.y) * 16;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float2 cs = cs_row[8 * (r >> 2) + 4 * h + (r & 3)];
+        const float a = y[fb][r], b = y[fb][r + 8];
+        y[fb][r] = a * cs.x - b * cs.y;
+        y[fb][r + 8] = b * cs.x + a * cs.y;
+      }
+    }
+  }
+  n2 = 0.f;
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const f32x4 v = {y[fb][4 * rq], y[fb][4 * rq + 1], y[fb][4 * rq + 2], y[fb][4 * rq + 3]};
+      o[fb][rq] = __builtin_convertvector(v, f16x4);
+      if (NORM) {
+        const f16x2 lo = {o[fb][rq][0], o[fb][rq][1]}, hi = {o[fb][rq][2], o[fb][rq][3]};
+        n2 = __builtin_amdgcn_fdot2(lo, lo, n2, false);
+        n2 = __builtin_amdgcn_fdot2(hi, hi, n2, false);
+      }
+    }
+  if (NORM) n2 += __shfl_xor(n2, 32);
+}
+
+// gamma / beta of the wave's head in the lane's feature order, times the
+// output scale.
+__device__ __forceinline__ void load_affine(const float* gam, const float* bet, float scale,
+                                            int h, float (&gm)[2][16], float (&bt)[2][16]) {
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      gm[fb][r] = gam[f] * scale;
+      bt[fb][r] = bet[f] * scale;
+    }
 }
 
 enum { kEpiQKV = 0, kEpiOut = 1 };
@@ -90,88 +208,41 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
     const int blk = fq / g.d;  // 0: q, 1: k, 2: v
     const int hd = (fq - blk * g.d) / kDh;
     if (blk < 2) {
-      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
-      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
       float gm[2][16], bt[2][16];
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          gm[fb][r] = gam[f];
-          bt[fb][r] = bet[f];
-        }
+      load_affine((blk == 0 ? g.qg : g.kg) + hd * kDh, (blk == 0 ? g.qb : g.kb) + hd * kDh,
+                  blk == 0 ? kQScale : 1.f, h, gm, bt);
       f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
-      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
-      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
-      float kmx = 0.f;
+      auto block = [&](auto norm_c) {
+        constexpr bool NORM = decltype(norm_c)::value;
+        float kmx = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const int64_t w = mbase + tb * 32 + j;
-        const int64_t src = row_src(g.map, w);
-        float s1 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
-        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
-        float s2 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dv = acc[fb][tb][r] - mean;
-            s2 = fmaf(dv, dv, s2);
-          }
-        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
-        const float rstd = 1.f / sqrtf(var + g.eps);
-        float y[2][16];
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
-        if (src >= 0) {
-          const int t = (int)src % g.T;
-          if (t >= kSpecial) {
-            const int pidx = t - kSpecial;
-            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
+        for (int tb = 0; tb < TB; ++tb) {
+          const int64_t w = mbase + tb * 32 + j;
+          const int64_t src = row_src(g, w);
+          f16x4 o[2][4];
+          float n2;
+          ln_rope_f16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
+                            n2);
+          if (!g.real_only || src >= 0) {
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-              for (int r = 0; r < 8; ++r) {
-                // feature i of the half pairs with i + 16: registers r and r + 8
-                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float2 cs = g.rope[pos[fb] * 16 + i];
-                const float a = y[fb][r], b = y[fb][r + 8];
-                y[fb][r] = a * cs.x - b * cs.y;
-                y[fb][r + 8] = b * cs.x + a * cs.y;
-              }
+              for (int rq = 0; rq < 4; ++rq)
+                *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
+                    o[fb][rq];
           }
+          if (NORM && src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
         }
-        float n2 = 0.f;
-        const bool store = !g.real_only || src >= 0;
+        if (NORM) {
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            f16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
-              const float back = (float)o[r];
-              n2 = fmaf(back, back, n2);
-            }
-            if (store)
-              *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) = o;
-          }
-        n2 += __shfl_xor(n2, 32);
-        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
-      }
+          for (int sh = 1; sh < 32; sh <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, sh));
+          if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
+        }
+      };
       if (blk == 1) {
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
+        block(std::true_type());
+      } else {
+        block(std::false_type());
       }
     } else {
       const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
@@ -179,7 +250,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
-        if (g.real_only && row_src(g.map, w) < 0) continue;
+        if (g.real_only && row_src(g, w) < 0) continue;
         const int64_t x = w + g.dst_off;
         // Key position inside its aligned group of 16: key 8a + 4c + b is
         // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
@@ -201,7 +272,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int64_t w = mbase + tb * 32 + j;
-      const int64_t src = row_src(g.map, w);
+      const int64_t src = row_src(g, w);
       if (src < 0) continue;
       bf16* dst = g.y + src * g.d + fbase + 4 * h;
 #pragma unroll
@@ -246,85 +317,41 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
       return;
     }
     if (blk < 2) {
-      const float* gam = (blk == 0 ? g.qg : g.kg) + hd * kDh;
-      const float* bet = (blk == 0 ? g.qb : g.kb) + hd * kDh;
       float gm[2][16], bt[2][16];
+      load_affine((blk == 0 ? g.qg : g.kg) + hd * kDh, (blk == 0 ? g.qb : g.kb) + hd * kDh,
+                  blk == 0 ? kQScale : 1.f, h, gm, bt);
+      // keys also record the largest norm of the stored vectors (the
+      // attention kernel's logit bound); queries skip it
+      auto block = [&](auto norm_c) {
+        constexpr bool NORM = decltype(norm_c)::value;
+        float kmx = 0.f;
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tl = tb * 32 + j;
+          const int64_t src = row_src(g, mbase + tl);
+          f16x4 o[2][4];
+          float n2;
+          ln_rope_f16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
+                            n2);
+          // features fb*32 + 8*rq + 4*h .. +3: 16-byte chunk fb*4 + rq, half h
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int f = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          gm[fb][r] = gam[f];
-          bt[fb][r] = bet[f];
+          for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+              *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
+                  o[fb][rq];
+          if (NORM && src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
         }
-      // q is pre-multiplied by log2(e)/sqrt(64): the attention kernel uses exp2.
-      const float oscale = blk == 0 ? 0.18033688011112042f : 1.f;
-      float kmx = 0.f;
+        if (NORM) {
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const int tl = tb * 32 + j;
-        const int64_t src = row_src(g.map, mbase + tl);
-        float s1 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s1 += acc[fb][tb][r];
-        const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
-        float s2 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dv = acc[fb][tb][r] - mean;
-            s2 = fmaf(dv, dv, s2);
-          }
-        const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
-        const float rstd = 1.f / sqrtf(var + g.eps);
-        float y[2][16];
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            y[fb][r] = fmaf((acc[fb][tb][r] - mean) * rstd, gm[fb][r], bt[fb][r]);
-        if (src >= 0) {
-          const int t = (int)src % g.T;
-          if (t >= kSpecial) {
-            const int pidx = t - kSpecial;
-            const int pos[2] = {pidx / g.gw + g.off, pidx % g.gw + g.off};
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-              for (int r = 0; r < 8; ++r) {
-                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float2 cs = g.rope[pos[fb] * 16 + i];
-                const float a = y[fb][r], b = y[fb][r + 8];
-                y[fb][r] = a * cs.x - b * cs.y;
-                y[fb][r + 8] = b * cs.x + a * cs.y;
-              }
-          }
+          for (int sh = 1; sh < 32; sh <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, sh));
+          if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
         }
-        float n2 = 0.f;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            f16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              o[r] = (f16)(y[fb][4 * rq + r] * oscale);
-              const float back = (float)o[r];
-              n2 = fmaf(back, back, n2);
-            }
-            // features fb*32 + 8*rq + 4*h .. +3: 16-byte chunk fb*4 + rq, half h
-            *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) = o;
-          }
-        n2 += __shfl_xor(n2, 32);
-        if (src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
-      }
+      };
       if (blk == 1) {
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-        if (lane == 0 && kmx > 0.f) atomic_max_nonneg(&g.sc->kmax[hd], kmx);
+        block(std::true_type());
+      } else {
+        block(std::false_type());
       }
       lds_wave_sync();
       f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
@@ -333,24 +360,29 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
         const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * 128 + ((c ^ (tl & 7)) << 4));
         const int64_t w = mbase + tl;
-        if (!g.real_only || row_src(g.map, w) >= 0)
+        if (!g.real_only || row_src(g, w) >= 0)
           *reinterpret_cast<u32x4*>(dst + (w + g.dst_off) * kDh + c * 8) = v;
       }
     } else {
-      const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
+      // 2^kv exactly: scaling by it and rounding to fp16 rounds once, as ldexp would
+      const float vs = __builtin_amdgcn_ldexpf(1.f, range_exponent(g.sc->xnorm * g.sc->wvnorm));
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int tl = tb * 32 + j;
         // slot of token tl inside its aligned group of 16 (bits 2 and 3 swapped)
         const int slot = (tl & ~15) | (((tl >> 2) & 1) << 3) | (((tl >> 3) & 1) << 2) | (tl & 3);
+        // feature e = fb*32 + 8*(r/4) + 4*h + r%4 has bit 2 = h, so the
+        // chunk swizzle is the lane's own: one base address per lane
+        char* base = lds + 4 * h * 256 + (((slot >> 3) ^ (h << 2)) << 4) + (slot & 7) * 2;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const int chunk = (slot >> 3) ^ (((e >> 2) & 1) << 2);
-            *reinterpret_cast<f16*>(lds + e * 256 + (chunk << 4) + (slot & 7) * 2) =
-                (f16)ldexpf(acc[fb][tb][r], kv);
+          for (int r = 0; r < 16; r += 2) {
+            const f32x2 v = {acc[fb][tb][r] * vs, acc[fb][tb][r + 1] * vs};
+            const f16x2 o = __builtin_convertvector(v, f16x2);
+            const int e0 = fb * 32 + 8 * (r >> 2) + (r & 3);  // feature minus 4*h
+            *reinterpret_cast<f16*>(base + e0 * 256) = o[0];
+            *reinterpret_cast<f16*>(base + (e0 + 1) * 256) = o[1];
           }
       }
       lds_wave_sync();
@@ -384,7 +416,7 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
       const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
-      const int64_t src = row_src(g.map, mbase + tl);
+      const int64_t src = row_src(g, mbase + tl);
       if (src < 0) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * 128 + ((c ^ (tl & 7)) << 4));
       *reinterpret_cast<u32x4*>(g.y + src * g.d + fbase + c * 8) = v;
@@ -444,7 +476,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     soff[i] = swz(row, col);
     aptr[i] = A + (int64_t)row * g.K + col * 8;
     if (EPI == kEpiQKV) {
-      const int64_t src = row_src(g.map, m0 + row);
+      const int64_t src = row_src(g, m0 + row);
       bval[i] = src >= 0;
       bptr[i] = Bbase + (bval[i] ? src : 0) * g.K + col * 8;
     } else {
@@ -596,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
     if (EPI == kEpiQKV) {
       // rows without a token read X row 0: finite values whose outputs are
       // masked keys or never read
-      const int64_t src = row_src(g.map, w);
+      const int64_t src = row_src(g, w);
       bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
     } else {
       bptr[q] = Bb + w * kDh + lcol * 8;
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     aptr[q] = A + (int64_t)(n0 + r0 + lrow) * g.K + lcol * 8;
     const int64_t w = m0 + r0 + lrow;
     if (EPI == kEpiQKV) {
-      const int64_t src = row_src(g.map, w);  // rows without a token read X row 0 (finite, unused)
+      const int64_t src = row_src(g, w);  // rows without a token read X row 0 (finite, unused)
       bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
     } else {
       bptr[q] = Bb + w * kDh + lcol * 8;
@@ -826,6 +858,14 @@ static int gemm_kind(const Plan& p, int nf) {
   return kind;
 }
 
+// The epilogues divide by the map's group stride, T and gw: set their
+// multipliers once per launch.
+static void set_divisors(GemmArgs& g) {
+  g.dgrp = fast_div(g.map.grp_stride);
+  g.dT = fast_div(g.T);
+  g.dgw = fast_div(g.gw);
+}
+
 static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   GemmArgs g{};
   g.rows = p.rows;
@@ -848,6 +888,7 @@ static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   g.m_first = 0;
   g.q_lo = p.q0;
   g.q_hi = p.window ? p.L : p.rows;
+  set_divisors(g);
   return g;
 }
 
@@ -897,6 +938,7 @@ hipError_t launch_desc_kv(char* cache, const DescLayout& L, int H, int d, float 
   g.map = RowMap{tiles * kWBM, 0, (int32_t)m, 1, 0};
   g.T = 1;
   g.gw = 1;
+  set_divisors(g);
   g.off = 0;
   g.d = d;
   g.eps = eps;
@@ -943,6 +985,7 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   const int bn = kind == 2 ? kWBN : kGemmBN;
   g.fgroups = feature_groups(g.Nf, g.K, 2, bn);
   g.map = p.out_map;
+  set_divisors(g);
   // token tiles covering the output rows: all rows, or the query window
   const int64_t bm = kind == 2 ? kWBM : kind == 1 ? kDmaBM : kGemmBM;
   const int64_t lo = p.window ? p.q0 / bm * bm : 0;
