@@ -32,7 +32,10 @@ def rows_call(w, d, begin, count):
 
 
 @pytest.mark.parametrize("name", ["tiny", "s24"])
-def test_rows_bitwise_equal_global(name):
+def test_rows_bitwise_equal_global(name, monkeypatch):
+    # with the split attention tail off: a window splits other workgroups
+    # than the full call, which changes the rounding of those rows
+    monkeypatch.setenv("VGGT_ATTN_SPLIT", "1")
     w = W[name]
     d = to_dev(synth.make_inputs(w))
     full = run("global", w, d).reshape(-1, w.d)
@@ -46,8 +49,10 @@ def test_rows_bitwise_equal_global(name):
         assert torch.equal(y, full[begin:begin + count]), (begin, count)
 
 
-def test_rows_s100_share_oracle_and_bitwise():
-    """The 1/8 share of the 100-frame layer (12,888 queries over 103,100 keys)."""
+def test_rows_s100_share_oracle_and_bitwise(monkeypatch):
+    """The 1/8 share of the 100-frame layer (12,888 queries over 103,100 keys):
+    as planned (its partly filled last round split into key ranges) against
+    the oracle, and unsplit bit for bit against the unsplit full call."""
     w = W["s100"]
     inp = synth.make_inputs(w)
     d = to_dev(inp)
@@ -55,8 +60,10 @@ def test_rows_s100_share_oracle_and_bitwise():
     begin = 3 * share
     log(f"[case] s100 rows [{begin}, {begin + share})")
     y = rows_call(w, d, begin, share)
+    monkeypatch.setenv("VGGT_ATTN_SPLIT", "1")
+    y1 = rows_call(w, d, begin, share)
     full = run("global", w, d).reshape(-1, w.d)
-    assert torch.equal(y, full[begin:begin + share])
+    assert torch.equal(y1, full[begin:begin + share])
     rows = np.sort(np.random.default_rng(7).choice(share, 96, replace=False)) + begin
     ref = oracle.global_attention_rows(f64(inp["X"]), oracle_params(w, inp), rows)
     assert_parity(np64(y)[rows - begin], ref, "s100/rows-share")

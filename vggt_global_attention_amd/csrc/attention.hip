@@ -72,6 +72,11 @@ struct AttnArgs {
   const f16* vt_all;   // [H][64][rows]
   const float* sums;   // [H][128]
   int nD, T, gw, sub_h, sub_w;
+  // split tail: workgroups [0, w0) run whole; block w0 + u is key range
+  // u % split_p of workgroup w0 + u / split_p, whose partial results go to
+  // part (unit u: [BQ][64] fp32 O, then [BQ] float2 (m, l) after all units)
+  int w0, split_p;
+  float* part;
 };
 
 // LDS tiles are 64 rows x 128 bytes.  The MFMA operand reads take one
@@ -357,16 +362,50 @@ __device__ __forceinline__ void rows_store(const Rows<QB, RES>& R, f16* qh, int6
   }
 }
 
+// Unnormalised state of a key range (split tail): O in fp32, the reference
+// m and the row sum l, for the merge kernel.
+template <int QB, bool RES>
+__device__ __forceinline__ void rows_store_partial(const Rows<QB, RES>& R, float* po, float2* pml,
+                                                   int lrow0, int j, int h) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = R.l[qb] + __shfl_xor(R.l[qb], 32);
+    const int lr = lrow0 + qb * 32 + j;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 o = {R.O[db][qb][4 * rq], R.O[db][qb][4 * rq + 1], R.O[db][qb][4 * rq + 2],
+                         R.O[db][qb][4 * rq + 3]};
+        *reinterpret_cast<f32x4*>(po + lr * kDh + db * 32 + 8 * rq + 4 * h) = o;
+      }
+    if (h == 0) pml[lr] = make_float2(R.m[qb], lt);
+  }
+}
+
+// Workgroup coordinates: (query tile, head, set) of the logical workgroup,
+// and for a unit of the split tail its key range ks (else -1).  Both parts of
+// the grid are remapped so that each XCD walks a contiguous range.
 struct BlockCoord {
-  int h, s, qt;
+  int h, s, qt, ks, unit;
 };
-__device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ BlockCoord coord_of(const AttnArgs& p, int logical) {
   BlockCoord c;
   c.qt = logical % p.qtiles;
   const int t2 = logical / p.qtiles;
   c.h = t2 % p.H;
   c.s = t2 / p.H;
+  c.ks = -1;
+  c.unit = -1;
+  return c;
+}
+__device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
+  const int b = blockIdx.x;
+  if (b < p.w0) return coord_of(p, xcd_remap(b, p.w0));
+  const int u = xcd_remap(b - p.w0, gridDim.x - p.w0);
+  BlockCoord c = coord_of(p, p.w0 + u / p.split_p);
+  c.ks = u % p.split_p;
+  c.unit = u;
   return c;
 }
 
@@ -387,7 +426,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
 
-  const BlockCoord bc = block_coord(p);
+  // only the 8-wave global-type grid has a split tail
+  constexpr bool kSplit = NW == 8 && !SGA;
+  const BlockCoord bc = kSplit ? block_coord(p) : coord_of(p, xcd_remap(blockIdx.x, gridDim.x));
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
   const int L = p.L;
@@ -404,8 +445,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   Rows<QB, RES> R;
   rows_init(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
 
+  // key tiles [t0, t1): all of them, or one key range of a split workgroup
+  // (only the range that ends the set has a masked last tile)
   const int ntiles = (p.Lk + 63) / 64;
-  const int last_valid = p.Lk - 64 * (ntiles - 1);
+  int t0 = 0, t1 = ntiles;
+  if (bc.ks >= 0) {
+    t0 = bc.ks * ntiles / p.split_p;
+    t1 = (bc.ks + 1) * ntiles / p.split_p;
+  }
+  const int last_valid = t1 == ntiles ? p.Lk - 64 * (ntiles - 1) : 64;
 
   // 1024 16-byte chunks per K+V tile, CH per thread: chunk c < 512 is K (row
   // c>>3, col c&7), chunk c >= 512 is V^T (feature row, col).
@@ -450,24 +498,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     gload(t + 1);
     if (active) {
       tile_qk<QB, RES, false>(R, smem[BUF][0], la, h, 64, S);
-      tile_softmax(R, S, pf, t == 0);
+      tile_softmax(R, S, pf, t == t0);
       tile_pv(R, smem[BUF][1], la, pf);
     }
     sstore(BUF ^ 1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  gload(0);
+  gload(t0);
   sstore(0);
   __syncthreads();
-  // all tiles but the last: no mask
-  int t = 0;
+  // all tiles of the range but its last: no mask; tile t sits in LDS buffer
+  // (t - t0) & 1
+  int t = t0;
   if constexpr (NW == 8) {
-    for (; t + 2 < ntiles; t += 2) {
+    for (; t + 2 < t1; t += 2) {
       step(std::integral_constant<int, 0>(), t);
       step(std::integral_constant<int, 1>(), t + 1);
     }
-    if (t < ntiles - 1) {
+    if (t < t1 - 1) {
       step(std::integral_constant<int, 0>(), t);
       ++t;
     }
@@ -478,20 +527,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     int lb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) lb[c] = la[c];
-    for (; t < ntiles - 1; ++t) {
+    for (; t < t1 - 1; ++t) {
       gload(t + 1);
       if (active) {
         tile_qk<QB, RES, false>(R, smem[0][0], lb, h, 64, S);
-        tile_softmax(R, S, pf, t == 0);
+        tile_softmax(R, S, pf, t == t0);
         tile_pv(R, smem[0][1], lb, pf);
       }
-      sstore((t & 1) ^ 1);
+      sstore(((t - t0) & 1) ^ 1);
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < 4; ++c) lb[c] ^= 2 * 64 * 128;  // the other buffer
     }
   }
-  // last tile (t = ntiles - 1): keys past the end of the set masked.  Small
+  // last tile of the range (t = t1 - 1): keys past the end of the set masked.  Small
   // sets (4-wave tiles, one query block per wave: frames, register sets)
   // often end in a short tile -- 7 of 64 keys for a 26 x 39 frame -- whose
   // empty 32- and 16-key groups are skipped (their probabilities are exactly
@@ -499,23 +548,117 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   if (active) {
     int lb[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) lb[c] = la[c] ^ ((t & 1) * 2 * 64 * 128);
+    for (int c = 0; c < 4; ++c) lb[c] = la[c] ^ (((t - t0) & 1) * 2 * 64 * 128);
+    const bool first = t1 - t0 == 1;
     if (NW == 4 && QB == 1 && last_valid <= 16) {
       tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax<QB, RES, 1, 1>(R, S, pf, ntiles == 1);
+      tile_softmax<QB, RES, 1, 1>(R, S, pf, first);
       tile_pv<QB, RES, 1>(R, smem[0][1], lb, pf);
     } else if (NW == 4 && QB == 1 && last_valid <= 32) {
       tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax<QB, RES, 1, 2>(R, S, pf, ntiles == 1);
+      tile_softmax<QB, RES, 1, 2>(R, S, pf, first);
       tile_pv<QB, RES, 2>(R, smem[0][1], lb, pf);
     } else {
       tile_qk<QB, RES, true>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax(R, S, pf, ntiles == 1);
+      tile_softmax(R, S, pf, first);
       tile_pv(R, smem[0][1], lb, pf);
     }
   }
   if (SGA && active) sga_columns(R, p, bc.h, qloc0, j, h);
-  if (active) rows_store(R, qh, seq0, qloc0, L, j, h);
+  if (kSplit && bc.unit >= 0) {
+    // a key range of a split workgroup: unnormalised state for the merge
+    float* po = p.part + (int64_t)bc.unit * BQ * kDh;
+    float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)(gridDim.x - p.w0) * BQ * kDh) +
+                  (int64_t)bc.unit * BQ;
+    if (active) rows_store_partial(R, po, pml, wave * QB * 32, j, h);
+  } else if (active) {
+    rows_store(R, qh, seq0, qloc0, L, j, h);
+  }
+}
+
+// Merge of a split tail: for each query row of a split workgroup, the
+// split_p key-range states (m_i, l_i, O_i) combine as one softmax over all
+// keys, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i,
+// stored in fp16 in place of the row's q like an unsplit workgroup.  16
+// threads per row, 4 features each.
+template <int BQ>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int nsplit_wg) {
+  const int per_wg = BQ / 16;
+  const int wi = blockIdx.x / per_wg;
+  const int lr = (blockIdx.x - wi * per_wg) * 16 + (threadIdx.x >> 4);
+  const int f = (threadIdx.x & 15) * 4;
+  const BlockCoord c = coord_of(p, p.w0 + wi);
+  const int row = p.q0 + c.qt * BQ + lr;
+  if (wi >= nsplit_wg || row >= p.L) return;
+  const int nunits = nsplit_wg * p.split_p;
+  const float2* ml = reinterpret_cast<const float2*>(p.part + (int64_t)nunits * BQ * kDh);
+  const int u0 = wi * p.split_p;
+  float M = -INFINITY;
+  for (int i = 0; i < p.split_p; ++i) M = fmaxf(M, ml[(int64_t)(u0 + i) * BQ + lr].x);
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < p.split_p; ++i) {
+    const float2 e = ml[(int64_t)(u0 + i) * BQ + lr];
+    const float w = __builtin_amdgcn_exp2f(e.x - M);
+    l = fmaf(w, e.y, l);
+    const f32x4 oi = *reinterpret_cast<const f32x4*>(p.part + ((int64_t)(u0 + i) * BQ + lr) * kDh + f);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = fmaf(w, oi[k], o[k]);
+  }
+  const float inv = 1.f / l;
+  f16x4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = (f16)(o[k] * inv);
+  f16* qh = p.q + (int64_t)c.h * p.rows * kDh;
+  *reinterpret_cast<f16x4*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
+}
+
+// Compute units of the current device (one 8-wave attention workgroup fits a
+// CU at a time), cached per device.
+static int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Split tail: with W workgroups on C CUs the last round holds r = W mod C of
+// them and leaves the other CUs idle.  Running each of those r as P key
+// ranges (P units of 1/P the work) shortens the tail from one workgroup time
+// to ceil(r P / C) / P.  P is the smallest that gets within 2% of the best,
+// with at least kSplitMinTiles key tiles per range and r P units within the
+// buffer.  VGGT_ATTN_SPLIT = P forces the key ranges per split workgroup
+// (1: no split; a tuning / testing switch).  Returns P (1: no split).
+static int choose_split(const Plan& p, int64_t W, int ntiles, int64_t* w0) {
+  *w0 = W;
+  if (p.split_cap <= 0) return 1;
+  const int64_t C = device_cus();
+  const int64_t r = W % C;
+  if (r == 0) return 1;
+  auto allowed = [&](int P) { return r * P <= p.split_cap && ntiles / P >= kSplitMinTiles; };
+  int best = 1;
+  double best_t = 1.0;
+  for (int P = 2; P <= kSplitMaxWays && allowed(P); ++P) {
+    const double t = (double)((r * P + C - 1) / C) / P;
+    if (t < best_t - 0.02) {
+      best_t = t;
+      best = P;
+    }
+  }
+  if (const char* e = getenv("VGGT_ATTN_SPLIT")) {
+    int P = atoi(e);
+    while (P > 1 && !allowed(P)) --P;
+    if (P >= 1) best = P;
+  }
+  if (best > 1) *w0 = W - r;
+  return best;
 }
 
 template <int QB, int NW, bool SGA>
@@ -547,7 +690,18 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
     g.sub_w = p.sub_w;
   }
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
-  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, g);
+  int64_t w0 = blocks;
+  const int P = (NW == 8 && !SGA) ? choose_split(p, blocks, (p.Lk + 63) / 64, &w0) : 1;
+  g.w0 = (int)w0;
+  g.split_p = P;
+  g.part = reinterpret_cast<float*>(a.ws + p.off_split);
+  const int64_t grid = w0 + (blocks - w0) * P;
+  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)grid), dim3(NW * 64), 0, st, g);
+  if (P > 1) {
+    const int nsplit = (int)(blocks - w0);
+    hipLaunchKernelGGL(attn_merge_kernel<BQ>, dim3((unsigned)(nsplit * (BQ / 16))), dim3(256), 0,
+                       st, g, nsplit);
+  }
   return hipGetLastError();
 }
 
