@@ -1,14 +1,16 @@
 """GPU checks of the split attention tail.
 
-The last round of 8-wave workgroups on the GPU is only partly filled. The
-library runs each of those workgroups as P key ranges. A merge kernel then
-combines the ranges' softmax states.
+The last round of workgroups of a single-set grid (global sets, query
+windows, register sets) is only partly filled. The library runs each of
+those workgroups as P key ranges. A merge kernel then combines the ranges'
+softmax states.
 
 What is checked:
 - split results match the fp64 oracle at the block bar;
 - they stay within a few fp16 roundings of O of the unsplit kernel
   (VGGT_ATTN_SPLIT = 1);
-- splitting every workgroup, forced splits, and query windows are exercised.
+- splitting every workgroup, forced splits, query windows and the 4-wave
+  register grid are exercised.
 """
 
 from __future__ import annotations
@@ -118,3 +120,20 @@ def test_split_query_window(monkeypatch):
     rows = np.sort(np.random.default_rng(3).choice(3000, 64, replace=False)) + 1000
     ref = oracle.global_attention_rows(f64(inp["X"]), oracle_params(w, inp), rows)
     assert_parity(np64(y)[rows - 1000], ref, "s24 rows window, split")
+
+
+def test_split_register_s500(monkeypatch):
+    """The 8,500-row register set of 500 frames on 4-wave workgroups (1,072 of
+    them): split as planned against the unsplit kernel and the oracle."""
+    w = configs.WORKLOADS["s500"]
+    inp = synth.make_inputs(w)
+    d = to_dev(inp)
+    y = run("register", w, d)
+    y1 = with_split(monkeypatch, 1, lambda: run("register", w, d))
+    spec = np.s_[:, :17]
+    m = metrics(np64(y[spec]), np64(y1[spec]))
+    assert m["relL1"] <= CLOSE_RELL1, m
+    assert torch.equal(y[:, 17:], y1[:, 17:])
+    frames = np.arange(0, w.S, 25)
+    ref = oracle.register_attention(f64(inp["X"]), oracle_params(w, inp), threads=8)
+    assert_parity(np64(y[frames, :17]), ref[frames, :17], "s500 register, split")

@@ -165,18 +165,20 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->off_part = off;  // [H][ceil(N/1024)][128] fp32 partial sums
     off += round_up((int64_t)s->H * ((N + 1023) / 1024) * 128 * sizeof(float), 256);
   }
-  // Partial results of a split attention tail (global sets and query
-  // windows; not the descriptor mode, whose key count is not known when its
-  // workspace is sized).  Sized from the shape alone, not the device.
+  // Partial results of a split attention tail (global sets, query windows
+  // and register sets; not frames, whose sets are short, nor the descriptor
+  // mode, whose key count is not known when its workspace is sized).  Sized
+  // from the shape alone, not the device.
   p->split_cap = 0;
   p->off_split = off;
-  if (p->attn_waves == 8 && mode == VGGT_ATTN_MODE_GLOBAL) {
-    const int64_t bq = 8 * p->attn_qb * 32;
+  if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER) {
+    const int64_t bq = (int64_t)p->attn_waves * p->attn_qb * 32;
     const int64_t W = (p->L - p->q0 + bq - 1) / bq * s->H * p->nseq;
     int64_t ways = (p->Lk + kAttnBK - 1) / kAttnBK / kSplitMinTiles;
     if (ways > kSplitMaxWays) ways = kSplitMaxWays;
     if (ways >= 2) {
-      p->split_cap = (int)(W * ways < kSplitMaxUnits ? W * ways : kSplitMaxUnits);
+      const int64_t cap = kSplitMaxRows / bq;
+      p->split_cap = (int)(W * ways < cap ? W * ways : cap);
       off += round_up((int64_t)p->split_cap * bq * (kDh + 2) * sizeof(float), 256);
     }
   }

@@ -426,8 +426,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
 
-  // only the 8-wave global-type grid has a split tail
-  constexpr bool kSplit = NW == 8 && !SGA;
+  // single-set grids (global, query windows, register sets) may have a split
+  // tail; the subsampled grid never does
+  constexpr bool kSplit = !SGA;
   const BlockCoord bc = kSplit ? block_coord(p) : coord_of(p, xcd_remap(blockIdx.x, gridDim.x));
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
@@ -613,8 +614,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int nsplit_
   *reinterpret_cast<f16x4*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
 }
 
-// Compute units of the current device (one 8-wave attention workgroup fits a
-// CU at a time), cached per device.
+// Compute units of the current device, cached per device.
 static int device_cus() {
   static int cache[64];
   int dev = 0;
@@ -629,17 +629,18 @@ static int device_cus() {
   return cache[dev];
 }
 
-// Split tail: with W workgroups on C CUs the last round holds r = W mod C of
-// them and leaves the other CUs idle.  Running each of those r as P key
+// Split tail: with W workgroups on C slots (CUs times the workgroups of the
+// kernel that fit a CU) the last round holds r = W mod C of them and leaves
+// the other slots idle.  Running each of those r as P key
 // ranges (P units of 1/P the work) shortens the tail from one workgroup time
 // to ceil(r P / C) / P.  P is the smallest that gets within 2% of the best,
 // with at least kSplitMinTiles key tiles per range and r P units within the
 // buffer.  VGGT_ATTN_SPLIT = P forces the key ranges per split workgroup
 // (1: no split; a tuning / testing switch).  Returns P (1: no split).
-static int choose_split(const Plan& p, int64_t W, int ntiles, int64_t* w0) {
+static int choose_split(const Plan& p, int64_t W, int ntiles, int per_cu, int64_t* w0) {
   *w0 = W;
   if (p.split_cap <= 0) return 1;
-  const int64_t C = device_cus();
+  const int64_t C = (int64_t)device_cus() * (per_cu > 0 ? per_cu : 1);
   const int64_t r = W % C;
   if (r == 0) return 1;
   auto allowed = [&](int P) { return r * P <= p.split_cap && ntiles / P >= kSplitMinTiles; };
@@ -691,7 +692,16 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   }
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
   int64_t w0 = blocks;
-  const int P = (NW == 8 && !SGA) ? choose_split(p, blocks, (p.Lk + 63) / 64, &w0) : 1;
+  int P = 1;
+  if (!SGA && p.split_cap > 0) {
+    // workgroups of this kernel resident per CU (register / LDS bound)
+    static int per_cu = 0;
+    if (per_cu == 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA>, NW * 64,
+                                                     0) != hipSuccess)
+      per_cu = -1;
+    P = choose_split(p, blocks, (p.Lk + 63) / 64, per_cu, &w0);
+  }
   g.w0 = (int)w0;
   g.split_p = P;
   g.part = reinterpret_cast<float*>(a.ws + p.off_split);

@@ -17,7 +17,7 @@ constexpr int kGemmBK = 64;
 constexpr int kAttnBK = 64;         // keys per attention tile
 constexpr int kRowAlign = 2048;     // workspace rows are padded to this (8 XCDs x 256-row tiles)
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
-constexpr int kSplitMaxUnits = 512; // key-range units of a split attention tail (bounds its buffer)
+constexpr int kSplitMaxRows = 1 << 18;  // query rows x key ranges of a split attention tail (its buffer)
 constexpr int kSplitMaxWays = 32;   // key ranges per split workgroup at most
 constexpr int kSplitMinTiles = 24;  // key tiles per range at least
 
@@ -80,8 +80,8 @@ struct Plan {
   int64_t kv_rows;     // rows per head of the key / value buffers
   int64_t kv_seq_stride;
   int nD;              // subsampled mode: discarded tokens (mean-filled columns)
-  // Split tail of the 8-wave attention grid (global sets and query
-  // windows): room for split_cap key-range units of partial results
+  // Split tail of a single-set attention grid (global sets, query windows,
+  // register sets): room for split_cap key-range units of partial results
   // (unnormalised O, reference, row sum); launch_core decides from the
   // device's CU count whether the last, partly filled round of workgroups
   // runs as key ranges that a merge kernel combines.
