@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from vggt_global_attention_amd import configs, synth
+from vggt_global_attention_amd import api, configs, synth
 from vggt_global_attention_amd import binding as B
 from helpers import assert_parity, f64, oracle_params
 from gpu_common import log, np64, require_gpu, run, to_dev
@@ -266,3 +266,22 @@ def test_large_magnitudes_range_guard():
     y = run("global", w, to_dev(big))
     ref = oracle.global_attention(f64(big["X"]), oracle_params(w, big))
     assert_parity(np64(y), ref, "tiny/large")
+
+
+def test_register_patch_copy_ordered_on_caller_stream():
+    """Register mode with Y != X, called on a non-default stream: work queued
+    on that stream right after the call sees every row of Y, the copied patch
+    rows included."""
+    w = W["s500"]
+    d = to_dev(synth.make_inputs(w))
+    blk = api.Block("register", d["X"], w.H, w.grid_h, w.grid_w)
+    args = [d[k] for k in ("X", "Wqkv", "Wo", "q_gamma", "q_beta", "k_gamma", "k_beta")]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            Y = torch.full_like(d["X"], float("nan"))
+            blk(*args, Y=Y, stream=s)
+            same = torch.equal(Y[:, 17:], d["X"][:, 17:])  # queued on s, right behind the call
+            assert same
+    torch.cuda.synchronize()
