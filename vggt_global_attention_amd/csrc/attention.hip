@@ -72,10 +72,12 @@ struct AttnArgs {
   const f16* vt_all;   // [H][64][rows]
   const float* sums;   // [H][128]
   int nD, T, gw, sub_h, sub_w;
-  // split tail: workgroups [0, w0) run whole; block w0 + u is key range
-  // u % split_p of workgroup w0 + u / split_p, whose partial results go to
-  // part (unit u: [BQ][64] fp32 O, then [BQ] float2 (m, l) after all units)
-  int w0, split_p;
+  // split tail (split_p > 1): each XCD runs its contiguous range of
+  // workgroups whole up to a multiple of its slots (xcd_slots) and the rest
+  // as split_p key ranges each; the partial results of XCD x's tail unit v
+  // go to unit x * umax + v of part ([units][BQ][64] fp32 O, then
+  // [units][BQ] float2 (m, l), units = 8 * umax)
+  int split_p, xcd_slots, umax;
   float* part;
 };
 
@@ -384,10 +386,11 @@ __device__ __forceinline__ void rows_store_partial(const Rows<QB, RES>& R, float
 }
 
 // Workgroup coordinates: (query tile, head, set) of the logical workgroup,
-// and for a unit of the split tail its key range ks (else -1).  Both parts of
-// the grid are remapped so that each XCD walks a contiguous range.
+// and for a unit of the split tail its key range ks (else -1); `skip` marks
+// the padding blocks of a split grid.
 struct BlockCoord {
   int h, s, qt, ks, unit;
+  bool skip;
 };
 __device__ __forceinline__ BlockCoord coord_of(const AttnArgs& p, int logical) {
   BlockCoord c;
@@ -397,15 +400,44 @@ __device__ __forceinline__ BlockCoord coord_of(const AttnArgs& p, int logical) {
   c.s = t2 / p.H;
   c.ks = -1;
   c.unit = -1;
+  c.skip = false;
   return c;
 }
+
+// The logical workgroups of XCD x: the contiguous range xcd_remap gives it.
+struct XcdRange {
+  int base, n, whole, tail;  // first logical id, count, whole ones, split ones
+};
+__device__ __forceinline__ XcdRange xcd_range(const AttnArgs& p, int x) {
+  const int W = p.qtiles * p.H * p.nseq;
+  const int per = W >> 3, rem = W & (kXcds - 1);
+  XcdRange r;
+  r.n = per + (x < rem ? 1 : 0);
+  r.base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  r.tail = r.n % p.xcd_slots;
+  r.whole = r.n - r.tail;
+  return r;
+}
+
+// Blocks go to the XCDs round-robin (block b to XCD b mod 8, in order of its
+// slot b / 8).  Without a split each XCD walks its range in order; with one,
+// slots [0, whole) of XCD x are its whole workgroups and the next tail *
+// split_p slots their key ranges, on the XCD whose L2 already holds the
+// range's keys and values.
 __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
   const int b = blockIdx.x;
-  if (b < p.w0) return coord_of(p, xcd_remap(b, p.w0));
-  const int u = xcd_remap(b - p.w0, gridDim.x - p.w0);
-  BlockCoord c = coord_of(p, p.w0 + u / p.split_p);
-  c.ks = u % p.split_p;
-  c.unit = u;
+  if (p.split_p <= 1) return coord_of(p, xcd_remap(b, gridDim.x));
+  const int x = b & (kXcds - 1), slot = b >> 3;
+  const XcdRange r = xcd_range(p, x);
+  if (slot < r.whole) return coord_of(p, r.base + slot);
+  const int v = slot - r.whole;
+  BlockCoord c = coord_of(p, r.base + r.whole + (v < r.tail * p.split_p ? v / p.split_p : 0));
+  if (v >= r.tail * p.split_p) {
+    c.skip = true;  // padding: this XCD has fewer slots than the longest
+    return c;
+  }
+  c.ks = v % p.split_p;
+  c.unit = x * p.umax + v;
   return c;
 }
 
@@ -430,6 +462,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   // tail; the subsampled grid never does
   constexpr bool kSplit = !SGA;
   const BlockCoord bc = kSplit ? block_coord(p) : coord_of(p, xcd_remap(blockIdx.x, gridDim.x));
+  if (kSplit && bc.skip) return;  // whole block: before any barrier
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
   const int L = p.L;
@@ -569,7 +602,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   if (kSplit && bc.unit >= 0) {
     // a key range of a split workgroup: unnormalised state for the merge
     float* po = p.part + (int64_t)bc.unit * BQ * kDh;
-    float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)(gridDim.x - p.w0) * BQ * kDh) +
+    float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)kXcds * p.umax * BQ * kDh) +
                   (int64_t)bc.unit * BQ;
     if (active) rows_store_partial(R, po, pml, wave * QB * 32, j, h);
   } else if (active) {
@@ -580,36 +613,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 // Merge of a split tail: for each query row of a split workgroup, the
 // split_p key-range states (m_i, l_i, O_i) combine as one softmax over all
 // keys, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i,
-// stored in fp16 in place of the row's q like an unsplit workgroup.  16
-// threads per row, 4 features each.
+// stored in fp16 in place of the row's q like an unsplit workgroup.  Blocks:
+// (XCD x, tail workgroup i of x, 16 rows); 16 threads per row, 4 features
+// each.
 template <int BQ>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p, int nsplit_wg) {
-  const int per_wg = BQ / 16;
-  const int wi = blockIdx.x / per_wg;
-  const int lr = (blockIdx.x - wi * per_wg) * 16 + (threadIdx.x >> 4);
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
+  constexpr int per_wg = BQ / 16;
+  const int tail_max = p.umax / p.split_p;
+  const int x = blockIdx.x / (tail_max * per_wg);
+  const int rest = blockIdx.x - x * tail_max * per_wg;
+  const int i = rest / per_wg;
+  const int lr = (rest - i * per_wg) * 16 + (threadIdx.x >> 4);
   const int f = (threadIdx.x & 15) * 4;
-  const BlockCoord c = coord_of(p, p.w0 + wi);
+  const XcdRange r = xcd_range(p, x);
+  if (i >= r.tail) return;
+  const BlockCoord c = coord_of(p, r.base + r.whole + i);
   const int row = p.q0 + c.qt * BQ + lr;
-  if (wi >= nsplit_wg || row >= p.L) return;
-  const int nunits = nsplit_wg * p.split_p;
-  const float2* ml = reinterpret_cast<const float2*>(p.part + (int64_t)nunits * BQ * kDh);
-  const int u0 = wi * p.split_p;
+  if (row >= p.L) return;
+  const float2* ml = reinterpret_cast<const float2*>(p.part + (int64_t)kXcds * p.umax * BQ * kDh);
+  const int64_t u0 = (int64_t)x * p.umax + (int64_t)i * p.split_p;
   float M = -INFINITY;
-  for (int i = 0; i < p.split_p; ++i) M = fmaxf(M, ml[(int64_t)(u0 + i) * BQ + lr].x);
+  for (int k = 0; k < p.split_p; ++k) M = fmaxf(M, ml[(u0 + k) * BQ + lr].x);
   float l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < p.split_p; ++i) {
-    const float2 e = ml[(int64_t)(u0 + i) * BQ + lr];
+  for (int k = 0; k < p.split_p; ++k) {
+    const float2 e = ml[(u0 + k) * BQ + lr];
     const float w = __builtin_amdgcn_exp2f(e.x - M);
     l = fmaf(w, e.y, l);
-    const f32x4 oi = *reinterpret_cast<const f32x4*>(p.part + ((int64_t)(u0 + i) * BQ + lr) * kDh + f);
+    const f32x4 oi = *reinterpret_cast<const f32x4*>(p.part + ((u0 + k) * BQ + lr) * kDh + f);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = fmaf(w, oi[k], o[k]);
+    for (int e4 = 0; e4 < 4; ++e4) o[e4] = fmaf(w, oi[e4], o[e4]);
   }
   const float inv = 1.f / l;
   f16x4 out;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) out[k] = (f16)(o[k] * inv);
+  for (int e4 = 0; e4 < 4; ++e4) out[e4] = (f16)(o[e4] * inv);
   f16* qh = p.q + (int64_t)c.h * p.rows * kDh;
   *reinterpret_cast<f16x4*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
 }
@@ -629,25 +667,40 @@ static int device_cus() {
   return cache[dev];
 }
 
-// Split tail: with W workgroups on C slots (CUs times the workgroups of the
-// kernel that fit a CU) the last round holds r = W mod C of them and leaves
-// the other slots idle.  Running each of those r as P key
-// ranges (P units of 1/P the work) shortens the tail from one workgroup time
-// to ceil(r P / C) / P.  P is the smallest that gets within 2% of the best,
-// with at least kSplitMinTiles key tiles per range and r P units within the
-// buffer.  VGGT_ATTN_SPLIT = P forces the key ranges per split workgroup
-// (1: no split; a tuning / testing switch).  Returns P (1: no split).
-static int choose_split(const Plan& p, int64_t W, int ntiles, int per_cu, int64_t* w0) {
-  *w0 = W;
-  if (p.split_cap <= 0) return 1;
+// Split tail.  Each XCD walks a contiguous range of the W workgroups on its
+// slots (its CUs times the workgroups of the kernel that fit a CU); the last
+// round of the range holds tail = n mod slots workgroups and leaves the other
+// slots idle.  Running each of those as P key ranges (P units of 1/P the
+// work, on the same XCD) shortens that round from one workgroup time to
+// ceil(tail P / slots) / P.  P is the smallest that gets within 2% of the
+// best, with at least kSplitMinTiles key tiles per range and 8 * tail * P
+// units within the partial-result buffer.  VGGT_ATTN_SPLIT = P forces the key
+// ranges per split workgroup (1: no split; a tuning / testing switch).
+struct SplitPlan {
+  int P = 1, xcd_slots = 0, umax = 0;
+  int64_t grid = 0;
+};
+
+static SplitPlan choose_split(const Plan& p, int64_t W, int ntiles, int per_cu) {
+  SplitPlan sp;
+  sp.grid = W;
   const int64_t C = (int64_t)device_cus() * (per_cu > 0 ? per_cu : 1);
-  const int64_t r = W % C;
-  if (r == 0) return 1;
-  auto allowed = [&](int P) { return r * P <= p.split_cap && ntiles / P >= kSplitMinTiles; };
+  if (p.split_cap <= 0 || C % kXcds != 0) return sp;
+  const int64_t cpx = C / kXcds;
+  const int64_t per = W / kXcds, rem = W % kXcds;
+  int64_t tail = 0;  // the largest tail of any XCD
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t n = per + (x < rem ? 1 : 0), t = n % cpx;
+    if (t > tail) tail = t;
+  }
+  if (tail == 0) return sp;
+  auto allowed = [&](int P) {
+    return kXcds * tail * P <= p.split_cap && ntiles / P >= kSplitMinTiles;
+  };
   int best = 1;
   double best_t = 1.0;
   for (int P = 2; P <= kSplitMaxWays && allowed(P); ++P) {
-    const double t = (double)((r * P + C - 1) / C) / P;
+    const double t = (double)((tail * P + cpx - 1) / cpx) / P;
     if (t < best_t - 0.02) {
       best_t = t;
       best = P;
@@ -658,8 +711,17 @@ static int choose_split(const Plan& p, int64_t W, int ntiles, int per_cu, int64_
     while (P > 1 && !allowed(P)) --P;
     if (P >= 1) best = P;
   }
-  if (best > 1) *w0 = W - r;
-  return best;
+  if (best <= 1) return sp;
+  int64_t slots = 0;  // the longest XCD
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t n = per + (x < rem ? 1 : 0), t = n % cpx;
+    if (n - t + t * best > slots) slots = n - t + t * best;
+  }
+  sp.P = best;
+  sp.xcd_slots = (int)cpx;
+  sp.umax = (int)(tail * best);
+  sp.grid = slots * kXcds;
+  return sp;
 }
 
 template <int QB, int NW, bool SGA>
@@ -691,8 +753,8 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
     g.sub_w = p.sub_w;
   }
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
-  int64_t w0 = blocks;
-  int P = 1;
+  SplitPlan sp;
+  sp.grid = blocks;
   if (!SGA && p.split_cap > 0) {
     // workgroups of this kernel resident per CU (register / LDS bound)
     static int per_cu = 0;
@@ -700,17 +762,17 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA>, NW * 64,
                                                      0) != hipSuccess)
       per_cu = -1;
-    P = choose_split(p, blocks, (p.Lk + 63) / 64, per_cu, &w0);
+    sp = choose_split(p, blocks, (p.Lk + 63) / 64, per_cu);
   }
-  g.w0 = (int)w0;
-  g.split_p = P;
+  g.split_p = sp.P;
+  g.xcd_slots = sp.xcd_slots;
+  g.umax = sp.umax;
   g.part = reinterpret_cast<float*>(a.ws + p.off_split);
-  const int64_t grid = w0 + (blocks - w0) * P;
-  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)grid), dim3(NW * 64), 0, st, g);
-  if (P > 1) {
-    const int nsplit = (int)(blocks - w0);
-    hipLaunchKernelGGL(attn_merge_kernel<BQ>, dim3((unsigned)(nsplit * (BQ / 16))), dim3(256), 0,
-                       st, g, nsplit);
+  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)sp.grid), dim3(NW * 64), 0, st, g);
+  if (sp.P > 1) {
+    const int tail_max = sp.umax / sp.P;
+    hipLaunchKernelGGL(attn_merge_kernel<BQ>, dim3((unsigned)(kXcds * tail_max * (BQ / 16))),
+                       dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }
