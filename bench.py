@@ -38,10 +38,13 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_kernel_s100_global_hbm_by
 
 
 def attention_source_hash() -> str:
+    """Hash of the attention kernel's code: its sources without // comments
+    and blank lines, so that comment edits keep the recorded counters valid."""
     h = hashlib.sha256()
     for f in ("attention.hip", "common.h"):
-        with open(os.path.join(ROOT, "vggt_global_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "vggt_global_attention_amd", "csrc", f)) as fh:
+            code = [line.split("//", 1)[0].rstrip() for line in fh.read().splitlines()]
+        h.update("\n".join(c for c in code if c.strip()).encode())
     return h.hexdigest()[:16]
 
 

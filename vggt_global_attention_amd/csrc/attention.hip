@@ -36,9 +36,12 @@
 //
 // One kernel, attn_kernel<QB, NW, SGA>: NW waves and NW*QB*32 queries per
 // workgroup (SGA: the subsampled global set, whose keys are a compact copy of
-// the kept tokens, plus two per-row columns folded in at the end).  Global sets use 8 waves x 64 queries (512 queries share each
-// K/V tile, one workgroup per CU, the -m initialiser kept resident); frame and
-// register sets use 4 waves x 32 queries (small sets, ragged ends).  Measured
+// the kept tokens, plus two per-row columns folded in at the end).  Global
+// sets use 8 waves x 64 queries (512 queries share each K/V tile, one
+// workgroup per CU, the -m initialiser kept resident); frame and register
+// sets use 4 waves x 32 queries (small sets, ragged ends).  The partly filled
+// last round of a single-set grid runs as key ranges whose softmax states
+// attn_merge_kernel combines (split tail, below).  Measured
 // alternatives that did not pay on gfx950: an 8-wave "ping-pong" split (waves
 // sharing a SIMD alternating MFMA and softmax phases between barriers),
 // 16x16x32 MFMAs, direct global->LDS loads three buffers deep, and 128
@@ -442,7 +445,7 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 }
 
 // ---------------------------------------------------------------------------
-// 4-wave kernel
+// The kernel
 // ---------------------------------------------------------------------------
 // K / V^T tiles are double buffered in LDS and fetched one tile ahead through
 // registers (global_load -> ds_write after the tile's compute), with one
