@@ -1,9 +1,9 @@
 """GPU checks of the split attention tail.
 
 The last round of workgroups of a single-set grid (global sets, query
-windows, register sets) is only partly filled. The library runs each of
-those workgroups as P key ranges. A merge kernel then combines the ranges'
-softmax states.
+windows, subsampled and register sets) is only partly filled. The library
+runs each of those workgroups as P key ranges. A merge kernel then combines
+the ranges' softmax states.
 
 What is checked:
 - split results match the fp64 oracle at the block bar;
@@ -137,3 +137,21 @@ def test_split_register_s500(monkeypatch):
     frames = np.arange(0, w.S, 25)
     ref = oracle.register_attention(f64(inp["X"]), oracle_params(w, inp), threads=8)
     assert_parity(np64(y[frames, :17]), ref[frames, :17], "s500 register, split")
+
+
+def test_split_subsampled_s24(monkeypatch):
+    """Subsampled global set of 24 frames with 3 x 3 windows (3,216 kept keys):
+    two key ranges per tail workgroup; the diagonal and mean columns enter in
+    the last range only."""
+    from oracle import avggt_sga
+    w = configs.WORKLOADS["s24"]
+    inp = synth.make_inputs(w)
+    d = to_dev(inp)
+    y1 = with_split(monkeypatch, 1, lambda: run("subsampled", w, d, sub=(3, 3)))
+    y2 = with_split(monkeypatch, 2, lambda: run("subsampled", w, d, sub=(3, 3)))
+    m = metrics(np64(y2), np64(y1))
+    assert m["relL1"] <= CLOSE_RELL1, m
+    qt = -(-w.N // 512)
+    rows = tail_rows(w, qt, (qt * w.H) % cus())
+    ref = avggt_sga.sga_attention_rows(f64(inp["X"]), oracle_params(w, inp), 3, 3, rows)
+    assert_parity(np64(y2.reshape(-1, w.d))[rows], ref, "s24 subsampled split 2")

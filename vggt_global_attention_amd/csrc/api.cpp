@@ -165,13 +165,15 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->off_part = off;  // [H][ceil(N/1024)][128] fp32 partial sums
     off += round_up((int64_t)s->H * ((N + 1023) / 1024) * 128 * sizeof(float), 256);
   }
-  // Partial results of a split attention tail (global sets, query windows
-  // and register sets; not frames, whose sets are short, nor the descriptor
-  // mode, whose key count is not known when its workspace is sized).  Sized
-  // from the shape alone, not the device.
+  // Partial results of a split attention tail (global sets, query windows,
+  // subsampled and register sets; not frames, whose sets are short, nor the
+  // descriptor mode, whose key count is not known when its workspace is
+  // sized).  Sized from the shape alone, not the device; in subsampled mode
+  // from the kept keys, largest with 1 x 1 windows, the size the workspace
+  // query reports.
   p->split_cap = 0;
   p->off_split = off;
-  if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER || subsampled) {
     const int64_t bq = (int64_t)p->attn_waves * p->attn_qb * 32;
     const int64_t W = (p->L - p->q0 + bq - 1) / bq * s->H * p->nseq;
     int64_t ways = (p->Lk + kAttnBK - 1) / kAttnBK / kSplitMinTiles;

@@ -461,9 +461,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
 
-  // single-set grids (global, query windows, register sets) may have a split
-  // tail; the subsampled grid never does
-  constexpr bool kSplit = !SGA;
+  // single-set grids may have a split tail
+  constexpr bool kSplit = true;
   const BlockCoord bc = kSplit ? block_coord(p) : coord_of(p, xcd_remap(blockIdx.x, gridDim.x));
   if (kSplit && bc.skip) return;  // whole block: before any barrier
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
@@ -601,7 +600,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       tile_pv(R, smem[0][1], lb, pf);
     }
   }
-  if (SGA && active) sga_columns(R, p, bc.h, qloc0, j, h);
+  // the diagonal and mean columns enter once per row: in its last key range
+  if (SGA && active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, j, h);
   if (kSplit && bc.unit >= 0) {
     // a key range of a split workgroup: unnormalised state for the merge
     float* po = p.part + (int64_t)bc.unit * BQ * kDh;
@@ -758,7 +758,7 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   const int64_t blocks = (int64_t)g.qtiles * p.H * p.nseq;
   SplitPlan sp;
   sp.grid = blocks;
-  if (!SGA && p.split_cap > 0) {
+  if (p.split_cap > 0) {
     // workgroups of this kernel resident per CU (register / LDS bound)
     static int per_cu = 0;
     if (per_cu == 0 &&

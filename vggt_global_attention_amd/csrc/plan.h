@@ -81,7 +81,7 @@ struct Plan {
   int64_t kv_seq_stride;
   int nD;              // subsampled mode: discarded tokens (mean-filled columns)
   // Split tail of a single-set attention grid (global sets, query windows,
-  // register sets): room for split_cap key-range units of partial results
+  // subsampled and register sets): room for split_cap key-range units of partial results
   // (unnormalised O, reference, row sum); launch_core decides from the
   // device's CU count whether the last, partly filled round of workgroups
   // runs as key ranges that a merge kernel combines.
