@@ -89,6 +89,9 @@ def parse():
                          "record its peak device memory at these frame counts, e.g. 1,25,100")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--power", action="store_true",
+                    help="instead of the layer: socket power and shader clock (amd-smi) while "
+                         "the workload's layer runs on its inputs and on zero q/k/v operands")
     return ap.parse_args()
 
 
@@ -334,6 +337,59 @@ def schedule_sweep(frames, steps, warmup):
     return rows
 
 
+def power_run(w, d, steps):
+    """Median socket power and shader clock, sampled with `amd-smi metric -p -c`
+    from a thread, while the layer runs back to back: idle, on the workload's
+    inputs, and on zero operands (Wqkv = 0, beta = 0: q = k = v = 0, every P
+    equal) -- the same kernels and instruction stream with no operand
+    toggling."""
+    import statistics
+    import subprocess
+    import threading
+    import time
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"],
+                                     capture_output=True, text=True, timeout=10).stdout
+                g = json.loads(out)
+                g = g["gpu_data"][0] if isinstance(g, dict) else g[0]
+                clk = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+                samples.append((time.time(), float(g["power"]["socket_power"]["value"]),
+                                sum(clk) / len(clk)))
+            except (OSError, ValueError, KeyError, IndexError, TypeError,
+                    subprocess.SubprocessError):
+                pass
+            time.sleep(0.2)
+
+    z = dict(d)
+    z["Wqkv"] = torch.zeros_like(d["Wqkv"])
+    z["q_beta"] = torch.zeros_like(d["q_beta"])
+    z["k_beta"] = torch.zeros_like(d["k_beta"])
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    rows = []
+    for name, inp in (("idle", None), ("synthetic inputs", d), ("zero operands", z)):
+        print(f"[bench] power: {name}", file=sys.stderr, flush=True)
+        t0 = time.time()
+        ms = core = None
+        if inp is None:
+            time.sleep(2.0)
+        else:
+            ms, core = time_block(w, "global", inp, steps, 3)
+        t1 = time.time()
+        sel = [s for s in samples if t0 + 0.5 < s[0] < t1 - 0.2]
+        rows.append({"case": name, "ms_per_layer": ms, "core_ms": core, "samples": len(sel),
+                     "socket_power_w": statistics.median(s[1] for s in sel) if sel else None,
+                     "gfx_clock_mhz": statistics.median(s[2] for s in sel) if sel else None})
+    stop.set()
+    th.join()
+    return rows
+
+
 def host_info():
     """CPU model, logical CPUs and NumPy's BLAS, for the oracle timing."""
     import platform
@@ -467,6 +523,9 @@ def main():
     sub = tuple(int(x) for x in a.sub.lower().split("x")) if a.mode == "subsampled" else (1, 1)
     print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
     inp, d = gpu_inputs(w)
+    if a.power:
+        print(json.dumps({"power": power_run(w, d, a.steps), "workload": w.name}), flush=True)
+        return
     if a.descriptors:
         r = time_descriptor(w, d, a.descriptors, a.steps, a.warmup)
         r["workload"] = w.name
