@@ -102,6 +102,12 @@ def test_s300_global_sampled():
     sampled_case(W["s300"], "global", n_rows=256)
 
 
+def test_s500_global_sampled():
+    """The largest global set of the workloads: 500 frames, 515,500 tokens
+    (q/k/v offsets past 2^31 bytes, 8,055 key tiles, a split tail)."""
+    sampled_case(W["s500"], "global", n_rows=128)
+
+
 def test_s500_frame_sampled():
     sampled_case(W["s500"], "frame")
 
