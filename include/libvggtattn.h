@@ -153,8 +153,11 @@ int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int
    the window only.  Y_rows is bf16 [row_count][d] (row i = token
    row_begin + i).  Requires 0 <= row_begin, 1 <= row_count,
    row_begin + row_count <= S*T (else VGGT_ATTN_ERANGE).  Workspace:
-   vggt_attn_workspace_bytes(VGGT_ATTN_MODE_GLOBAL).  The rows are bitwise
-   those vggt_attn_global writes for them. */
+   vggt_attn_workspace_bytes(VGGT_ATTN_MODE_GLOBAL).  The rows equal those
+   vggt_attn_global writes for them up to the fp32 summation order of the
+   query blocks that either call runs as split key ranges (the partly filled
+   last round of workgroups on the device); with the environment variable
+   VGGT_ATTN_SPLIT=1 (no split) they are bitwise equal. */
 int vggt_attn_global_rows(const vggt_attn_shape* shape, int64_t row_begin, int64_t row_count,
                           const void* X, const void* Wqkv, const void* Wo, const float* q_gamma,
                           const float* q_beta, const float* k_gamma, const float* k_beta,
