@@ -17,9 +17,12 @@ constexpr int kGemmBK = 64;
 constexpr int kAttnBK = 64;         // keys per attention tile
 constexpr int kRowAlign = 2048;     // workspace rows are padded to this (8 XCDs x 256-row tiles)
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
-constexpr int kSplitMaxRows = 1 << 18;  // query rows x key ranges of a split attention tail (its buffer)
-constexpr int kSplitMaxWays = 32;   // key ranges per split workgroup at most
-constexpr int kSplitMinTiles = 24;  // key tiles per range at least
+// Split attention tail: its partial-result buffer holds at most
+// kSplitMaxRows query rows x key ranges; a split workgroup runs at most
+// kSplitMaxWays key ranges of at least kSplitMinTiles key tiles each.
+constexpr int kSplitMaxRows = 1 << 18;
+constexpr int kSplitMaxWays = 32;
+constexpr int kSplitMinTiles = 24;
 
 // Options of the extended entry points.
 struct CallOpts {
@@ -81,10 +84,10 @@ struct Plan {
   int64_t kv_seq_stride;
   int nD;              // subsampled mode: discarded tokens (mean-filled columns)
   // Split tail of a single-set attention grid (global sets, query windows,
-  // subsampled and register sets): room for split_cap key-range units of partial results
-  // (unnormalised O, reference, row sum); launch_core decides from the
-  // device's CU count whether the last, partly filled round of workgroups
-  // runs as key ranges that a merge kernel combines.
+  // subsampled and register sets): room for split_cap key-range units of
+  // partial results (unnormalised O, reference, row sum); launch_core
+  // decides from the device's CU count whether the last, partly filled round
+  // of workgroups runs as key ranges that a merge kernel combines.
   int split_cap;
   // workspace carve-up (byte offsets)
   size_t off_scal, off_rope, off_wo, off_q, off_k, off_v;
