@@ -89,6 +89,9 @@ def parse():
                          "record its peak device memory at these frame counts, e.g. 1,25,100")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --schedule: also time the forward captured into a HIP graph "
+                         "(frame counts up to 100)")
     ap.add_argument("--power", action="store_true",
                     help="instead of the layer: socket power and shader clock (amd-smi) while "
                          "the workload's layer runs on its inputs and on zero q/k/v operands")
@@ -275,10 +278,13 @@ def hbm_kernels(steps):
     return out
 
 
-def schedule_forward(w, spec, steps, warmup, ls=1e-5):
+def schedule_forward(w, spec, steps, warmup, ls=1e-5, graph=False):
     """ms per attention-only forward of `spec` and the peak device memory of
     the run (torch's allocator high-water mark: input, state, kept states,
-    workspace and the weights of every block)."""
+    workspace and the weights of every block).  graph: also the forward
+    captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed, which
+    removes the host launch cost of its ~400 kernels (into its own state
+    buffer, after the memory figure is taken)."""
     import torch
     from vggt_global_attention_amd import schedule as S
     from vggt_global_attention_amd import synth
@@ -311,12 +317,33 @@ def schedule_forward(w, spec, steps, warmup, ls=1e-5):
            "state_bytes": X.numel() * 2, "caches_bytes": caches.numel() * 2,
            "workspace_bytes": sch.workspace.numel(), "flop_per_forward": flop,
            "inter_modes": [spec.inter_mode(l) for l in range(spec.n_layers)]}
+    if graph:
+        state = torch.empty_like(X)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            sch(X, state=state, caches=caches)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            sch(X, state=state, caches=caches)
+        for _ in range(max(warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["ms_per_forward_graph"] = e0.elapsed_time(e1) / steps
+        del g, state
     del sch, caches, X, blocks
     torch.cuda.empty_cache()
     return out
 
 
-def schedule_sweep(frames, steps, warmup):
+def schedule_sweep(frames, steps, warmup, graph=False):
     from vggt_global_attention_amd import configs
     from vggt_global_attention_amd import schedule as S
     variants = {"vggt": S.ScheduleSpec(),
@@ -329,10 +356,13 @@ def schedule_sweep(frames, steps, warmup):
         for vname, spec in variants.items():
             print(f"[bench] schedule {vname} S={n}", file=sys.stderr, flush=True)
             st = steps if n <= 100 else 1
-            r = schedule_forward(w, spec, st, min(warmup, 1) if n > 100 else warmup)
+            r = schedule_forward(w, spec, st, min(warmup, 1) if n > 100 else warmup,
+                                 graph=graph and n <= 100)
             r["variant"] = vname
             rows.append(r)
-            print(f"[bench]   {r['ms_per_forward']:.1f} ms, peak {r['peak_gb']:.2f} GB",
+            gtxt = (f", graph replay {r['ms_per_forward_graph']:.1f} ms"
+                    if "ms_per_forward_graph" in r else "")
+            print(f"[bench]   {r['ms_per_forward']:.1f} ms{gtxt}, peak {r['peak_gb']:.2f} GB",
                   file=sys.stderr, flush=True)
     return rows
 
@@ -513,7 +543,7 @@ def main():
         return
     if a.schedule:
         frames = [int(x) for x in a.schedule.split(",")]
-        rows = schedule_sweep(frames, a.steps, a.warmup)
+        rows = schedule_sweep(frames, a.steps, a.warmup, graph=a.graph)
         print(json.dumps({"schedule_sweep": rows, "layers": 24,
                           "register_layers": [2, 6, 9, 14, 20], "cached_layers": [4, 11, 17, 23],
                           "shape": "T=1031 (26x39 patches + 17), d=1024, H=16, bf16 state",
