@@ -90,7 +90,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     const int w = atoi(e);
     if (w == 4 || w == 8) p->attn_waves = w;
   }
-  p->rows = round_up(cover, kRowAlign);
+  p->rows = round_up(cover, cover >= kRowAlignFrom ? kRowAlign : 256);
   if (p->rows >= ((int64_t)1 << 31)) return VGGT_ATTN_ESHAPE;  // kernels index rows in 32 bits
   p->sub_h = sub_h;
   p->sub_w = sub_w;

@@ -845,16 +845,33 @@ static int feature_groups(int nf, int k, int elem_bytes, int bn) {
 
 // Kernel choice: 2 = wide (256 x 256, output features a multiple of 256),
 // 1 = DMA 256 x 128, 0 = register-staged 128 x 128.  The DMA kernels need
-// whole 256-row token tiles.  VGGT_GEMM = 0 | 1 | 2 caps the choice (a tuning
+// whole 256-row token tiles.  VGGT_GEMM = 0 | 1 | 2 picks the kind (a tuning
 // / comparison switch).
 static int gemm_kind(const Plan& p, int nf) {
   int kind = 2;
+  bool forced = false;
   if (const char* e = getenv("VGGT_GEMM")) {
     const int v = atoi(e);
-    if (v >= 0 && v < 2) kind = v;
+    if (v >= 0 && v <= 2) {
+      kind = v;
+      forced = true;
+    }
   }
   if (kind == 2 && nf % kWBN != 0) kind = 1;
   if (kind >= 1 && p.rows % kDmaBM != 0) kind = 0;
+  // Few token rows (small sets): the smaller tiles that give more CUs a
+  // workgroup, while the larger ones would leave most of them idle.
+  if (!forced) {
+    static int cus = 0;
+    if (cus == 0) {
+      int dev = 0, n = 0;
+      cus = (hipGetDevice(&dev) == hipSuccess &&
+             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+             n > 0) ? n : 256;
+    }
+    if (kind == 2 && (p.rows / kWBM) * (nf / kWBN) < cus) kind = 1;
+    if (kind == 1 && (p.rows / kDmaBM) * (nf / kDmaBN) < cus) kind = 0;
+  }
   return kind;
 }
 

@@ -15,7 +15,11 @@ constexpr int kGemmBM = 128;        // token rows per GEMM tile
 constexpr int kGemmBN = 128;        // output features per GEMM tile (two heads)
 constexpr int kGemmBK = 64;
 constexpr int kAttnBK = 64;         // keys per attention tile
-constexpr int kRowAlign = 2048;     // workspace rows are padded to this (8 XCDs x 256-row tiles)
+// Workspace rows are padded to kRowAlign (8 XCDs x 256-row GEMM tiles, so
+// each XCD walks whole token tiles), or to one 256-row tile when that
+// padding would be large (fewer than kRowAlignFrom rows).
+constexpr int kRowAlign = 2048;
+constexpr int kRowAlignFrom = 16384;
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
 // Split attention tail: its partial-result buffer holds at most
 // kSplitMaxRows query rows x key ranges; a split workgroup runs at most
@@ -68,7 +72,7 @@ struct Plan {
   int L;               // query rows of a set end here (= q0 + query count)
   int q0;              // first query row (a window of the global set), else 0
   int64_t seq_stride;
-  int64_t rows;        // workspace rows held by q/k/v (multiple of kRowAlign)
+  int64_t rows;        // workspace rows held by q/k/v (multiple of 256)
   RowMap map;          // workspace row -> X row
   RowMap out_map;      // workspace row -> Y row (the window's rows only, when windowed)
   bool window;         // global mode restricted to query rows [q0, L)
