@@ -137,6 +137,8 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   size_t off = 0;
   p->off_scal = off;
   off += round_up((int64_t)sizeof(float) * (4 + s->H), 256);
+  p->off_bounds = off;  // partial maxima of the prep stage
+  off += round_up((int64_t)sizeof(float) * (kBoundsX + kBoundsV + kBoundsO), 256);
   p->off_rope = off;
   off += round_up((int64_t)p->rope_npos * 16 * sizeof(float2), 256);
   p->off_wo = off;

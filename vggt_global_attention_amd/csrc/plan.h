@@ -24,6 +24,10 @@ constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are pa
 // Split attention tail: its partial-result buffer holds at most
 // kSplitMaxRows query rows x key ranges; a split workgroup runs at most
 // kSplitMaxWays key ranges of at least kSplitMinTiles key tiles each.
+// Prep stage: per-workgroup partial maxima of the range bounds (X row norms
+// over up to kBoundsX workgroups, V rows of Wqkv over kBoundsV, |Wo| over
+// kBoundsO), reduced by the Wo conversion.
+constexpr int kBoundsX = 2048, kBoundsV = 64, kBoundsO = 128;
 constexpr int kSplitMaxRows = 1 << 18;
 constexpr int kSplitMaxWays = 32;
 constexpr int kSplitMinTiles = 24;
@@ -94,7 +98,7 @@ struct Plan {
   // of workgroups runs as key ranges that a merge kernel combines.
   int split_cap;
   // workspace carve-up (byte offsets)
-  size_t off_scal, off_rope, off_wo, off_q, off_k, off_v;
+  size_t off_scal, off_bounds, off_rope, off_wo, off_q, off_k, off_v;
   size_t off_kc, off_vc, off_sums, off_part;  // subsampled mode only (else 0)
   size_t off_split;    // [split_cap][BQ][64] fp32 O, then [split_cap][BQ] float2 (m, l)
   DescLayout desc;     // descriptor mode: layout of the key / value cache

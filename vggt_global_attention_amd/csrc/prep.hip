@@ -1,30 +1,124 @@
 // Prep-stage kernels (all HBM-bound and small next to the GEMMs and the
-// attention core):
-//   * clear the workspace scalars (and the subsampled mode's sums) and
-//     tabulate cos/sin of the 2D RoPE angles;
-//   * range bounds: max L2 norm of the X rows of the attention set(s), of the
-//     V rows of Wqkv, and max |Wo| -- they pick exact power-of-two scales that
-//     keep V, O and Wo inside fp16 range for the attention and output kernels;
-//   * an fp16 copy of Wo scaled by 2^s (the output GEMM runs on fp16 MFMA);
-//   * the register-mode patch-row copy Y = X.
+// attention core), two launches per call:
+//   * bounds_kernel: cos/sin of the 2D RoPE angles, the subsampled mode's
+//     sums cleared, and the range bounds -- max L2 norm of the X rows of the
+//     attention set(s), of the V rows of Wqkv, and max |Wo| -- as one partial
+//     maximum per workgroup (no atomics, nothing to clear first);
+//   * wo_convert_kernel: reduces the partial maxima into the workspace
+//     scalars (exact power-of-two scales that keep V, O and Wo inside fp16
+//     range) and writes the fp16 copy of Wo scaled by 2^s (the output GEMM
+//     runs on fp16 MFMA);
+// plus the register-mode patch-row copy Y = X and the residual update of a
+// layer schedule.
 #include "plan.h"
 
 namespace vggt {
 
 // RoPE table entry (pos, i) = (cos, sin)(pos * base^(-i/16)) for the 16
 // frequencies of a 32-feature half of a 64-wide head; angles in double.
-// Also clears `nsums` floats at `sums` (subsampled mode: the discarded-token
-// sums the CORE stage accumulates).
-__global__ void prep_kernel(float* scal, int nscal, float* sums, int nsums, float2* rope, int npos,
-                            float base) {
-  for (int i = threadIdx.x; i < nscal; i += blockDim.x) scal[i] = 0.f;
-  for (int i = threadIdx.x; i < nsums; i += blockDim.x) sums[i] = 0.f;
-  for (int i = threadIdx.x; i < npos * 16; i += blockDim.x) {
-    int pos = i >> 4, f = i & 15;
-    double theta = pow((double)base, -(double)f / 16.0);
-    double sn, cs;
-    sincos((double)pos * theta, &sn, &cs);
-    rope[i] = make_float2((float)cs, (float)sn);
+__device__ __forceinline__ float2 rope_entry(int i, float base) {
+  const int pos = i >> 4, f = i & 15;
+  const double theta = pow((double)base, -(double)f / 16.0);
+  double sn, cs;
+  sincos((double)pos * theta, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
+// Largest L2 norm of the bf16 rows of `len` elements (a multiple of 8) that
+// waves wave0, wave0 + nwaves, ... of the grid walk (four rows at a time,
+// loads issued together); rows are mapped through `map`, unmapped rows
+// skipped.  Per-lane result (every lane of a wave holds the wave's value).
+__device__ __forceinline__ float rows_norm_max(const bf16* base, int64_t nrows, int len,
+                                               const RowMap& map, int64_t wave0, int64_t nwaves,
+                                               int lane) {
+  float best = 0.f;
+  for (int64_t w0 = wave0; w0 < nrows; w0 += 4 * nwaves) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t w = w0 + u * nwaves;
+      const int64_t src = w < nrows ? map.src(w) : -1;
+      if (src < 0) continue;
+      const bf16* row = base + src * len;
+      for (int c = lane * 8; c < len; c += 512) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)v[e];
+          acc[u] = fmaf(f, f, acc[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float a = acc[u];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+      best = fmaxf(best, sqrtf(a));
+    }
+  }
+  return best;
+}
+
+// Maximum of v over a 256-thread workgroup (result in thread 0).
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();  // `red` may still be read from a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+struct BoundsArgs {
+  const bf16* X;      // rows through map (skipped when null: descriptor mode)
+  int64_t rows;
+  RowMap map;
+  const bf16* Wv;     // the V rows of Wqkv, [d][d] (skipped when X is null)
+  const bf16* Wo;     // [d][d]
+  int d;
+  float* part;        // [kBoundsX] X, then [kBoundsV] Wv, then [kBoundsO] Wo partial maxima
+  float2* rope;
+  int nrope;          // table entries (positions x 16)
+  float base;
+  float* sums;        // subsampled mode: cleared
+  int nsums;
+};
+
+// One launch: RoPE table, cleared sums and the partial bound maxima.  Every
+// workgroup takes part in the X rows; the first kBoundsV in the V rows of
+// Wqkv, the first kBoundsO in |Wo|.  The grid has at least kBoundsO
+// workgroups and at most kBoundsX.
+__global__ __launch_bounds__(256) void bounds_kernel(BoundsArgs b) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + tid, gthreads = (int64_t)gridDim.x * 256;
+  for (int64_t i = gtid; i < b.nrope; i += gthreads) b.rope[i] = rope_entry((int)i, b.base);
+  for (int64_t i = gtid; i < b.nsums; i += gthreads) b.sums[i] = 0.f;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  float xm = 0.f, vm = 0.f, om = 0.f;
+  if (b.X) {
+    xm = rows_norm_max(b.X, b.rows, b.d, b.map, wave, (int64_t)gridDim.x * 4, lane);
+    if (blockIdx.x < kBoundsV) {
+      const RowMap ident{INT64_MAX / 2, 0, b.d, 1, 0};
+      vm = rows_norm_max(b.Wv, b.d, b.d, ident, wave, (int64_t)kBoundsV * 4, lane);
+    }
+  }
+  if (blockIdx.x < kBoundsO) {
+    const int64_t n8 = (int64_t)b.d * b.d / 8;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n8; i += (int64_t)kBoundsO * 256) {
+      const bf16x8 v = reinterpret_cast<const bf16x8*>(b.Wo)[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) om = fmaxf(om, fabsf((float)v[e]));
+    }
+  }
+  xm = block_max(xm, red);
+  vm = block_max(vm, red);
+  om = block_max(om, red);
+  if (tid == 0) {
+    b.part[blockIdx.x] = xm;
+    if (blockIdx.x < kBoundsV) b.part[kBoundsX + blockIdx.x] = vm;
+    if (blockIdx.x < kBoundsO) b.part[kBoundsX + kBoundsV + blockIdx.x] = om;
   }
 }
 
@@ -73,30 +167,31 @@ __global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int6
   }
 }
 
-__global__ __launch_bounds__(256) void absmax_kernel(const bf16* x, int64_t n8, float* out) {
-  __shared__ float red[4];
-  float best = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    bf16x8 v = reinterpret_cast<const bf16x8*>(x)[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) best = fmaxf(best, fabsf((float)v[e]));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (m > 0.f) atomic_max_nonneg(out, m);
-  }
-}
-
 // Wo (bf16) -> fp16 * 2^s with s chosen from max|Wo| so the largest entry
-// lands near 2^14; exact for every entry within 2^-24 of the largest.
+// lands near 2^14; exact for every entry within 2^-24 of the largest.  Every
+// workgroup reduces the |Wo| partial maxima itself; workgroup 0 also writes
+// the scalars: the three bounds and cleared key norms (the QKV epilogue
+// takes their maximum).  nx = X partials written by the bounds kernel.
 __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t n8,
-                                                         const Scalars* sc, f16* out) {
-  const int s = range_exponent(sc->woabs);
+                                                         const float* part, int nx, Scalars* sc,
+                                                         int H, f16* out) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const float woabs = block_max(tid < kBoundsO ? part[kBoundsX + kBoundsV + tid] : 0.f, red);
+  if (blockIdx.x == 0) {
+    float xm = 0.f;
+    for (int i = tid; i < nx; i += 256) xm = fmaxf(xm, part[i]);
+    xm = block_max(xm, red);
+    const float vm = block_max(tid < kBoundsV ? part[kBoundsX + tid] : 0.f, red);
+    if (tid == 0) {
+      sc->xnorm = xm;
+      sc->wvnorm = vm;
+      sc->woabs = woabs;
+      sc->pad = 0.f;
+    }
+    for (int i = tid; i < H; i += 256) sc->kmax[i] = 0.f;
+  }
+  const int s = range_exponent(woabs);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
     bf16x8 v = reinterpret_cast<const bf16x8*>(wo)[i];
@@ -168,25 +263,29 @@ static int grid_for(int64_t work, int per_block, int cap) {
 hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   Scalars* sc = ws_scalars(p, a);
   const bool sub = p.mode == VGGT_ATTN_MODE_SUBSAMPLED;
-  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(sc),
-                     4 + p.H, sub ? ws_sums(p, a) : nullptr, sub ? 128 * p.H : 0, ws_rope(p, a),
-                     p.rope_npos, p.base);
   // Descriptor mode: no values are projected here; the bounds of the cached
   // values are copied in after the Wo conversion (launch_desc_load).
-  if (p.mode != VGGT_ATTN_MODE_DESCRIPTOR) {
-    // X rows of the set(s): walk the workspace rows through the row map.
-    hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.rows, 16, 2048)), dim3(256), 0, st,
-                       a.X, p.rows, p.d, p.map, &sc->xnorm);
-    RowMap ident{INT64_MAX / 2, 0, p.d, 1};
-    hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid_for(p.d, 16, 2048)), dim3(256), 0, st,
-                       a.Wqkv + (int64_t)2 * p.d * p.d, (int64_t)p.d, p.d, ident, &sc->wvnorm);
-  }
+  const bool desc = p.mode == VGGT_ATTN_MODE_DESCRIPTOR;
+  BoundsArgs b;
+  b.X = desc ? nullptr : a.X;
+  b.rows = p.rows;
+  b.map = p.map;
+  b.Wv = a.Wqkv + (int64_t)2 * p.d * p.d;
+  b.Wo = a.Wo;
+  b.d = p.d;
+  b.part = reinterpret_cast<float*>(a.ws + p.off_bounds);
+  b.rope = ws_rope(p, a);
+  b.nrope = p.rope_npos * 16;
+  b.base = p.base;
+  b.sums = sub ? ws_sums(p, a) : nullptr;
+  b.nsums = sub ? 128 * p.H : 0;
+  int grid = desc ? kBoundsO : grid_for(p.rows, 16, kBoundsX);
+  if (grid < kBoundsO) grid = kBoundsO;
+  hipLaunchKernelGGL(bounds_kernel, dim3(grid), dim3(256), 0, st, b);
   const int64_t n8 = (int64_t)p.d * p.d / 8;
-  hipLaunchKernelGGL(absmax_kernel, dim3(grid_for(n8, 1024, 256)), dim3(256), 0, st, a.Wo, n8,
-                     &sc->woabs);
   hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
-                     n8, (const Scalars*)sc, ws_wo(p, a));
-  if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return launch_desc_load(p, a, st);
+                     n8, (const float*)b.part, grid, sc, p.H, ws_wo(p, a));
+  if (desc) return launch_desc_load(p, a, st);
   return hipGetLastError();
 }
 
