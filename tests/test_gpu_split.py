@@ -75,9 +75,11 @@ def test_forced_split_s24(monkeypatch, ways):
     assert_parity(np64(yp.reshape(-1, w.d))[rows], ref, f"s24 split {ways}")
 
 
-def test_split_every_workgroup():
-    """Three frames: 112 workgroups, fewer than the CUs, so the default plan
-    splits all of them (no whole workgroup); full oracle."""
+def test_split_every_workgroup(monkeypatch):
+    """Three frames on the 8-wave tile (forced: a grid this small picks the
+    4-wave one): 112 workgroups, fewer than the CUs, so the plan splits all
+    of them (no whole workgroup); full oracle."""
+    monkeypatch.setenv("VGGT_ATTN_WAVES", "8")
     w = configs.custom("split3", 3, 26, 39, 1024, 16, cid=23)
     inp = synth.make_inputs(w)
     d = to_dev(inp)

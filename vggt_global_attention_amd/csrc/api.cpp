@@ -82,13 +82,20 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   }
   // Tuning override of the attention tile: VGGT_ATTN_QB = 1 or 2 query
   // blocks of 32 per wave, VGGT_ATTN_WAVES = 4 or 8 waves per workgroup.
+  bool tile_forced = false;
   if (const char* e = getenv("VGGT_ATTN_QB")) {
     const int q = atoi(e);
-    if (q == 1 || q == 2) p->attn_qb = q;
+    if (q == 1 || q == 2) {
+      p->attn_qb = q;
+      tile_forced = true;
+    }
   }
   if (const char* e = getenv("VGGT_ATTN_WAVES")) {
     const int w = atoi(e);
-    if (w == 4 || w == 8) p->attn_waves = w;
+    if (w == 4 || w == 8) {
+      p->attn_waves = w;
+      tile_forced = true;
+    }
   }
   p->rows = round_up(cover, cover >= kRowAlignFrom ? kRowAlign : 256);
   if (p->rows >= ((int64_t)1 << 31)) return VGGT_ATTN_ESHAPE;  // kernels index rows in 32 bits
@@ -130,6 +137,16 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->q0 = (int)o.q_begin;
     p->L = (int)(o.q_begin + o.q_count);
     p->out_map = RowMap{p->rows, 0, (int32_t)o.q_count, 1, o.q_begin};
+  }
+  // Small global-type grids (global sets, query windows, descriptor
+  // attention): when the 8-wave tile would give fewer workgroups than an
+  // MI355X has CUs (256), the 4-wave tile of one query block per wave runs
+  // four times as many, up to three per CU.  Both tiles compute every row
+  // the same way, bit for bit.
+  if ((mode == VGGT_ATTN_MODE_GLOBAL || desc) && !tile_forced &&
+      (int64_t)(p->L - p->q0 + 511) / 512 * s->H < 256) {
+    p->attn_qb = 1;
+    p->attn_waves = 4;
   }
   p->rope_npos = (s->grid_h > s->grid_w ? s->grid_h : s->grid_w) + s->pos_offset;
   if (p->rope_npos < 1) p->rope_npos = 1;
