@@ -4,11 +4,27 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "entry.h"
 
 namespace vggt {
 
 static int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Kept tokens per frame in subsampled mode: the 17 specials and the top-left
 // cell of every sub_h x sub_w window of the grid.

@@ -48,6 +48,7 @@
 // queries per wave (spills).  With random fp16 operands this loop is
 // power-bound: the shader clock settles near 1.9 GHz, so lowering the energy
 // per FLOP (LDS bytes, non-MFMA instructions) matters as much as issue slots.
+#include <atomic>
 #include <type_traits>
 
 #include "plan.h"
@@ -655,21 +656,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   *reinterpret_cast<f16x4*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
 }
 
-// Compute units of the current device, cached per device.
-static int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n < 1)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // Split tail.  Each XCD walks a contiguous range of the W workgroups on its
 // slots (its CUs times the workgroups of the kernel that fit a CU); the last
 // round of the range holds tail = n mod slots workgroups and leaves the other
@@ -687,7 +673,7 @@ struct SplitPlan {
 static SplitPlan choose_split(const Plan& p, int64_t W, int ntiles, int per_cu) {
   SplitPlan sp;
   sp.grid = W;
-  const int64_t C = (int64_t)device_cus() * (per_cu > 0 ? per_cu : 1);
+  const int64_t C = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : 1);
   if (p.split_cap <= 0 || C % kXcds != 0) return sp;
   const int64_t cpx = C / kXcds;
   const int64_t per = W / kXcds, rem = W % kXcds;
@@ -760,11 +746,14 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   sp.grid = blocks;
   if (p.split_cap > 0) {
     // workgroups of this kernel resident per CU (register / LDS bound)
-    static int per_cu = 0;
-    if (per_cu == 0 &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA>, NW * 64,
-                                                     0) != hipSuccess)
-      per_cu = -1;
+    static std::atomic<int> occupancy{0};
+    int per_cu = occupancy.load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA>,
+                                                       NW * 64, 0) != hipSuccess)
+        per_cu = -1;
+      occupancy.store(per_cu, std::memory_order_relaxed);
+    }
     sp = choose_split(p, blocks, (p.Lk + 63) / 64, per_cu);
   }
   g.split_p = sp.P;

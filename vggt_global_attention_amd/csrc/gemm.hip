@@ -862,13 +862,7 @@ static int gemm_kind(const Plan& p, int nf) {
   // Few token rows (small sets): the smaller tiles that give more CUs a
   // workgroup, while the larger ones would leave most of them idle.
   if (!forced) {
-    static int cus = 0;
-    if (cus == 0) {
-      int dev = 0, n = 0;
-      cus = (hipGetDevice(&dev) == hipSuccess &&
-             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-             n > 0) ? n : 256;
-    }
+    const int cus = device_cu_count();
     if (kind == 2 && (p.rows / kWBM) * (nf / kWBN) < cus) kind = 1;
     if (kind == 1 && (p.rows / kDmaBM) * (nf / kDmaBN) < cus) kind = 0;
   }

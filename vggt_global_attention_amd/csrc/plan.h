@@ -118,6 +118,10 @@ struct Ptrs {
   char* cache;  // descriptor mode: the key / value cache (read-only there)
 };
 
+// Compute units of the current device (256 when it cannot be queried),
+// cached per device.
+int device_cu_count();
+
 // Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  `o` carries
 // the subsampling windows (VGGT_ATTN_MODE_SUBSAMPLED) or the query-row
 // window (VGGT_ATTN_MODE_GLOBAL); defaults mean neither.
