@@ -44,7 +44,8 @@
 // attn_merge_kernel combines (split tail, below).  Measured
 // alternatives that did not pay on gfx950: an 8-wave "ping-pong" split (waves
 // sharing a SIMD alternating MFMA and softmax phases between barriers),
-// 16x16x32 MFMAs, direct global->LDS loads three buffers deep, and 128
+// 16x16x32 MFMAs, direct global->LDS loads three buffers deep (two deep is
+// what the loop uses), and 128
 // queries per wave (spills).  With random fp16 operands this loop is
 // power-bound: the shader clock settles near 1.9 GHz, so lowering the energy
 // per FLOP (LDS bytes, non-MFMA instructions) matters as much as issue slots.
@@ -90,8 +91,16 @@ struct AttnArgs {
 // with row bits 0..2 and bit 3 spreads such a read over all banks (measured
 // on gfx950: 5.2 cycles per ds_read_b128 per CU, against 8.8 with bits 0..2
 // alone).
-__device__ __forceinline__ int lds_swz(int row, int col) {
-  return row * 128 + ((col ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+__device__ __forceinline__ int lds_slot(int row, int col) {
+  return col ^ (row & 7) ^ ((row >> 3) & 1);  // an involution in col for a fixed row
+}
+__device__ __forceinline__ int lds_swz(int row, int col) { return row * 128 + (lds_slot(row, col) << 4); }
+
+// 16 bytes per lane global -> LDS by the load unit (global_load_lds): lane i
+// of the wave writes lds_wave_base + 16 i.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
 // Softmax state of the QB*32 query rows one wave owns (lane: row l%32 of
@@ -448,14 +457,12 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-// K / V^T tiles are double buffered in LDS and fetched one tile ahead through
-// registers (global_load -> ds_write after the tile's compute), with one
-// workgroup barrier per tile.
+// K / V^T tiles are double buffered in LDS and copied one tile ahead by the
+// load unit (global_load_lds, no register staging), with one workgroup
+// barrier per tile.
 template <int QB, int NW, bool SGA>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
-  constexpr int NT = NW * 64;
-  constexpr int CH = 1024 / NT;  // 16-byte chunks per thread per K+V tile
   __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];
 
   const int tid = threadIdx.x;
@@ -492,33 +499,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   }
   const int last_valid = t1 == ntiles ? p.Lk - 64 * (ntiles - 1) : 64;
 
-  // 1024 16-byte chunks per K+V tile, CH per thread: chunk c < 512 is K (row
-  // c>>3, col c&7), chunk c >= 512 is V^T (feature row, col).
-  u32x4 rg[CH];
-  int soff[CH];
-  const f16* gsrc[CH];
-  int64_t gstep[CH];
+  // K and v^T tiles are 64 rows of 128 bytes each.  The load unit copies them
+  // straight into LDS: one instruction fills 8 consecutive rows (1 KB; lane i
+  // lands in row i/8, slot i%8), so lane i fetches the source chunk that the
+  // row swizzle puts in that slot.  Wave w fills rows [8 KI w, 8 KI (w+1)) of
+  // both tiles.  A tile is complete once every wave has waited for its own
+  // copies (vmcnt) and passed the workgroup barrier.
+  constexpr int KI = 8 / NW;
+  const f16* gk[KI];
+  const f16* gv[KI];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = tid + NT * i;
-    const int cc = c & 511, row = cc >> 3, col = cc & 7;
-    soff[i] = (c >> 9) * (64 * 128) + lds_swz(row, col);
-    if (c < 512) {
-      gsrc[i] = kh + (kv0 + row) * kDh + col * 8;
-      gstep[i] = 64 * kDh;
-    } else {
-      gsrc[i] = vh + (int64_t)row * p.kv_rows + kv0 + col * 8;
-      gstep[i] = 64;
-    }
+  for (int i = 0; i < KI; ++i) {
+    const int row = 8 * (wave * KI + i) + (lane >> 3);
+    const int col = lds_slot(row, lane & 7);
+    gk[i] = kh + (kv0 + row) * kDh + col * 8;
+    gv[i] = vh + (int64_t)row * p.kv_rows + kv0 + col * 8;
   }
-  auto gload = [&](int tile) {
+  auto issue = [&](int tile, int buf) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      rg[i] = *reinterpret_cast<const u32x4*>(gsrc[i] + (int64_t)tile * gstep[i]);
+    for (int i = 0; i < KI; ++i) {
+      lds_dma16(gk[i] + (int64_t)tile * 64 * kDh, &smem[buf][0][0] + (wave * KI + i) * 1024);
+      lds_dma16(gv[i] + (int64_t)tile * 64, &smem[buf][1][0] + (wave * KI + i) * 1024);
+    }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(&smem[buf][0][0] + soff[i]) = rg[i];
+  auto land = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS
+    __syncthreads();
   };
 
   f32x16 S[2][QB];
@@ -532,19 +538,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   // halves from being interleaved (which would only add live registers).
   auto step = [&](auto buf_c, int t) {
     constexpr int BUF = decltype(buf_c)::value;
-    gload(t + 1);
+    issue(t + 1, BUF ^ 1);
     if (active) {
       tile_qk<QB, RES, false>(R, smem[BUF][0], la, h, 64, S);
       tile_softmax(R, S, pf, t == t0);
       tile_pv(R, smem[BUF][1], la, pf);
     }
-    sstore(BUF ^ 1);
-    __syncthreads();
+    land();
     __builtin_amdgcn_sched_barrier(0);
   };
-  gload(t0);
-  sstore(0);
-  __syncthreads();
+  issue(t0, 0);
+  land();
   // all tiles of the range but its last: no mask; tile t sits in LDS buffer
   // (t - t0) & 1
   int t = t0;
@@ -565,14 +569,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) lb[c] = la[c];
     for (; t < t1 - 1; ++t) {
-      gload(t + 1);
+      issue(t + 1, ((t - t0) & 1) ^ 1);
       if (active) {
         tile_qk<QB, RES, false>(R, smem[0][0], lb, h, 64, S);
         tile_softmax(R, S, pf, t == t0);
         tile_pv(R, smem[0][1], lb, pf);
       }
-      sstore(((t - t0) & 1) ^ 1);
-      __syncthreads();
+      land();
 #pragma unroll
       for (int c = 0; c < 4; ++c) lb[c] ^= 2 * 64 * 128;  // the other buffer
     }
