@@ -3,19 +3,19 @@
 // the per-frame sets (S sets of T tokens), the global set (S*T tokens) and the
 // register set (17*S tokens): a set is just a run of workspace rows.
 //
-// MFMA layout.  Each wave keeps QB*32 queries in registers and per 64-key tile
-// runs two MFMA 32x32x16 fp16 products, both computed transposed so no data
-// moves between lanes:
+// MFMA layout.  Each wave keeps QB*32 queries in registers, as 2*QB blocks
+// of 16, and per 64-key tile runs two MFMA 16x16x32 fp16 products, both
+// computed transposed so no data moves between lanes:
 //   S^T[key, query] = K[key, :] . Q[query, :]            (A = K tile, B = Q)
 //   O^T[feat, query] += V^T[feat, key] . P^T[key, query] (A = V^T tile, B = P)
-// With this orientation lane l holds query column l%32 and, per 32-key block,
-// keys 8*(r/4) + 4*(l/32) + r%4 (r = 0..15).  Eight consecutive accumulator
-// registers then hold exactly the 8 probabilities the lane's B operand needs
-// for a 16-key step, in the order (4h+0..3, 8+4h+0..3) with h = l/32; the QKV
-// kernel stores v^T with that same order inside every aligned group of 16
-// keys (key bits 2 and 3 swapped), so the PV product is exact.  (32x32x16
-// rather than 16x16x32: on gfx950 the smaller MFMA holds the VALU issue port
-// for a larger share of its run time, which the exp2 stream cannot spare.)
+// Lane l holds query column l%16 of each block; the K rows are read in the
+// permuted order given with Rows below, so that the probabilities a lane
+// holds after the softmax are exactly the B operand of its PV step, given
+// v^T's key order (the QKV kernel swaps key bits 2 and 3 inside every aligned
+// group of 16).  16x16x32 rather than 32x32x16: the same work per tile at
+// twice the MFMA issues but half the accumulator traffic per FLOP, which is
+// what counts once random fp16 operands hold the chip at its power limit
+// (measured: 3% faster at 103,100 tokens).
 //
 // Softmax (base 2: q carries log2(e)/sqrt(Dh)): online softmax with a
 // per-query reference m; logits leave the MFMA already shifted (the
@@ -38,17 +38,18 @@
 // workgroup (SGA: the subsampled global set, whose keys are a compact copy of
 // the kept tokens, plus two per-row columns folded in at the end).  Global
 // sets use 8 waves x 64 queries (512 queries share each K/V tile, one
-// workgroup per CU, the -m initialiser kept resident); frame and register
-// sets use 4 waves x 32 queries (small sets, ragged ends).  The partly filled
-// last round of a single-set grid runs as key ranges whose softmax states
-// attn_merge_kernel combines (split tail, below).  Measured
+// workgroup per CU); frame and register sets use 4 waves x 32 queries (small
+// sets, ragged ends).  Every shape runs the same per-row arithmetic, so a row
+// comes out bit for bit the same whichever tile computes it.  The partly
+// filled last round of a single-set grid runs as key ranges whose softmax
+// states attn_merge_kernel combines (split tail, below).  Measured
 // alternatives that did not pay on gfx950: an 8-wave "ping-pong" split (waves
 // sharing a SIMD alternating MFMA and softmax phases between barriers),
-// 16x16x32 MFMAs, direct global->LDS loads three buffers deep (two deep is
-// what the loop uses), and 128
-// queries per wave (spills).  With random fp16 operands this loop is
-// power-bound: the shader clock settles near 1.9 GHz, so lowering the energy
-// per FLOP (LDS bytes, non-MFMA instructions) matters as much as issue slots.
+// direct global->LDS loads three buffers deep (two deep is what the loop
+// uses), and 128 queries per wave (spills).  With random fp16 operands this
+// loop is power-bound: the shader clock settles near 1.9 GHz, so lowering the
+// energy per FLOP (LDS bytes, accumulator traffic, non-MFMA instructions)
+// matters as much as issue slots.
 #include <atomic>
 #include <type_traits>
 
@@ -86,13 +87,14 @@ struct AttnArgs {
   float* part;
 };
 
-// LDS tiles are 64 rows x 128 bytes.  The MFMA operand reads take one
-// 16-byte chunk from each of 32 consecutive rows; XOR-ing the chunk index
-// with row bits 0..2 and bit 3 spreads such a read over all banks (measured
-// on gfx950: 5.2 cycles per ds_read_b128 per CU, against 8.8 with bits 0..2
-// alone).
+// LDS tiles are 64 rows x 128 bytes.  An MFMA operand read takes one 16-byte
+// chunk per lane, 16 lanes at a time: 16 consecutive rows (v^T) or rows
+// {0..7, 16..23} + 8 jj of a 32-row block (K, read in the permuted key order).
+// XOR-ing the chunk index with row bits 0..2, bit 3 and bit 4 spreads either
+// pattern over all banks (measured on gfx950 for consecutive rows: 5.2 cycles
+// per ds_read_b128 per CU, against 8.8 with row bits 0..2 alone).
 __device__ __forceinline__ int lds_slot(int row, int col) {
-  return col ^ (row & 7) ^ ((row >> 3) & 1);  // an involution in col for a fixed row
+  return col ^ (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 4) & 1);  // an involution in col
 }
 __device__ __forceinline__ int lds_swz(int row, int col) { return row * 128 + (lds_slot(row, col) << 4); }
 
@@ -103,38 +105,80 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) 
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// Softmax state of the QB*32 query rows one wave owns (lane: row l%32 of
-// each 32-row block, half h = l/32 of the keys / features).
-template <int QB, bool RES>
+// ---------------------------------------------------------------------------
+// The tile.  Lane l: r = l % 16 (query of a 16-row block; A-row of an operand read),
+// g = l / 16.  S^T blocks are 16 keys x 16 queries, accumulator i of lane l
+// holding A-row 4g + i.  The K rows are read in a permuted order: A-row r of
+// key block kb is key
+//   32 (kb/2) + 16 (r/8) + 8 (kb%2) + 4 ((r/4)%2) + r%4,
+// so accumulator i of block kb holds key 32(kb/2) + 16(g/2) + 8(kb%2) +
+// 4(g%2) + i.  With v^T's key order (bits 2 and 3 swapped in each aligned
+// group of 16), positions 32c + 8g .. +7 -- what lane group g feeds to the
+// 32-key step c of the PV product -- are then exactly the keys of
+// accumulators 0..3 of block 2c followed by those of block 2c + 1.
+// O^T blocks are 16 features x 16 queries: accumulator i of block db holds
+// feature 16 db + 4g + i.
+// ---------------------------------------------------------------------------
+template <int NB>  // 16-row query blocks per wave
 struct Rows {
-  f16x8 qf[QB][4];   // B operand of S^T: q[row][16*dc + 8*h .. +7]
-  float bound[QB];   // upper bound of every logit of the row (-inf: no row)
-  float m[QB];       // reference the logits are taken relative to
-  float l[QB];       // partial row sum (this lane's keys)
-  f32x16 negm[RES ? QB : 1];  // -m broadcast, kept resident when RES (else splat per tile)
-  f32x16 O[2][QB];   // O^T[32*db + 8*(r/4) + 4*h + r%4][row]
-  bool track;        // wave-uniform: some row is not settled yet
+  f16x8 qf[NB][2];  // B operand of S^T: q[row 16 qb + r][32 dc + 8 g .. +7]
+  float bound[NB];  // upper bound of every logit of the row (-inf: no row)
+  float m[NB];      // reference the logits are taken relative to
+  float l[NB];      // partial row sum (this lane's keys)
+  f32x4 negm[NB];   // -m broadcast
+  f32x4 O[4][NB];   // O^T[16 db + 4 g + i][row 16 qb + r]
+  bool track;       // wave-uniform: some row is not settled yet
 };
 
-__device__ __forceinline__ f32x16 splat16(float v) {
-  f32x16 r;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = v;
-  return r;
+__device__ __forceinline__ float max_over_groups16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float sum_over_groups16(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
 }
 
-template <int QB, bool RES>
-__device__ __forceinline__ void rows_init(Rows<QB, RES>& R, const f16* qh, int64_t seq0, int qloc0,
-                                          int L, int j, int h, float kmax) {
+// LDS lane offsets of the operand reads: ka[kb % 2][dc] for K (block kb adds
+// (kb / 2) * 4096), va[db % 2][c] for v^T (block db adds (db / 2) * 4096).
+struct Lanes {
+  int ka[2][2], va[2][2];
+  __device__ __forceinline__ explicit Lanes(int lane) {
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qloc0 + qb * 32 + j;
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc)
+        ka[jj][dc] = lds_swz(16 * (r >> 3) + 8 * jj + 4 * ((r >> 2) & 1) + (r & 3), 4 * dc + g);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) va[par][c] = lds_swz(16 * par + r, 4 * c + g);
+  }
+  __device__ __forceinline__ void flip(int off) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        ka[a][b] ^= off;
+        va[a][b] ^= off;
+      }
+  }
+};
+
+template <int NB>
+__device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t seq0, int qloc0, int L,
+                                          int lane, float kmax) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) {
+    const int row = qloc0 + qb * 16 + r;
     const bool ok = row < L;
     float n2 = 0.f;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
+    for (int dc = 0; dc < 2; ++dc) {
       if (ok) {
-        R.qf[qb][dc] = *reinterpret_cast<const f16x8*>(qh + (seq0 + row) * kDh + dc * 16 + h * 8);
+        R.qf[qb][dc] = *reinterpret_cast<const f16x8*>(qh + (seq0 + row) * kDh + dc * 32 + g * 8);
       } else {
         R.qf[qb][dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
@@ -144,71 +188,60 @@ __device__ __forceinline__ void rows_init(Rows<QB, RES>& R, const f16* qh, int64
         n2 = fmaf(f, f, n2);
       }
     }
-    n2 += __shfl_xor(n2, 32);
+    n2 = sum_over_groups16(n2);
     // 2^-10 relative margin covers the fp32 rounding of norms and dot products.
     R.bound[qb] = ok ? sqrtf(n2) * kmax * (1.f + 0x1p-10f) : -INFINITY;
     R.m[qb] = 0.f;
     R.l[qb] = 0.f;
-    if (RES) R.negm[RES ? qb : 0] = splat16(0.f);
+    R.negm[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 2; ++db) R.O[db][qb] = splat16(0.f);
+    for (int db = 0; db < 4; ++db) R.O[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   R.track = true;
 }
 
-// S^T = K Q^T - m for one 64-key tile in LDS.  MASK: keys at or beyond
-// `valid` (the last tile of a set) start from -inf instead of -m, so their
-// probability is exactly 0.
-// `la` holds this lane's four LDS row offsets lds_swz(j, 2 * c + h) (the
-// 32-row block kb adds kb * 4096: the swizzle only uses row bits 0..3).
-// KB = 1: only keys 0..31 of the tile (a short last tile).
-template <int QB, bool RES, bool MASK, int KB = 2>
-__device__ __forceinline__ void tile_qk(const Rows<QB, RES>& R, const char* Ks, const int (&la)[4],
-                                        int h, int valid, f32x16 (&S)[2][QB]) {
+// One 64-key tile: S^T = K Q^T - m (MASK: keys at or beyond `valid` start from
+// -inf, so their probability is exactly 0); on the first tile, or while a row
+// is unsettled, the row max moves or pins the reference; P = 2^S in fp16 with
+// the row sums; then O^T += V^T P^T.  KB = 2 (a short last tile of at most 32 keys): key
+// blocks 0 and 1 only, which hold keys 0..31, and the first PV step; the
+// other probabilities are exactly zero, so the result is the same bit for bit.
+template <bool MASK, int KB = 4, int NB>
+__device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const char* Ks,
+                                         const char* Vs, int lane, int valid, bool first) {
+  static_assert(KB == 4 || KB == 2, "whole tile or its first 32 keys");
+  constexpr int NC = KB / 2;  // 32-key PV steps
+  const int g = lane >> 4;
+  f32x4 S[KB][NB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    f16x8 kf[4];
+    f16x8 kf[2];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc)
-      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + la[dc] + kb * 4096);
+    for (int dc = 0; dc < 2; ++dc)
+      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + ln.ka[kb & 1][dc] + (kb >> 1) * 4096);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 c = RES ? R.negm[RES ? qb : 0] : splat16(-R.m[qb]);
+    for (int qb = 0; qb < NB; ++qb) {
+      f32x4 c = R.negm[qb];
       if (MASK) {
+        const int key0 = 32 * (kb >> 1) + 16 * (g >> 1) + 8 * (kb & 1) + 4 * (g & 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          c[r] = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= valid ? -INFINITY : c[r];
+        for (int i = 0; i < 4; ++i) c[i] = key0 + i >= valid ? -INFINITY : c[i];
       }
-      S[kb][qb] = mfma32x32x16(kf[0], R.qf[qb][0], c);
-#pragma unroll
-      for (int dc = 1; dc < 4; ++dc) S[kb][qb] = mfma32x32x16(kf[dc], R.qf[qb][dc], S[kb][qb]);
+      S[kb][qb] = mfma16x16x32(kf[0], R.qf[qb][0], c);
+      S[kb][qb] = mfma16x16x32(kf[1], R.qf[qb][1], S[kb][qb]);
     }
   }
-}
-
-
-
-// Softmax of one tile: on the first tile, or while a row is unsettled, take
-// the row max and move / pin the reference; then P = 2^S in fp16 and the row
-// sums.  pf[qb][c] is the B operand of the PV product for keys 16c..16c+15.
-// A short last tile passes KB = 1 (keys 0..31 only) and NC = the number of
-// 16-key groups that hold any valid key: the other probabilities are zero.
-template <int QB, bool RES, int KB = 2, int NC = 4>
-__device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB],
-                                             f16x8 (&pf)[QB][4], bool first) {
   if (first || R.track) {
     bool unsettled = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < NB; ++qb) {
       float mt = S[0][qb][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(S[kb][qb][r], S[kb][qb][r + 1]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));  // row max of this tile, relative to m (m = 0 before the first)
-      // new reference: the observed max (first tile, or a jump past kTau) ...
+        for (int i = 0; i < 4; i += 2) mt = fmaxf(mt, fmaxf(S[kb][qb][i], S[kb][qb][i + 1]));
+      mt = max_over_groups16(mt);  // row max of this tile, relative to m
       float mn = (first || mt > kTau) ? R.m[qb] + mt : R.m[qb];
-      // ... pinned just under the bound once the bound leaves fp16 room.
       const bool settled = mn >= R.bound[qb] - kSettleGap;
       if (settled) mn = fmaxf(mn, R.bound[qb] - kPinBelow);
       unsettled = unsettled || !settled;
@@ -217,101 +250,95 @@ __device__ __forceinline__ void tile_softmax(Rows<QB, RES>& R, f32x16 (&S)[2][QB
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) S[kb][qb][r] -= dl;
-        // O and l are still zero before the first tile: leave them alone
-        // (2^-dl may not even be finite there).
+          for (int i = 0; i < 4; ++i) S[kb][qb][i] -= dl;
         const float al = first ? 1.f : __builtin_amdgcn_exp2f(-dl);
         R.l[qb] *= al;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) R.O[db][qb][r] *= al;
+          for (int i = 0; i < 4; ++i) R.O[db][qb][i] *= al;
       }
       R.m[qb] = mn;
-      if (RES) R.negm[RES ? qb : 0] = splat16(-mn);
+      R.negm[qb] = f32x4{-mn, -mn, -mn, -mn};
     }
     R.track = __ballot(unsettled) != 0;
   }
+  f16x8 pf[NB][2];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       f16x8 v;
 #pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const f32x2 e2 = {__builtin_amdgcn_exp2f(S[c >> 1][qb][8 * (c & 1) + r]),
-                          __builtin_amdgcn_exp2f(S[c >> 1][qb][8 * (c & 1) + r + 1])};
-        const f16x2 h2 = __builtin_convertvector(e2, f16x2);
-        v[r] = h2[0];
-        v[r + 1] = h2[1];
-        R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
-      }
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const f32x2 e2 = {__builtin_amdgcn_exp2f(S[2 * c + half][qb][i]),
+                            __builtin_amdgcn_exp2f(S[2 * c + half][qb][i + 1])};
+          const f16x2 h2 = __builtin_convertvector(e2, f16x2);
+          v[4 * half + i] = h2[0];
+          v[4 * half + i + 1] = h2[1];
+          R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
+        }
       pf[qb][c] = v;
     }
-}
-
-// O^T += V^T P^T for one tile in LDS (the first NC groups of 16 keys).
-template <int QB, bool RES, int NC = 4>
-__device__ __forceinline__ void tile_pv(Rows<QB, RES>& R, const char* Vs, const int (&la)[4],
-                                        const f16x8 (&pf)[QB][4]) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + la[c] + db * 4096);
+    for (int db = 0; db < 4; ++db) {
+      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + ln.va[db & 1][c] + (db >> 1) * 4096);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) R.O[db][qb] = mfma32x32x16(vf, pf[qb][c], R.O[db][qb]);
+      for (int qb = 0; qb < NB; ++qb) R.O[db][qb] = mfma16x16x32(vf, pf[qb][c], R.O[db][qb]);
     }
 }
 
-// Subsampled global set: fold into each row's softmax the two columns the
-// key loop does not hold -- the token's own key / value when the token itself
-// was discarded (a kept token's diagonal is already in the loop), and the
-// mean key / value pair of the discarded tokens, which fills the row's other
-// n_i discarded columns (logit + log2 n_i).  Rescales O and l to the new
-// reference like one more online-softmax step, in fp32.  One query block at a
+// Subsampled global set: fold into each row's softmax the two columns the key
+// loop does not hold -- the token's own key / value when the token itself was
+// discarded (a kept token's diagonal is already in the loop), and the mean key
+// / value pair of the discarded tokens, which stands for the row's other n_i
+// discarded columns (logit + log2 n_i).  Rescales O and l to the new reference
+// like one more online-softmax step, in fp32.  One query block (QBI) at a
 // time, loads issued before the arithmetic that uses them.
-template <int QB, bool RES, int QBI>
-__device__ __forceinline__ void sga_block(Rows<QB, RES>& R, const AttnArgs& p, int hd, int qloc0,
-                                          int j, int h) {
-  const int row = qloc0 + QBI * 32 + j;  // = token index: one set, identity row map
-  if (row >= p.L) return;                // lanes j and j + 32 leave together
+template <int QBI, int NB>
+__device__ __forceinline__ void sga_block(Rows<NB>& R, const AttnArgs& p, int hd, int qloc0, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int row = qloc0 + QBI * 16 + r;  // = token index: one set, identity row map
+  if (row >= p.L) return;                // the row's four lane groups leave together
   const int t = row % p.T;
   bool kept = true;
   if (t >= kSpecial) {
-    const int pidx = t - kSpecial, r = pidx / p.gw, c = pidx - r * p.gw;
-    kept = (r % p.sub_h) == 0 && (c % p.sub_w) == 0;
+    const int pidx = t - kSpecial, pr = pidx / p.gw, pc = pidx - pr * p.gw;
+    kept = (pr % p.sub_h) == 0 && (pc % p.sub_w) == 0;
   }
   const float* sk = p.sums + hd * 128;
   const float* sv = sk + 64;
-  // this lane's 32 features of the token's own key (q layout) and value (O layout)
-  f16x8 kd[4];
-  f16 vd[2][16];
+  // this lane's 16 features of the token's own key (q layout) and value (O layout)
+  f16x8 kd[2];
+  f16 vd[4][4];
   if (!kept) {
-    const f16* krow = p.k_all + ((int64_t)hd * p.rows + row) * kDh + h * 8;
+    const f16* krow = p.k_all + ((int64_t)hd * p.rows + row) * kDh + g * 8;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) kd[dc] = *reinterpret_cast<const f16x8*>(krow + dc * 16);
+    for (int dc = 0; dc < 2; ++dc) kd[dc] = *reinterpret_cast<const f16x8*>(krow + dc * 32);
     const int64_t slot = ((int64_t)row & ~(int64_t)15) | (((row >> 2) & 1) << 3) |
                          (((row >> 3) & 1) << 2) | (row & 3);
-    const f16* vcol = p.vt_all + ((int64_t)hd * kDh + 4 * h) * p.rows + slot;
+    const f16* vcol = p.vt_all + ((int64_t)hd * kDh + 4 * g) * p.rows + slot;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        vd[db][r] = vcol[(int64_t)(db * 32 + 8 * (r >> 2) + (r & 3)) * p.rows];
+      for (int i = 0; i < 4; ++i) vd[db][i] = vcol[(int64_t)(db * 16 + i) * p.rows];
   } else {
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) kd[dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int dc = 0; dc < 2; ++dc) kd[dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) vd[db][r] = (f16)0.f;
+      for (int i = 0; i < 4; ++i) vd[db][i] = (f16)0.f;
   }
   float sd = 0.f, sm = 0.f;
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc) {
-    const f32x4 k0 = *reinterpret_cast<const f32x4*>(sk + dc * 16 + h * 8);
-    const f32x4 k1 = *reinterpret_cast<const f32x4*>(sk + dc * 16 + h * 8 + 4);
+  for (int dc = 0; dc < 2; ++dc) {
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(sk + dc * 32 + g * 8);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(sk + dc * 32 + g * 8 + 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float qv = (float)R.qf[QBI][dc][e];
@@ -319,8 +346,8 @@ __device__ __forceinline__ void sga_block(Rows<QB, RES>& R, const AttnArgs& p, i
       sm = fmaf(qv, e < 4 ? k0[e & 3] : k1[e & 3], sm);
     }
   }
-  sd += __shfl_xor(sd, 32);
-  sm += __shfl_xor(sm, 32);
+  sd = sum_over_groups16(sd);
+  sm = sum_over_groups16(sm);
   const float inv = p.nD > 0 ? 1.f / (float)p.nD : 0.f;
   const int n = p.nD - (kept ? 0 : 1);
   const float s_d = kept ? -INFINITY : sd;
@@ -328,73 +355,64 @@ __device__ __forceinline__ void sga_block(Rows<QB, RES>& R, const AttnArgs& p, i
   const float mn = fmaxf(R.m[QBI], fmaxf(s_d, s_m));
   const float al = __builtin_amdgcn_exp2f(R.m[QBI] - mn);
   const float pd = __builtin_amdgcn_exp2f(s_d - mn), pm = __builtin_amdgcn_exp2f(s_m - mn);
-  R.l[QBI] = R.l[QBI] * al + (h == 0 ? pd + pm : 0.f);
+  R.l[QBI] = R.l[QBI] * al + (g == 0 ? pd + pm : 0.f);
   const float pmi = pm * inv;
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < 4; ++db) {
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(sv + db * 16 + 4 * g);
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const f32x4 vb = *reinterpret_cast<const f32x4*>(sv + db * 32 + 8 * rq + 4 * h);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int r = 4 * rq + r4;
-        R.O[db][QBI][r] = fmaf(R.O[db][QBI][r], al, fmaf(pd, (float)vd[db][r], pmi * vb[r4]));
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      R.O[db][QBI][i] = fmaf(R.O[db][QBI][i], al, fmaf(pd, (float)vd[db][i], pmi * vb[i]));
+  }
   R.m[QBI] = mn;
 }
 
-template <int QB, bool RES>
-__device__ __forceinline__ void sga_columns(Rows<QB, RES>& R, const AttnArgs& p, int hd,
-                                            int qloc0, int j, int h) {
-  sga_block<QB, RES, 0>(R, p, hd, qloc0, j, h);
-  if constexpr (QB > 1) {
+template <int NB>
+__device__ __forceinline__ void sga_columns(Rows<NB>& R, const AttnArgs& p, int hd, int qloc0,
+                                            int lane) {
+  sga_block<0>(R, p, hd, qloc0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  sga_block<1>(R, p, hd, qloc0, lane);
+  if constexpr (NB == 4) {
     __builtin_amdgcn_sched_barrier(0);
-    sga_block<QB, RES, 1>(R, p, hd, qloc0, j, h);
+    sga_block<2>(R, p, hd, qloc0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    sga_block<3>(R, p, hd, qloc0, lane);
   }
 }
 
-// Normalise and store O in place of q, valid rows only.
-template <int QB, bool RES>
-__device__ __forceinline__ void rows_store(const Rows<QB, RES>& R, f16* qh, int64_t seq0, int qloc0,
-                                           int L, int j, int h) {
+template <int NB>
+__device__ __forceinline__ void rows_store(const Rows<NB>& R, f16* qh, int64_t seq0, int qloc0, int L,
+                                           int lane) {
+  const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = R.l[qb] + __shfl_xor(R.l[qb], 32);
-    const float inv = 1.f / lt;
-    const int row = qloc0 + qb * 32 + j;
+  for (int qb = 0; qb < NB; ++qb) {
+    const float inv = 1.f / sum_over_groups16(R.l[qb]);
+    const int row = qloc0 + qb * 16 + r;
     if (row < L) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 4; ++db) {
+        f16x4 o;
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          f16x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (f16)(R.O[db][qb][4 * rq + r] * inv);
-          *reinterpret_cast<f16x4*>(qh + (seq0 + row) * kDh + db * 32 + 8 * rq + 4 * h) = o;
-        }
+        for (int i = 0; i < 4; ++i) o[i] = (f16)(R.O[db][qb][i] * inv);
+        *reinterpret_cast<f16x4*>(qh + (seq0 + row) * kDh + db * 16 + 4 * g) = o;
+      }
     }
   }
 }
 
-// Unnormalised state of a key range (split tail): O in fp32, the reference
-// m and the row sum l, for the merge kernel.
-template <int QB, bool RES>
-__device__ __forceinline__ void rows_store_partial(const Rows<QB, RES>& R, float* po, float2* pml,
-                                                   int lrow0, int j, int h) {
+template <int NB>
+__device__ __forceinline__ void rows_store_partial(const Rows<NB>& R, float* po, float2* pml, int lrow0,
+                                                   int lane) {
+  const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = R.l[qb] + __shfl_xor(R.l[qb], 32);
-    const int lr = lrow0 + qb * 32 + j;
+  for (int qb = 0; qb < NB; ++qb) {
+    const float lt = sum_over_groups16(R.l[qb]);
+    const int lr = lrow0 + qb * 16 + r;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const f32x4 o = {R.O[db][qb][4 * rq], R.O[db][qb][4 * rq + 1], R.O[db][qb][4 * rq + 2],
-                         R.O[db][qb][4 * rq + 3]};
-        *reinterpret_cast<f32x4*>(po + lr * kDh + db * 32 + 8 * rq + 4 * h) = o;
-      }
-    if (h == 0) pml[lr] = make_float2(R.m[qb], lt);
+    for (int db = 0; db < 4; ++db)
+      *reinterpret_cast<f32x4*>(po + lr * kDh + db * 16 + 4 * g) = R.O[db][qb];
+    if (g == 0) pml[lr] = make_float2(R.m[qb], lt);
   }
 }
 
@@ -467,7 +485,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 31, h = lane >> 5;
 
   // single-set grids may have a split tail
   constexpr bool kSplit = true;
@@ -482,12 +499,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
 
-  // The -m accumulator initialiser stays resident where the registers allow
-  // it (8-wave tiles, and one query block per wave); otherwise it is
-  // re-splatted before each QK chain.
-  constexpr bool RES = NW == 8 || QB == 1;
-  Rows<QB, RES> R;
-  rows_init(R, qh, seq0, qloc0, L, j, h, p.sc->kmax[bc.h]);
+  // the wave's QB * 32 queries as 2 QB blocks of 16 (16x16x32 tile)
+  using LanesT = Lanes;
+  Rows<2 * QB> R;
+  rows_init(R, qh, seq0, qloc0, L, lane, p.sc->kmax[bc.h]);
 
   // key tiles [t0, t1): all of them, or one key range of a split workgroup
   // (only the range that ends the set has a masked last tile)
@@ -527,11 +542,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     __syncthreads();
   };
 
-  f32x16 S[2][QB];
-  f16x8 pf[QB][4];
-  int la[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) la[c] = lds_swz(j, 2 * c + h);
+  const LanesT ln(lane);
   // One tile from LDS buffer BUF while the next tile moves into BUF ^ 1.  The
   // loop is unrolled by two so that BUF is a constant and every LDS address
   // is a lane offset plus an immediate; a scheduling barrier keeps the two
@@ -539,11 +550,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   auto step = [&](auto buf_c, int t) {
     constexpr int BUF = decltype(buf_c)::value;
     issue(t + 1, BUF ^ 1);
-    if (active) {
-      tile_qk<QB, RES, false>(R, smem[BUF][0], la, h, 64, S);
-      tile_softmax(R, S, pf, t == t0);
-      tile_pv(R, smem[BUF][1], la, pf);
-    }
+    if (active) tile_run<false>(R, ln, smem[BUF][0], smem[BUF][1], lane, 64, t == t0);
     land();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -565,55 +572,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     // 4-wave tiles keep the rolled loop (unrolled, the extra registers cost
     // a wave of occupancy); the lane offsets carry the buffer bit instead,
     // flipped once per tile.
-    int lb[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) lb[c] = la[c];
+    LanesT lb = ln;
     for (; t < t1 - 1; ++t) {
       issue(t + 1, ((t - t0) & 1) ^ 1);
-      if (active) {
-        tile_qk<QB, RES, false>(R, smem[0][0], lb, h, 64, S);
-        tile_softmax(R, S, pf, t == t0);
-        tile_pv(R, smem[0][1], lb, pf);
-      }
+      if (active) tile_run<false>(R, lb, smem[0][0], smem[0][1], lane, 64, t == t0);
       land();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lb[c] ^= 2 * 64 * 128;  // the other buffer
+      lb.flip(2 * 64 * 128);  // the other buffer
     }
   }
   // last tile of the range (t = t1 - 1): keys past the end of the set masked.  Small
-  // sets (4-wave tiles, one query block per wave: frames, register sets)
-  // often end in a short tile -- 7 of 64 keys for a 26 x 39 frame -- whose
-  // empty 32- and 16-key groups are skipped (their probabilities are exactly
-  // zero, so the result is the same bit for bit).
+  // sets (4-wave tiles: frames, register sets) often end in a short tile --
+  // 7 of 64 keys for a 26 x 39 frame -- whose second half is skipped (its
+  // probabilities are exactly zero, so the result is the same bit for bit).
   if (active) {
-    int lb[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) lb[c] = la[c] ^ (((t - t0) & 1) * 2 * 64 * 128);
+    LanesT lb = ln;
+    lb.flip(((t - t0) & 1) * 2 * 64 * 128);
     const bool first = t1 - t0 == 1;
-    if (NW == 4 && QB == 1 && last_valid <= 16) {
-      tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax<QB, RES, 1, 1>(R, S, pf, first);
-      tile_pv<QB, RES, 1>(R, smem[0][1], lb, pf);
-    } else if (NW == 4 && QB == 1 && last_valid <= 32) {
-      tile_qk<QB, RES, true, 1>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax<QB, RES, 1, 2>(R, S, pf, first);
-      tile_pv<QB, RES, 2>(R, smem[0][1], lb, pf);
+    if (NW == 4 && last_valid <= 32) {
+      tile_run<true, 2>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first);
     } else {
-      tile_qk<QB, RES, true>(R, smem[0][0], lb, h, last_valid, S);
-      tile_softmax(R, S, pf, first);
-      tile_pv(R, smem[0][1], lb, pf);
+      tile_run<true>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first);
     }
   }
   // the diagonal and mean columns enter once per row: in its last key range
-  if (SGA && active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, j, h);
+  if (SGA && active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, lane);
   if (kSplit && bc.unit >= 0) {
     // a key range of a split workgroup: unnormalised state for the merge
     float* po = p.part + (int64_t)bc.unit * BQ * kDh;
     float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)kXcds * p.umax * BQ * kDh) +
                   (int64_t)bc.unit * BQ;
-    if (active) rows_store_partial(R, po, pml, wave * QB * 32, j, h);
+    if (active) rows_store_partial(R, po, pml, wave * QB * 32, lane);
   } else if (active) {
-    rows_store(R, qh, seq0, qloc0, L, j, h);
+    rows_store(R, qh, seq0, qloc0, L, lane);
   }
 }
 
