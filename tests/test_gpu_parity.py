@@ -69,6 +69,12 @@ RAGGED = [
     configs.custom("patchless", 1, 0, 0, 128, 2, cid=13),  # T = 17: specials only
     configs.custom("onerow", 5, 1, 1, 128, 2, cid=14),     # T = 18: 1x1 grid
     configs.custom("wide", 4, 9, 30, 128, 2, cid=15),      # T = 287, N = 1148
+    # last key tile of a frame at the edges of the short-tile path (at most 32
+    # valid keys: only the tile's first half runs)
+    configs.custom("edge32", 2, 1, 79, 128, 2, cid=16),    # T = 96: 32-key tail (short path)
+    configs.custom("edge33", 2, 8, 10, 128, 2, cid=17),    # T = 97: 33-key tail (whole tile)
+    configs.custom("edge64", 2, 1, 47, 128, 2, cid=18),    # T = 64: no tail
+    configs.custom("edge65", 2, 6, 8, 128, 2, cid=19),     # T = 65: 1-key tail
 ]
 
 
