@@ -125,8 +125,9 @@ def test_split_query_window(monkeypatch):
 
 
 def test_split_register_s500(monkeypatch):
-    """The 8,500-row register set of 500 frames on 4-wave workgroups (1,072 of
-    them): split as planned against the unsplit kernel and the oracle."""
+    """The 8,500-row register set of 500 frames on 4-wave workgroups of 64
+    queries per wave (544 of them): split as planned against the unsplit
+    kernel and the oracle."""
     w = configs.WORKLOADS["s500"]
     inp = synth.make_inputs(w)
     d = to_dev(inp)

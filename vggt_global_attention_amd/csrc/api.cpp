@@ -164,6 +164,14 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->attn_qb = 1;
     p->attn_waves = 4;
   }
+  // Register sets (one set of 17 S rows) take 64 queries per wave on 4-wave
+  // workgroups while that grid still has a workgroup per CU (measured at
+  // S = 500, 8,500 rows: 0.29 against 0.32 ms with 32 queries per wave, and
+  // 0.30 ms on 8-wave workgroups); smaller sets keep 32 queries per wave for
+  // the workgroup count.
+  if (mode == VGGT_ATTN_MODE_REGISTER && !tile_forced && (R + 255) / 256 * s->H >= 256) {
+    p->attn_qb = 2;
+  }
   p->rope_npos = (s->grid_h > s->grid_w ? s->grid_h : s->grid_w) + s->pos_offset;
   if (p->rope_npos < 1) p->rope_npos = 1;
 
