@@ -50,8 +50,14 @@
  *     workspace, with one exception: vggt_attn_global_register accepts Y == X
  *     (in place), and then writes only the 17*S special rows.
  *   - Errors: every argument is checked before anything is enqueued; on a
- *     nonzero return nothing was launched and Y is untouched.  Non-finite
- *     values inside X or the weights are not checked and propagate to Y.
+ *     nonzero return nothing was launched and Y is untouched.  Value ranges
+ *     are checked on the device, without a host synchronisation: the call's
+ *     first stage writes VGGT_ATTN_RANGE_* bits into the workspace's status
+ *     word when an input holds a non-finite value, when a QK-norm affine
+ *     could overflow fp16 q / k, or when a bound is beyond what the call's
+ *     power-of-two pre-scales bring into fp16 range (the cases in which Y
+ *     may hold inf or NaN).  The kernels still run; read the word with
+ *     vggt_attn_range_status() after the call, which reports ERANGE.
  */
 #ifndef LIBVGGTATTN_H
 #define LIBVGGTATTN_H
@@ -72,7 +78,21 @@ extern "C" {
 #define VGGT_ATTN_EHIP       (-5) /* the HIP runtime rejected a launch */
 #define VGGT_ATTN_ERANGE     (-6) /* rope_base / ln_eps not finite and positive, pos_offset out of
                                      range, subsampling window < 1, row window outside the set,
-                                     descriptor count outside the cache */
+                                     descriptor count outside the cache; from
+                                     vggt_attn_range_status: a value range bit is set */
+
+/* Value range bits, found on the device by a call's first stage and kept in
+   the 32-bit status word at byte VGGT_ATTN_STATUS_OFFSET of its workspace. */
+#define VGGT_ATTN_STATUS_OFFSET 16
+#define VGGT_ATTN_RANGE_X      1u  /* an X row (or appended descriptor) holds a non-finite
+                                      value, or its squared norm overflows fp32 */
+#define VGGT_ATTN_RANGE_WQKV   2u  /* Wqkv holds a non-finite value */
+#define VGGT_ATTN_RANGE_WO     4u  /* Wo holds a non-finite value */
+#define VGGT_ATTN_RANGE_AFFINE 8u  /* a q / k gamma or beta is non-finite, or 8|gamma| + |beta|
+                                      >= 2^15 (a LayerNorm-ed q / k could leave fp16) */
+#define VGGT_ATTN_RANGE_SCALE 16u  /* max||x|| max||w_v|| or max|Wo| needs a power-of-two
+                                      scale beyond 2^+-60 to reach fp16 range, or the output
+                                      bound d max||x|| max||w_v|| max|Wo| reaches 3e38 */
 
 /* Block modes. */
 #define VGGT_ATTN_MODE_FRAME    0
@@ -156,8 +176,8 @@ int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int
    vggt_attn_workspace_bytes(VGGT_ATTN_MODE_GLOBAL).  The rows equal those
    vggt_attn_global writes for them up to the fp32 summation order of the
    query blocks that either call runs as split key ranges (the partly filled
-   last round of workgroups on the device); with the environment variable
-   VGGT_ATTN_SPLIT=1 (no split) they are bitwise equal. */
+   last round of workgroups on the device); with the split off (tuning build,
+   VGGT_ATTN_SPLIT=1) they are bitwise equal. */
 int vggt_attn_global_rows(const vggt_attn_shape* shape, int64_t row_begin, int64_t row_count,
                           const void* X, const void* Wqkv, const void* Wo, const float* q_gamma,
                           const float* q_beta, const float* k_gamma, const float* k_beta,
@@ -317,6 +337,19 @@ size_t vggt_attn_schedule_workspace_bytes(const vggt_attn_shape* shape,
 int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedule* sched,
                            const vggt_attn_block_weights* blocks, const void* X, void* state,
                            void* caches, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Value range check of the last call that used `workspace` (any block call
+   or stage sequence above, including descriptor attention, or a whole
+   vggt_attn_schedule_run, whose blocks OR their bits together).  The call's
+   first stage wrote the VGGT_ATTN_RANGE_* bits into the status word at byte
+   VGGT_ATTN_STATUS_OFFSET of the workspace without any host
+   synchronisation.  This function enqueues a 4-byte device-to-host copy of
+   that word on `stream` (the call's stream), waits for the stream, stores the
+   bits in *bits (when bits is not NULL) and returns VGGT_ATTN_OK if none is
+   set, VGGT_ATTN_ERANGE if any is.  EINVAL for a null or misaligned
+   workspace, EHIP if the copy fails.  It synchronises, so it does not belong
+   inside a graph capture; a caller can instead copy the word itself. */
+int vggt_attn_range_status(const void* workspace, uint32_t* bits, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* vggt_attn_status_str(int status);

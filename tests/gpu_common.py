@@ -3,6 +3,7 @@ run the library through its C ABI (via the torch front end)."""
 
 from __future__ import annotations
 
+import contextlib
 import sys
 
 import numpy as np
@@ -39,3 +40,17 @@ def run(mode: str, w, d: dict, X=None, Y=None, **shape_kw) -> torch.Tensor:
 
 def np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+@contextlib.contextmanager
+def tuned(monkeypatch, **knobs):
+    """Run the block through the tuning build with the given overrides set
+    (e.g. VGGT_ATTN_SPLIT=1); the product library reads no environment."""
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, str(v))
+    try:
+        with B.tuning_build():
+            yield
+    finally:
+        for k in knobs:
+            monkeypatch.delenv(k, raising=False)

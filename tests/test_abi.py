@@ -34,6 +34,45 @@ def test_library_exports_every_header_symbol():
     assert set(header_functions()) == set(B.EXPORTS)
 
 
+def _dynamic_imports(path):
+    """Undefined dynamic symbols of a library built here (nm -D -u)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "-u", path], capture_output=True, text=True, check=True)
+    return {line.split()[-1].split("@")[0] for line in out.stdout.splitlines() if line.strip()}
+
+
+def test_product_library_reads_no_environment():
+    """Tile, split and GEMM choices depend on the shape and device only: the
+    product library imports no getenv; the tuning build (overrides for sweeps
+    and tests) does, and exports the same entry points."""
+    from vggt_global_attention_amd.build import LIB, TUNE_LIB
+    assert "getenv" not in _dynamic_imports(LIB)
+    assert "getenv" in _dynamic_imports(TUNE_LIB)
+    import ctypes
+    T = ctypes.CDLL(TUNE_LIB)
+    for name in header_functions():
+        assert hasattr(T, name), name
+
+
+def test_range_status_argument_errors():
+    """vggt_attn_range_status checks its workspace pointer before any HIP call."""
+    assert B.vggt_attn_range_status(None, None)[0] == B.EINVAL
+    assert B.vggt_attn_range_status(0x10000010, None)[0] == B.EINVAL  # not 256-byte aligned
+
+
+def test_status_word_offset_matches_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define VGGT_ATTN_STATUS_OFFSET (\d+)", txt)
+    assert m and int(m.group(1)) == B.STATUS_OFFSET
+    for name, val in (("X", 1), ("WQKV", 2), ("WO", 4), ("AFFINE", 8), ("SCALE", 16)):
+        m = re.search(rf"#define VGGT_ATTN_RANGE_{name}\s+(\d+)u", txt)
+        assert m and int(m.group(1)) == val == getattr(B, f"RANGE_{name}")
+
+
 def shape(**kw):
     base = dict(S=100, T=1031, d=1024, H=16, grid_h=26, grid_w=39)
     base.update(kw)
@@ -385,3 +424,4 @@ def test_descriptor_attend_errors():
     a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
     assert B.vggt_attn_stage(B.MODE_DESCRIPTOR, B.STAGE_CORE, s, *a, 0x10000000, 1 << 30,
                              None) == B.EINVAL
+

@@ -12,7 +12,7 @@ import oracle
 from vggt_global_attention_amd import api, configs, synth
 from vggt_global_attention_amd import binding as B
 from helpers import assert_parity, f64, oracle_params
-from gpu_common import log, np64, require_gpu, run, to_dev
+from gpu_common import log, np64, require_gpu, run, to_dev, tuned
 
 pytestmark = pytest.mark.gpu
 
@@ -35,18 +35,18 @@ def rows_call(w, d, begin, count):
 def test_rows_bitwise_equal_global(name, monkeypatch):
     # with the split attention tail off: a window splits other workgroups
     # than the full call, which changes the rounding of those rows
-    monkeypatch.setenv("VGGT_ATTN_SPLIT", "1")
     w = W[name]
     d = to_dev(synth.make_inputs(w))
-    full = run("global", w, d).reshape(-1, w.d)
-    N = w.N
-    windows = [(0, N), (0, (N + 7) // 8), (N // 3, 1), (N - 100, 100), (17, min(513, N - 17)),
-               (N // 2, N // 4)]
-    for begin, count in windows:
-        log(f"[case] {name} rows [{begin}, {begin + count})")
-        y = rows_call(w, d, begin, count)
-        assert y.shape == (count, w.d)
-        assert torch.equal(y, full[begin:begin + count]), (begin, count)
+    with tuned(monkeypatch, VGGT_ATTN_SPLIT=1):
+        full = run("global", w, d).reshape(-1, w.d)
+        N = w.N
+        windows = [(0, N), (0, (N + 7) // 8), (N // 3, 1), (N - 100, 100),
+                   (17, min(513, N - 17)), (N // 2, N // 4)]
+        for begin, count in windows:
+            log(f"[case] {name} rows [{begin}, {begin + count})")
+            y = rows_call(w, d, begin, count)
+            assert y.shape == (count, w.d)
+            assert torch.equal(y, full[begin:begin + count]), (begin, count)
 
 
 def test_rows_s100_share_oracle_and_bitwise(monkeypatch):
@@ -60,9 +60,9 @@ def test_rows_s100_share_oracle_and_bitwise(monkeypatch):
     begin = 3 * share
     log(f"[case] s100 rows [{begin}, {begin + share})")
     y = rows_call(w, d, begin, share)
-    monkeypatch.setenv("VGGT_ATTN_SPLIT", "1")
-    y1 = rows_call(w, d, begin, share)
-    full = run("global", w, d).reshape(-1, w.d)
+    with tuned(monkeypatch, VGGT_ATTN_SPLIT=1):
+        y1 = rows_call(w, d, begin, share)
+        full = run("global", w, d).reshape(-1, w.d)
     assert torch.equal(y1, full[begin:begin + share])
     rows = np.sort(np.random.default_rng(7).choice(share, 96, replace=False)) + begin
     ref = oracle.global_attention_rows(f64(inp["X"]), oracle_params(w, inp), rows)

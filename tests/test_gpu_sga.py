@@ -15,7 +15,7 @@ import torch
 import oracle
 from vggt_global_attention_amd import configs, synth
 from helpers import assert_parity, f64, oracle_params
-from gpu_common import log, np64, require_gpu, run, to_dev
+from gpu_common import log, np64, require_gpu, run, to_dev, tuned
 from test_gpu_parity import RAGGED, uniform_inputs
 
 pytestmark = pytest.mark.gpu
@@ -88,10 +88,10 @@ def test_sga_1x1_equals_global_bitwise(monkeypatch):
     """Nothing discarded: the compact keys are the full keys in the same order
     and no column is added, so the result is the global block bit for bit
     (the global call with its split tail off: the subsampled grid has none)."""
-    monkeypatch.setenv("VGGT_ATTN_SPLIT", "1")
     w = W["s24"]
     d = to_dev(synth.make_inputs(w))
-    assert torch.equal(run("subsampled", w, d, sub=(1, 1)), run("global", w, d))
+    with tuned(monkeypatch, VGGT_ATTN_SPLIT=1):
+        assert torch.equal(run("subsampled", w, d, sub=(1, 1)), run("global", w, d))
 
 
 def test_sga_deterministic_and_stages():

@@ -8,7 +8,7 @@ the ranges' softmax states.
 What is checked:
 - split results match the fp64 oracle at the block bar;
 - they stay within a few fp16 roundings of O of the unsplit kernel
-  (VGGT_ATTN_SPLIT = 1);
+  (VGGT_ATTN_SPLIT = 1, through the tuning build);
 - splitting every workgroup, forced splits, query windows and the 4-wave
   register grid are exercised.
 """
@@ -22,7 +22,7 @@ import torch
 import oracle
 from vggt_global_attention_amd import api, configs, synth
 from helpers import assert_parity, f64, metrics, oracle_params
-from gpu_common import log, np64, require_gpu, run, to_dev
+from gpu_common import log, np64, require_gpu, run, to_dev, tuned
 
 pytestmark = pytest.mark.gpu
 
@@ -40,11 +40,8 @@ def cus():
 
 
 def with_split(monkeypatch, ways, fn):
-    monkeypatch.setenv("VGGT_ATTN_SPLIT", str(ways))
-    try:
+    with tuned(monkeypatch, VGGT_ATTN_SPLIT=ways):
         return fn()
-    finally:
-        monkeypatch.delenv("VGGT_ATTN_SPLIT")
 
 
 def tail_rows(w, qtiles_per_head, n_tail, bq=512, count=64, seed=0):
@@ -79,11 +76,11 @@ def test_split_every_workgroup(monkeypatch):
     """Three frames on the 8-wave tile (forced: a grid this small picks the
     4-wave one): 112 workgroups, fewer than the CUs, so the plan splits all
     of them (no whole workgroup); full oracle."""
-    monkeypatch.setenv("VGGT_ATTN_WAVES", "8")
     w = configs.custom("split3", 3, 26, 39, 1024, 16, cid=23)
     inp = synth.make_inputs(w)
     d = to_dev(inp)
-    y = run("global", w, d)
+    with tuned(monkeypatch, VGGT_ATTN_WAVES=8):
+        y = run("global", w, d)
     ref = oracle.global_attention(f64(inp["X"]), oracle_params(w, inp), threads=8)
     assert_parity(np64(y), ref, "3 frames, all split")
 

@@ -84,3 +84,122 @@ def test_library_design_fits_the_bar(case):
     assert design < 2e-3 and design < 1.25 * only_y, (design, only_y)
     # ... while a plain bf16 pipeline does not fit.
     assert plain_bf16 > 2e-3, plain_bf16
+
+
+# ----------------------------------------------------------------------------
+# The attention kernel's softmax reference rule, emulated on the CPU
+# ----------------------------------------------------------------------------
+# The kernel takes logits in base 2 (q carries log2(e)/sqrt(Dh)) relative to a
+# per-row reference m and rounds P = 2^(s - m) to fp16.  It knows an upper
+# bound of every logit of a row before the first 64-key tile: |q| * max|k|
+# (Cauchy-Schwarz), times 1 + 2^-10.  After the first tile a row whose max m0
+# satisfies bound - m0 <= SETTLE_GAP is "settled": its reference is pinned at
+# max(m0, bound - PIN_BELOW) and never moves again (no logit can push P past
+# 2^PIN_BELOW).  Other rows keep an online max -- the exact running max over
+# the first EAGER_TILES tiles, later lazy rescaling (only when a tile's max
+# exceeds m + TAU) -- and re-check the settle condition per tile.  The pinned
+# reference can sit up to SETTLE_GAP - PIN_BELOW above the row's true max,
+# which pushes the row's probabilities toward fp16's subnormal range.
+TAU, PIN_BELOW, SETTLE_GAP, EAGER_TILES = 8.0, 15.0, 19.0, 16
+LOG2E = 1.0 / math.log(2.0)
+
+
+def _ln(x, g, b):
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + 1e-5) * g + b
+
+
+def kernel_softmax_core(q, k, v, settle_gap=SETTLE_GAP, tile=64):
+    """Emulated attention core of one head: q [R,64] (scaled, fp16 values),
+    k, v [N,64] (fp16 values).  Returns (O rounded to fp16, settled flags)."""
+    R, N = q.shape[0], k.shape[0]
+    kmax = np.sqrt((k * k).sum(1)).max()
+    bound = np.sqrt((q * q).sum(1)) * kmax * (1 + 2.0 ** -10)
+    m = np.zeros(R)
+    l = np.zeros(R)
+    O = np.zeros((R, q.shape[1]))
+    settled = np.zeros(R, bool)
+    for t0 in range(0, N, tile):
+        s = q @ k[t0:t0 + tile].T - m[:, None]
+        first = t0 == 0
+        track = first | ~settled  # per row (the kernel tracks per wave: never less precise)
+        mt = s.max(1)
+        lazy = 0.0 if t0 < EAGER_TILES * tile else TAU
+        mn = np.where(first | (mt > lazy), m + mt, m)
+        ok = mn >= bound - settle_gap
+        mn = np.where(ok, np.maximum(mn, bound - PIN_BELOW), mn)
+        mn = np.where(track, mn, m)
+        settled |= track & ok
+        dl = mn - m
+        s -= dl[:, None]
+        if not first:
+            al = np.exp2(-dl)
+            l *= al
+            O *= al[:, None]
+        m = mn
+        P = fp16(np.exp2(s))
+        l += P.sum(1)
+        O += P @ v[t0:t0 + tile]
+    return fp16(O / l[:, None]), settled
+
+
+def _exact_core(q, k, v):
+    s = q @ k.T
+    P = np.exp2(s - s.max(1, keepdims=True))
+    return (P @ v) / P.sum(1, keepdims=True)
+
+
+def _head(seed, R, N, gamma=None, recipe=False):
+    """One head's fp16 q (scaled), k, v: LayerNorm-ed random vectors with a
+    uniform gain `gamma` and no shift, or the synthetic workloads' affine
+    recipe (gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1) per feature)."""
+    rng = np.random.default_rng(seed)
+    if recipe:
+        sd = math.sqrt(0.1)
+        gq, bq = 1 + sd * rng.standard_normal(64), sd * rng.standard_normal(64)
+        gk, bk = 1 + sd * rng.standard_normal(64), sd * rng.standard_normal(64)
+    else:
+        gq = gk = np.full(64, gamma)
+        bq = bk = np.zeros(64)
+    q = fp16(_ln(rng.standard_normal((R, 64)), gq, bq) * (LOG2E / 8))
+    k = fp16(_ln(rng.standard_normal((N, 64)), gk, bk))
+    v = fp16(rng.standard_normal((N, 64)))
+    return q, k, v
+
+
+def _row_rel(o, ref):
+    return np.abs(o - ref).sum(1) / np.abs(ref).sum(1)
+
+
+@pytest.mark.parametrize("gamma", [1.0, 1.9, 2.0, 2.05, 2.2])
+def test_settle_rule_keeps_rows_precise_at_large_qk_gain(gamma):
+    """A uniform QK-norm gain near 2 makes the logit bound loose enough that
+    first-tile rows settle with a lifted reference; every row's attention
+    output must still stay within fp16 round-off of the exact softmax (the
+    online-max path measures <= 4.6e-4 per row here)."""
+    q, k, v = _head(100 + int(gamma * 100), R=256, N=24744, gamma=gamma)
+    o, _ = kernel_softmax_core(q, k, v)
+    worst = _row_rel(o, _exact_core(q, k, v)).max()
+    assert worst < 1e-3, (gamma, worst)
+
+
+def test_wider_settle_gap_is_caught():
+    """Planted mistake: the earlier gap of 29 (reference up to 14 above the row
+    max) breaks the per-row bound at a gain of 2.05, so the check above has
+    teeth."""
+    q, k, v = _head(305, R=256, N=24744, gamma=2.05)
+    o, _ = kernel_softmax_core(q, k, v, settle_gap=29.0)
+    worst = _row_rel(o, _exact_core(q, k, v)).max()
+    assert worst > 2e-3, worst
+
+
+def test_synthetic_recipe_rows_settle_early():
+    """With the workloads' QK-norm affine every row has settled after the
+    eager tiles, so the measured kernel runs the cheap path (no per-tile row
+    max) for the rest of the key loop."""
+    q, k, v = _head(7, R=1024, N=24744, recipe=True)
+    o, settled = kernel_softmax_core(q, k, v, tile=64)
+    _, settled_early = kernel_softmax_core(q, k[:64 * EAGER_TILES], v[:64 * EAGER_TILES], tile=64)
+    assert settled_early.all()
+    assert _row_rel(o, _exact_core(q, k, v)).max() < 1e-3

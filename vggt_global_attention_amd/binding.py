@@ -9,11 +9,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-from .build import LIB
+import contextlib
+
+from .build import LIB, TUNE_LIB
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
 MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR = 0, 1, 2, 3, 4
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
+STATUS_OFFSET = 16
+RANGE_X, RANGE_WQKV, RANGE_WO, RANGE_AFFINE, RANGE_SCALE = 1, 2, 4, 8, 16
 MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
          "subsampled": MODE_SUBSAMPLED, "descriptor": MODE_DESCRIPTOR}
 
@@ -23,7 +27,7 @@ EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_desc_cache_bytes", "vggt_attn_desc_cache_init", "vggt_attn_desc_append",
            "vggt_attn_desc_attend", "vggt_attn_desc_attend_stage",
            "vggt_attn_residual", "vggt_attn_schedule_workspace_bytes", "vggt_attn_schedule_run",
-           "vggt_attn_status_str", "vggt_attn_version")
+           "vggt_attn_range_status", "vggt_attn_status_str", "vggt_attn_version")
 
 
 class vggt_attn_shape(ctypes.Structure):
@@ -52,16 +56,41 @@ class VggtAttnError(RuntimeError):
 
 
 _lib = None
+_tune_lib = None
+_active = None  # the tuning build while inside tuning_build(), else None
 _CALL_ARGS = [ctypes.POINTER(vggt_attn_shape)] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 4 + \
     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
 
 def lib(path: str | None = None) -> ctypes.CDLL:
-    """Load (once) the built library; raise if it is not there."""
+    """Load (once) the built library; raise if it is not there.  Inside
+    tuning_build() this is the tuning build instead."""
     global _lib
+    if _active is not None:
+        return _active
     if _lib is not None:
         return _lib
-    path = path or LIB
+    _lib = _load(path or LIB)
+    return _lib
+
+
+@contextlib.contextmanager
+def tuning_build():
+    """Route every call in the block through libvggtattn_tune.so, the build
+    that honours the tuning environment variables (VGGT_ATTN_SPLIT,
+    VGGT_ATTN_QB, VGGT_ATTN_WAVES, VGGT_GEMM, VGGT_GEMM_FGROUPS).  The
+    product library ignores them."""
+    global _tune_lib, _active
+    if _tune_lib is None:
+        _tune_lib = _load(TUNE_LIB)
+    prev, _active = _active, _tune_lib
+    try:
+        yield _tune_lib
+    finally:
+        _active = prev
+
+
+def _load(path: str) -> ctypes.CDLL:
     # torch wheels bundle their own HIP runtime: load it first so that the
     # library binds to the same runtime as torch's streams and allocations
     # (loaded the other way round, two runtimes coexist and launches fail).
@@ -116,11 +145,13 @@ def lib(path: str | None = None) -> ctypes.CDLL:
                                          ctypes.POINTER(vggt_attn_block_weights), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
+    L.vggt_attn_range_status.restype = ctypes.c_int
+    L.vggt_attn_range_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32),
+                                         ctypes.c_void_p]
     L.vggt_attn_status_str.restype = ctypes.c_char_p
     L.vggt_attn_status_str.argtypes = [ctypes.c_int]
     L.vggt_attn_version.restype = ctypes.c_int
     L.vggt_attn_version.argtypes = []
-    _lib = L
     return L
 
 
@@ -227,6 +258,13 @@ def vggt_attn_schedule_run(shape, sched, blocks, X, state, caches, workspace, wo
     """`blocks` is a ctypes array of vggt_attn_block_weights (2 * n_layers)."""
     return _call("vggt_attn_schedule_run", ctypes.byref(shape), ctypes.byref(sched), blocks, X,
                  state, caches, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_range_status(workspace, stream) -> tuple:
+    """(status, range bits) of the last call that used `workspace`."""
+    bits = ctypes.c_uint32(0)
+    st = _call("vggt_attn_range_status", workspace, ctypes.byref(bits), stream)
+    return st, bits.value
 
 
 def status_str(status: int) -> str:

@@ -12,6 +12,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvggtattn.so")
+# The same sources with the tuning overrides compiled in (environment
+# variables that force tile, split and GEMM choices; see csrc/plan.h): for
+# sweeps and for the tests that force a choice.  Never the product library.
+TUNE_LIB = os.path.join(PKG, "libvggtattn_tune.so")
 SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip", "subsample.hip",
            "desc.hip", "schedule.cpp"]
 
@@ -27,9 +31,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, extra_flags=(), tuning: bool = True) -> str:
+    """Compile every HIP source for gfx950 and link the shared library (and,
+    unless tuning=False, the tuning build beside it)."""
+    if tuning:
+        _link(TUNE_LIB, verbose, (*extra_flags, "-DVGGT_ATTN_TUNING"))
+    return _link(LIB, verbose, extra_flags)
+
+
+def _link(out: str, verbose: bool, extra_flags) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared", "-I", INCLUDE, "-I", CSRC,
            "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
@@ -41,8 +52,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

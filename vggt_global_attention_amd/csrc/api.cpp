@@ -1,6 +1,7 @@
 // C ABI of libvggtattn: argument checks, planning and stage dispatch.  Every
 // check runs before the first HIP call, so a rejected call launches nothing.
 #include <math.h>
+#include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -10,7 +11,21 @@
 
 namespace vggt {
 
+static_assert(offsetof(Scalars, status) == VGGT_ATTN_STATUS_OFFSET,
+              "the status word's offset is part of the ABI");
+
 static int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+#ifdef VGGT_ATTN_TUNING
+bool tuning_knob(const char* name, int* value) {
+  const char* e = getenv(name);
+  if (!e || !*e) return false;
+  *value = atoi(e);
+  return true;
+}
+#else
+bool tuning_knob(const char*, int*) { return false; }
+#endif
 
 int device_cu_count() {
   static std::atomic<int> cache[64];
@@ -72,6 +87,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   p->off = s->pos_offset;
   p->base = s->rope_base;
   p->eps = s->ln_eps;
+  p->keep_status = o.keep_status;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc) {
@@ -96,22 +112,16 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->attn_qb = 1;
     p->attn_waves = 4;
   }
-  // Tuning override of the attention tile: VGGT_ATTN_QB = 1 or 2 query
-  // blocks of 32 per wave, VGGT_ATTN_WAVES = 4 or 8 waves per workgroup.
+  // Tuning override of the attention tile (tuning build only).
   bool tile_forced = false;
-  if (const char* e = getenv("VGGT_ATTN_QB")) {
-    const int q = atoi(e);
-    if (q == 1 || q == 2) {
-      p->attn_qb = q;
-      tile_forced = true;
-    }
+  int knob = 0;
+  if (tuning_knob("VGGT_ATTN_QB", &knob) && (knob == 1 || knob == 2)) {
+    p->attn_qb = knob;
+    tile_forced = true;
   }
-  if (const char* e = getenv("VGGT_ATTN_WAVES")) {
-    const int w = atoi(e);
-    if (w == 4 || w == 8) {
-      p->attn_waves = w;
-      tile_forced = true;
-    }
+  if (tuning_knob("VGGT_ATTN_WAVES", &knob) && (knob == 4 || knob == 8)) {
+    p->attn_waves = knob;
+    tile_forced = true;
   }
   p->rows = round_up(cover, cover >= kRowAlignFrom ? kRowAlign : 256);
   if (p->rows >= ((int64_t)1 << 31)) return VGGT_ATTN_ESHAPE;  // kernels index rows in 32 bits
@@ -155,12 +165,13 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->out_map = RowMap{p->rows, 0, (int32_t)o.q_count, 1, o.q_begin};
   }
   // Small global-type grids (global sets, query windows, descriptor
-  // attention): when the 8-wave tile would give fewer workgroups than an
-  // MI355X has CUs (256), the 4-wave tile of one query block per wave runs
-  // four times as many, up to three per CU.  Both tiles compute every row
-  // the same way, bit for bit.
+  // attention): when the 8-wave tile would give fewer workgroups than the
+  // device has CUs, the 4-wave tile of one query block per wave runs four
+  // times as many, up to three per CU.  Both tiles compute every row the
+  // same way, bit for bit.
+  const int64_t cus = o.cus > 0 ? o.cus : 256;
   if ((mode == VGGT_ATTN_MODE_GLOBAL || desc) && !tile_forced &&
-      (int64_t)(p->L - p->q0 + 511) / 512 * s->H < 256) {
+      (int64_t)(p->L - p->q0 + 511) / 512 * s->H < cus) {
     p->attn_qb = 1;
     p->attn_waves = 4;
   }
@@ -169,7 +180,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   // S = 500, 8,500 rows: 0.29 against 0.32 ms with 32 queries per wave, and
   // 0.30 ms on 8-wave workgroups); smaller sets keep 32 queries per wave for
   // the workgroup count.
-  if (mode == VGGT_ATTN_MODE_REGISTER && !tile_forced && (R + 255) / 256 * s->H >= 256) {
+  if (mode == VGGT_ATTN_MODE_REGISTER && !tile_forced && (R + 255) / 256 * s->H >= cus) {
     p->attn_qb = 2;
   }
   p->rope_npos = (s->grid_h > s->grid_w ? s->grid_h : s->grid_w) + s->pos_offset;
@@ -177,9 +188,9 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
 
   size_t off = 0;
   p->off_scal = off;
-  off += round_up((int64_t)sizeof(float) * (4 + s->H), 256);
+  off += round_up((int64_t)scalars_bytes(s->H), 256);
   p->off_bounds = off;  // partial maxima of the prep stage
-  off += round_up((int64_t)sizeof(float) * (kBoundsX + kBoundsV + kBoundsO), 256);
+  off += round_up((int64_t)sizeof(float) * kBoundsParts, 256);
   p->off_rope = off;
   off += round_up((int64_t)p->rope_npos * 16 * sizeof(float2), 256);
   p->off_wo = off;
@@ -214,17 +225,27 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   // sized).  Sized from the shape alone, not the device; in subsampled mode
   // from the kept keys, largest with 1 x 1 windows, the size the workspace
   // query reports.
+  // The region is sized for the largest need over the attention tiles (128,
+  // 256 or 512 queries per workgroup), so that the size does not depend on
+  // which tile the device's CU count picks.
   p->split_cap = 0;
   p->off_split = off;
   if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER || subsampled) {
-    const int64_t bq = (int64_t)p->attn_waves * p->attn_qb * 32;
-    const int64_t W = (p->L - p->q0 + bq - 1) / bq * s->H * p->nseq;
     int64_t ways = (p->Lk + kAttnBK - 1) / kAttnBK / kSplitMinTiles;
     if (ways > kSplitMaxWays) ways = kSplitMaxWays;
     if (ways >= 2) {
-      const int64_t cap = kSplitMaxRows / bq;
-      p->split_cap = (int)(W * ways < cap ? W * ways : cap);
-      off += round_up((int64_t)p->split_cap * bq * (kDh + 2) * sizeof(float), 256);
+      auto units = [&](int64_t bq) {
+        const int64_t W = (p->L - p->q0 + bq - 1) / bq * s->H * p->nseq;
+        const int64_t cap = kSplitMaxRows / bq;
+        return W * ways < cap ? W * ways : cap;
+      };
+      int64_t region = 0;
+      for (int64_t bq = 128; bq <= 512; bq *= 2) {
+        const int64_t b = units(bq) * bq * (kDh + 2) * (int64_t)sizeof(float);
+        if (b > region) region = b;
+      }
+      p->split_cap = (int)units((int64_t)p->attn_waves * p->attn_qb * 32);
+      off += round_up(region, 256);
     }
   }
   p->total = off;
@@ -245,7 +266,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 int check_call(int mode, const vggt_attn_shape* shape, const CallOpts& o, const void* X,
                const void* Wqkv, const void* Wo, const float* qg, const float* qb, const float* kg,
                const float* kb, void* Y, void* ws, size_t ws_bytes, Plan* plan) {
-  int st = make_plan(mode, shape, o, plan);
+  CallOpts oc = o;
+  oc.cus = device_cu_count();
+  int st = make_plan(mode, shape, oc, plan);
   if (st != VGGT_ATTN_OK) return st;
   const bool desc = mode == VGGT_ATTN_MODE_DESCRIPTOR;
   // descriptor mode: keys come from the cache, so no key affine is passed
@@ -517,12 +540,25 @@ const char* vggt_attn_status_str(int status) {
     case VGGT_ATTN_EWORKSPACE: return "workspace smaller than vggt_attn_workspace_bytes()";
     case VGGT_ATTN_EHIP: return "HIP runtime error while enqueueing a kernel";
     case VGGT_ATTN_ERANGE:
-      return "rope_base / ln_eps must be finite and > 0, pos_offset in 0..65535, sub_h / sub_w >= 1, "
-             "row window inside the set";
+      return "value out of range: rope_base / ln_eps must be finite and > 0, pos_offset in "
+             "0..65535, sub_h / sub_w >= 1, row window inside the set; or (range status) a "
+             "non-finite input or a bound beyond fp16 range";
     default: return "unknown status";
   }
 }
 
-int vggt_attn_version(void) { return 10100; }
+int vggt_attn_range_status(const void* workspace, uint32_t* bits, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return VGGT_ATTN_EINVAL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, reinterpret_cast<const char*>(workspace) + VGGT_ATTN_STATUS_OFFSET,
+                     sizeof(word), hipMemcpyDeviceToHost, hs) != hipSuccess ||
+      hipStreamSynchronize(hs) != hipSuccess)
+    return VGGT_ATTN_EHIP;
+  if (bits) *bits = word;
+  return word ? VGGT_ATTN_ERANGE : VGGT_ATTN_OK;
+}
+
+int vggt_attn_version(void) { return 10200; }
 
 }  // extern "C"

@@ -25,21 +25,36 @@
 //     the LayerNorm-ed, rotated vectors), known before the first tile;
 //   * fp16 holds P <= 2^15 without overflow and keeps full relative precision
 //     for P >= 2^-14.
-// The first tile takes the row max m0.  If bound - m0 <= 29, the reference is
+// The first tile takes the row max m0.  If bound - m0 <= 19, the reference is
 // pinned at max(m0, bound - 15): no later logit can push P above 2^15, and the
-// largest term of the row (>= m0) stays >= 2^-14, so the row is "settled" and
-// its max is never taken again.  Rows that are not settled (very peaked rows
-// whose first tile is far below the bound) keep an ordinary online max with
-// lazy rescaling (only when a logit exceeds m + 8) and re-check the settle
-// condition after each tile.  The row sum accumulates the fp16-rounded
+// reference sits at most 4 above the row's largest logit (>= m0), so the top
+// term of the row stays >= 2^-4 and the row's probabilities keep fp16's
+// relative precision down to 2^-10 of it; the row is "settled" and its max is
+// never taken again.  Rows that are not settled keep an online max and
+// re-check the settle condition after each tile: over the first kEagerTiles
+// tiles of a key range the reference follows the running max exactly (a
+// first tile's max is a poor estimate of the row's: at 103,100 tokens with
+// the workloads' QK-norm affine, 800 of 25,760 waves hold a row that the
+// first tile leaves unsettled, 46 after 4 tiles, 2 after 16), later only
+// lazily (when a logit exceeds m + 8).  Rows far below their bound -- peaked
+// rows, or a loose bound when the QK-norm gain is large -- so run as ordinary
+// online-softmax rows.  A wider settle gap would let the reference float up
+// to (gap - 15) above the row max and push the bulk of the row's
+// probabilities into fp16's subnormal range (per-row error 1e-2 at a gap of
+// 29 with a QK-norm gain near 2).  Waves that stay unsettled cost more than
+// their share: their workgroup runs at their pace, and a few slow workgroups
+// stretch the end of the launch (measured at 103,100 tokens against the
+// 29 gap: 16% slower when rows could settle only on their first tile, 7%
+// with 4 eager tiles, 4% with 8, none with 16).  The row sum accumulates the fp16-rounded
 // probabilities with v_dot2 (the same values the PV MFMA consumes).
 //
 // One kernel, attn_kernel<QB, NW, SGA>: NW waves and NW*QB*32 queries per
 // workgroup (SGA: the subsampled global set, whose keys are a compact copy of
 // the kept tokens, plus two per-row columns folded in at the end).  Global
 // sets use 8 waves x 64 queries (512 queries share each K/V tile, one
-// workgroup per CU); frame and register sets use 4 waves x 32 queries (small
-// sets, ragged ends).  Every shape runs the same per-row arithmetic, so a row
+// workgroup per CU); frame sets use 4 waves x 32 queries (small sets, ragged
+// ends); register sets use 4 waves x 64 queries while that grid still gives
+// every CU a workgroup, else 4 x 32.  Every shape runs the same per-row arithmetic, so a row
 // comes out bit for bit the same whichever tile computes it.  The partly
 // filled last round of a single-set grid runs as key ranges whose softmax
 // states attn_merge_kernel combines (split tail, below).  Measured
@@ -59,7 +74,9 @@ namespace vggt {
 
 constexpr float kTau = 8.f;        // unsettled rows: rescale when a logit exceeds m + kTau
 constexpr float kPinBelow = 15.f;  // settled rows: reference pinned at bound - kPinBelow (P <= 2^15)
-constexpr float kSettleGap = 29.f; // settle once bound - m <= kSettleGap (top term stays >= 2^-14)
+constexpr float kSettleGap = 19.f; // settle once bound - m <= kSettleGap: the pinned reference
+                                   // is at most kSettleGap - kPinBelow = 4 above the row max
+constexpr int kEagerTiles = 16;    // unsettled rows follow the exact running max this long
 
 struct AttnArgs {
   f16* q;              // [H][rows][64] scaled queries; overwritten with O
@@ -127,16 +144,29 @@ struct Rows {
   float l[NB];      // partial row sum (this lane's keys)
   f32x4 negm[NB];   // -m broadcast
   f32x4 O[4][NB];   // O^T[16 db + 4 g + i][row 16 qb + r]
+  unsigned settled; // bit qb: the row of query block qb is settled (its reference is final)
   bool track;       // wave-uniform: some row is not settled yet
 };
 
+// Reductions over the four 16-lane groups that hold one query row, through
+// gfx950's permlane swaps (VALU; no LDS round trip and no wait): each lane's
+// pair of results is its own value and that of lane l ^ 16 (then l ^ 32), in
+// the same order on both lanes, so every lane of a row gets the same bits.
 __device__ __forceinline__ float max_over_groups16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_groups16(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // LDS lane offsets of the operand reads: ka[kb % 2][dc] for K (block kb adds
@@ -197,18 +227,23 @@ __device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t se
 #pragma unroll
     for (int db = 0; db < 4; ++db) R.O[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  R.settled = 0u;
   R.track = true;
 }
 
-// One 64-key tile: S^T = K Q^T - m (MASK: keys at or beyond `valid` start from
-// -inf, so their probability is exactly 0); on the first tile, or while a row
-// is unsettled, the row max moves or pins the reference; P = 2^S in fp16 with
-// the row sums; then O^T += V^T P^T.  KB = 2 (a short last tile of at most 32 keys): key
+// The probabilities of one 64-key tile: S^T = K Q^T - m (MASK: keys at or
+// beyond `valid` start from -inf, so their probability is exactly 0); where
+// needed (below) the max of every row that is not settled moves or pins its
+// reference first -- to the exact running max while `eager`, else only when
+// the tile's max exceeds m + kTau; then P = 2^S in fp16 into pf, and the row
+// sums.  KB = 2 (a short last tile of at most 32 keys): key
 // blocks 0 and 1 only, which hold keys 0..31, and the first PV step; the
-// other probabilities are exactly zero, so the result is the same bit for bit.
-template <bool MASK, int KB = 4, int NB>
-__device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const char* Ks,
-                                         const char* Vs, int lane, int valid, bool first) {
+// other probabilities are exactly zero, so the result is the same bit for
+// bit.
+template <bool MASK, int KB, int NB>
+__device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const char* Ks, int lane,
+                                           int valid, bool first, bool eager,
+                                           f16x8 (&pf)[NB][2]) {
   static_assert(KB == 4 || KB == 2, "whole tile or its first 32 keys");
   constexpr int NC = KB / 2;  // 32-key PV steps
   const int g = lane >> 4;
@@ -241,9 +276,14 @@ __device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const cha
 #pragma unroll
         for (int i = 0; i < 4; i += 2) mt = fmaxf(mt, fmaxf(S[kb][qb][i], S[kb][qb][i + 1]));
       mt = max_over_groups16(mt);  // row max of this tile, relative to m
-      float mn = (first || mt > kTau) ? R.m[qb] + mt : R.m[qb];
-      const bool settled = mn >= R.bound[qb] - kSettleGap;
-      if (settled) mn = fmaxf(mn, R.bound[qb] - kPinBelow);
+      // a settled row keeps its reference whatever its wave does, so a row's
+      // arithmetic never depends on the other rows of its wave
+      const bool fixed = !first && ((R.settled >> qb) & 1u);
+      float mn = (first || mt > (eager ? 0.f : kTau)) ? R.m[qb] + mt : R.m[qb];
+      if (fixed) mn = R.m[qb];
+      const bool settled = fixed || mn >= R.bound[qb] - kSettleGap;
+      if (settled && !fixed) mn = fmaxf(mn, R.bound[qb] - kPinBelow);
+      if (settled) R.settled |= 1u << qb;
       unsettled = unsettled || !settled;
       const float dl = mn - R.m[qb];
       if (dl != 0.f) {
@@ -263,7 +303,6 @@ __device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const cha
     }
     R.track = __ballot(unsettled) != 0;
   }
-  f16x8 pf[NB][2];
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
@@ -282,6 +321,16 @@ __device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const cha
         }
       pf[qb][c] = v;
     }
+}
+
+// One 64-key tile: its probabilities (tile_probs), then O^T += V^T P^T.
+template <bool MASK, int KB = 4, int NB>
+__device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const char* Ks,
+                                         const char* Vs, int lane, int valid, bool first,
+                                         bool eager) {
+  constexpr int NC = KB / 2;  // 32-key PV steps
+  f16x8 pf[NB][2];
+  tile_probs<MASK, KB>(R, ln, Ks, lane, valid, first, eager, pf);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -550,7 +599,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   auto step = [&](auto buf_c, int t) {
     constexpr int BUF = decltype(buf_c)::value;
     issue(t + 1, BUF ^ 1);
-    if (active) tile_run<false>(R, ln, smem[BUF][0], smem[BUF][1], lane, 64, t == t0);
+    if (active)
+      tile_run<false>(R, ln, smem[BUF][0], smem[BUF][1], lane, 64, t == t0, t - t0 < kEagerTiles);
     land();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -575,7 +625,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     LanesT lb = ln;
     for (; t < t1 - 1; ++t) {
       issue(t + 1, ((t - t0) & 1) ^ 1);
-      if (active) tile_run<false>(R, lb, smem[0][0], smem[0][1], lane, 64, t == t0);
+      if (active)
+        tile_run<false>(R, lb, smem[0][0], smem[0][1], lane, 64, t == t0, t - t0 < kEagerTiles);
       land();
       lb.flip(2 * 64 * 128);  // the other buffer
     }
@@ -587,11 +638,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   if (active) {
     LanesT lb = ln;
     lb.flip(((t - t0) & 1) * 2 * 64 * 128);
-    const bool first = t1 - t0 == 1;
+    const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
     if (NW == 4 && last_valid <= 32) {
-      tile_run<true, 2>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first);
+      tile_run<true, 2>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first, eager);
     } else {
-      tile_run<true>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first);
+      tile_run<true>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first, eager);
     }
   }
   // the diagonal and mean columns enter once per row: in its last key range
@@ -656,8 +707,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
 // work, on the same XCD) shortens that round from one workgroup time to
 // ceil(tail P / slots) / P.  P is the smallest that gets within 2% of the
 // best, with at least kSplitMinTiles key tiles per range and 8 * tail * P
-// units within the partial-result buffer.  VGGT_ATTN_SPLIT = P forces the key
-// ranges per split workgroup (1: no split; a tuning / testing switch).
+// units within the partial-result buffer.  The tuning build's VGGT_ATTN_SPLIT
+// = P forces the key ranges per split workgroup (1: no split).
 struct SplitPlan {
   int P = 1, xcd_slots = 0, umax = 0;
   int64_t grid = 0;
@@ -688,8 +739,9 @@ static SplitPlan choose_split(const Plan& p, int64_t W, int ntiles, int per_cu) 
       best = P;
     }
   }
-  if (const char* e = getenv("VGGT_ATTN_SPLIT")) {
-    int P = atoi(e);
+  int forced = 0;
+  if (tuning_knob("VGGT_ATTN_SPLIT", &forced)) {
+    int P = forced;
     while (P > 1 && !allowed(P)) --P;
     if (P >= 1) best = P;
   }

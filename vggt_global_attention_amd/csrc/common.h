@@ -47,14 +47,18 @@ struct RowMap {
 };
 
 // Scalars the kernels exchange through the workspace (all written by the
-// prep stage before they are read).
+// prep stage before they are read).  The workspace starts with them, so the
+// status word sits at byte VGGT_ATTN_STATUS_OFFSET of every workspace.  A
+// descriptor cache starts with the same header.
 struct Scalars {
-  float xnorm;     // max L2 norm over the X rows of the set(s)
-  float wvnorm;    // max L2 norm over the V rows of Wqkv
-  float woabs;     // max |Wo|
-  float pad;
-  float kmax[1];   // [H] max L2 norm of the normalised, rotated fp16 keys per head
+  float xnorm;      // max L2 norm over the X rows of the set(s); +inf if one is not finite
+  float wvnorm;     // max L2 norm over the V rows of Wqkv; +inf if one is not finite
+  float woabs;      // max |Wo|; +inf if an entry is not finite
+  float pad;        // descriptor cache: exponent of the stored values (int bits)
+  uint32_t status;  // VGGT_ATTN_RANGE_* bits the prep stage found (0: all in range)
+  float kmax[1];    // [H] max L2 norm of the normalised, rotated fp16 keys per head
 };
+inline constexpr size_t scalars_bytes(int H) { return sizeof(float) * (5 + (size_t)H); }
 
 // Blocks are handed to the 8 XCDs round-robin; remap so that each XCD works
 // through one contiguous range of logical block ids (shared operands then
@@ -80,12 +84,30 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Power-of-two exponent e such that bound * 2^e <= 2^14 (clamped); 0 if the
-// bound is zero or not finite.
+// Power-of-two exponent e such that bound * 2^e <= 2^14 (clamped to
+// [-60, 60], so that the output projection's 2^-(e + s) stays a normal fp32
+// number); 0 if the bound is zero or not finite.
 __device__ __forceinline__ int range_exponent(float bound) {
   if (!(bound > 0.f) || !(bound < 3.0e38f)) return 0;
   int e = (int)floorf(14.f - log2f(bound));
   return e < -60 ? -60 : (e > 60 ? 60 : e);
+}
+
+// True when range_exponent cannot do its job for `bound`: the bound is not
+// finite (or beyond 3e38), or the exponent it needs lies outside [-60, 60].
+// A zero bound (all values zero) is in range.
+__device__ __forceinline__ bool range_exponent_clamped(float bound) {
+  if (bound == 0.f) return false;
+  if (!(bound > 0.f) || !(bound < 3.0e38f)) return true;
+  const float e = floorf(14.f - log2f(bound));
+  return e < -60.f || e > 60.f;
+}
+
+// x if finite and non-negative-ordered into a running maximum, else +inf
+// (fmaxf would drop a NaN): the bounds of the prep stage carry a non-finite
+// input forward as +inf, which the status check then reports.
+__device__ __forceinline__ float max_or_inf(float best, float x) {
+  return x < INFINITY ? fmaxf(best, x) : INFINITY;
 }
 
 // Max-reduce across the four 16-lane groups that hold one MFMA column.

@@ -59,12 +59,21 @@ __global__ void desc_commit_kernel(Scalars* hdr) {
 
 // Copy the cache's bounds into a call's scalars: the value bound (so the
 // output projection undoes the cache's scale) and the per-head key norms (the
-// attention kernel's softmax bound).
+// attention kernel's softmax bound); a non-finite descriptor (its norm is
+// +inf) or a value bound out of the scale's reach adds its range bits.
 __global__ void desc_load_kernel(const Scalars* hdr, Scalars* sc, int H) {
   const int t = threadIdx.x;
   if (t == 0) {
-    sc->xnorm = hdr->xnorm;
-    sc->wvnorm = hdr->wvnorm;
+    const float xm = hdr->xnorm, vm = hdr->wvnorm;
+    sc->xnorm = xm;
+    sc->wvnorm = vm;
+    uint32_t bits = 0;
+    if (!(xm < INFINITY)) bits |= VGGT_ATTN_RANGE_X;
+    if (!(vm < INFINITY)) bits |= VGGT_ATTN_RANGE_WQKV;
+    if (!bits && (range_exponent_clamped(xm * vm) ||
+                  (double)xm * vm * sc->woabs * (H * kDh) >= 3.0e38))
+      bits |= VGGT_ATTN_RANGE_SCALE;
+    sc->status |= bits;
   }
   for (int h = t; h < H; h += blockDim.x) sc->kmax[h] = hdr->kmax[h];
 }

@@ -833,10 +833,8 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
 // count) whose weight slice fits a ~2 MB share of an XCD's 4 MB L2.
 static int feature_groups(int nf, int k, int elem_bytes, int bn) {
   const int ntn = nf / bn;
-  if (const char* e = getenv("VGGT_GEMM_FGROUPS")) {  // tuning override (must divide the tile count)
-    const int v = atoi(e);
-    if (v >= 1 && ntn % v == 0) return v;
-  }
+  int v = 0;  // tuning override (must divide the tile count)
+  if (tuning_knob("VGGT_GEMM_FGROUPS", &v) && v >= 1 && ntn % v == 0) return v;
   const int64_t bytes = (int64_t)nf * k * elem_bytes;
   for (int gcount = 1; gcount < ntn; ++gcount)
     if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)2 << 20)) return gcount;
@@ -845,17 +843,15 @@ static int feature_groups(int nf, int k, int elem_bytes, int bn) {
 
 // Kernel choice: 2 = wide (256 x 256, output features a multiple of 256),
 // 1 = DMA 256 x 128, 0 = register-staged 128 x 128.  The DMA kernels need
-// whole 256-row token tiles.  VGGT_GEMM = 0 | 1 | 2 picks the kind (a tuning
-// / comparison switch).
+// whole 256-row token tiles.  The tuning build's VGGT_GEMM = 0 | 1 | 2 picks
+// the kind (a comparison switch).
 static int gemm_kind(const Plan& p, int nf) {
   int kind = 2;
   bool forced = false;
-  if (const char* e = getenv("VGGT_GEMM")) {
-    const int v = atoi(e);
-    if (v >= 0 && v <= 2) {
-      kind = v;
-      forced = true;
-    }
+  int v = 0;
+  if (tuning_knob("VGGT_GEMM", &v) && v >= 0 && v <= 2) {
+    kind = v;
+    forced = true;
   }
   if (kind == 2 && nf % kWBN != 0) kind = 1;
   if (kind >= 1 && p.rows % kDmaBM != 0) kind = 0;
@@ -964,10 +960,8 @@ hipError_t launch_desc_kv(char* cache, const DescLayout& L, int H, int d, float 
   g.vt = reinterpret_cast<f16*>(cache + L.off_v);
   g.y = nullptr;
   int kind = 2;
-  if (const char* e = getenv("VGGT_GEMM")) {
-    const int v = atoi(e);
-    if (v >= 0 && v < 2) kind = v;
-  }
+  int v = 0;
+  if (tuning_knob("VGGT_GEMM", &v) && v >= 0 && v < 2) kind = v;
   if (kind == 2 && g.Nf % kWBN != 0) kind = 1;
   const int bn = kind == 2 ? kWBN : kind == 1 ? kDmaBN : kGemmBN;
   g.fgroups = feature_groups(g.Nf, g.K, 2, bn);

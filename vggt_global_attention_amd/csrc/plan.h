@@ -27,7 +27,10 @@ constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are pa
 // Prep stage: per-workgroup partial maxima of the range bounds (X row norms
 // over up to kBoundsX workgroups, V rows of Wqkv over kBoundsV, |Wo| over
 // kBoundsO), reduced by the Wo conversion.
+// The first kBoundsV workgroups also check the Q and K rows of Wqkv for
+// non-finite values (their own partials, after the |Wo| ones).
 constexpr int kBoundsX = 2048, kBoundsV = 64, kBoundsO = 128;
+constexpr int kBoundsParts = kBoundsX + kBoundsV + kBoundsO + kBoundsV;
 constexpr int kSplitMaxRows = 1 << 18;
 constexpr int kSplitMaxWays = 32;
 constexpr int kSplitMinTiles = 24;
@@ -42,6 +45,12 @@ struct CallOpts {
   size_t cache_bytes = 0;
   int64_t desc_capacity = 0;
   int64_t desc_count = 0;
+  // CUs of the device the call runs on (tile choices); 0 when only sizing
+  // the workspace, whose size never depends on the device
+  int cus = 0;
+  // the prep stage ORs its range bits into the workspace's status word
+  // instead of replacing it (the blocks of a schedule after the first)
+  bool keep_status = false;
 };
 
 // Descriptor key / value cache (caller-owned device buffer, 256-byte
@@ -57,7 +66,7 @@ struct DescLayout {
 inline DescLayout desc_layout(int H, int64_t capacity) {
   DescLayout L;
   L.cap_rows = (capacity + kKvAlign - 1) / kKvAlign * kKvAlign;
-  const size_t hdr = ((sizeof(float) * (4 + H)) + 255) / 256 * 256;
+  const size_t hdr = (scalars_bytes(H) + 255) / 256 * 256;
   const size_t arr = (size_t)H * L.cap_rows * kDh * 2;
   L.off_k = hdr;
   L.off_v = hdr + arr;
@@ -97,6 +106,7 @@ struct Plan {
   // decides from the device's CU count whether the last, partly filled round
   // of workgroups runs as key ranges that a merge kernel combines.
   int split_cap;
+  bool keep_status;    // see CallOpts
   // workspace carve-up (byte offsets)
   size_t off_scal, off_bounds, off_rope, off_wo, off_q, off_k, off_v;
   size_t off_kc, off_vc, off_sums, off_part;  // subsampled mode only (else 0)
@@ -121,6 +131,19 @@ struct Ptrs {
 // Compute units of the current device (256 when it cannot be queried),
 // cached per device.
 int device_cu_count();
+
+// Tuning overrides.  The product library reads no environment: its tile,
+// split and GEMM choices depend on the shape and the device only, so a call
+// gives the same bits whatever the caller's environment.  A separate tuning
+// build (compiled with VGGT_ATTN_TUNING, libvggtattn_tune.so) reads these
+// variables on every call, for sweeps and for tests that force a choice:
+//   VGGT_ATTN_QB = 1 | 2      query blocks of 32 per attention wave
+//   VGGT_ATTN_WAVES = 4 | 8   waves per attention workgroup
+//   VGGT_ATTN_SPLIT = P       key ranges per split-tail workgroup (1: no split)
+//   VGGT_GEMM = 0 | 1 | 2     projection kernel (128x128, 256x128 DMA, 256x256 DMA)
+//   VGGT_GEMM_FGROUPS = g     weight slices an XCD walks
+// Returns true and sets *value when the variable is set (tuning build only).
+bool tuning_knob(const char* name, int* value);
 
 // Fills `p`; returns VGGT_ATTN_OK or the shape / range status.  `o` carries
 // the subsampling windows (VGGT_ATTN_MODE_SUBSAMPLED) or the query-row

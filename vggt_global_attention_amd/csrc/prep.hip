@@ -6,8 +6,9 @@
 //     maximum per workgroup (no atomics, nothing to clear first);
 //   * wo_convert_kernel: reduces the partial maxima into the workspace
 //     scalars (exact power-of-two scales that keep V, O and Wo inside fp16
-//     range) and writes the fp16 copy of Wo scaled by 2^s (the output GEMM
-//     runs on fp16 MFMA);
+//     range), sets the range status bits (non-finite inputs, affines or
+//     bounds that no pre-scale brings into fp16 range) and writes the fp16
+//     copy of Wo scaled by 2^s (the output GEMM runs on fp16 MFMA);
 // plus the register-mode patch-row copy Y = X and the residual update of a
 // layer schedule.
 #include "plan.h"
@@ -27,7 +28,9 @@ __device__ __forceinline__ float2 rope_entry(int i, float base) {
 // Largest L2 norm of the bf16 rows of `len` elements (a multiple of 8) that
 // waves wave0, wave0 + nwaves, ... of the grid walk (four rows at a time,
 // loads issued together); rows are mapped through `map`, unmapped rows
-// skipped.  Per-lane result (every lane of a wave holds the wave's value).
+// skipped; +inf once a row holds a non-finite value or its squared norm
+// overflows fp32.  Per-lane result (every lane of a wave holds the wave's
+// value).
 __device__ __forceinline__ float rows_norm_max(const bf16* base, int64_t nrows, int len,
                                                const RowMap& map, int64_t wave0, int64_t nwaves,
                                                int lane) {
@@ -54,7 +57,7 @@ __device__ __forceinline__ float rows_norm_max(const bf16* base, int64_t nrows, 
       float a = acc[u];
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
-      best = fmaxf(best, sqrtf(a));
+      best = max_or_inf(best, sqrtf(a));
     }
   }
   return best;
@@ -71,13 +74,14 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 struct BoundsArgs {
-  const bf16* X;      // rows through map (skipped when null: descriptor mode)
+  const bf16* X;      // rows through map (skipped when null)
   int64_t rows;
   RowMap map;
-  const bf16* Wv;     // the V rows of Wqkv, [d][d] (skipped when X is null)
+  const bf16* Wqkv;   // [3d][d]: V rows for the bound (skipped when X is null), Q and K rows
+                      // checked for non-finite values
   const bf16* Wo;     // [d][d]
   int d;
-  float* part;        // [kBoundsX] X, then [kBoundsV] Wv, then [kBoundsO] Wo partial maxima
+  float* part;        // [kBoundsX] X, [kBoundsV] Wv, [kBoundsO] Wo, [kBoundsV] Wq / Wk partials
   float2* rope;
   int nrope;          // table entries (positions x 16)
   float base;
@@ -96,29 +100,33 @@ __global__ __launch_bounds__(256) void bounds_kernel(BoundsArgs b) {
   for (int64_t i = gtid; i < b.nrope; i += gthreads) b.rope[i] = rope_entry((int)i, b.base);
   for (int64_t i = gtid; i < b.nsums; i += gthreads) b.sums[i] = 0.f;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (tid >> 6);
-  float xm = 0.f, vm = 0.f, om = 0.f;
+  float xm = 0.f, vm = 0.f, om = 0.f, qkm = 0.f;
+  const RowMap ident{INT64_MAX / 2, 0, 3 * b.d, 1, 0};
   if (b.X) {
     xm = rows_norm_max(b.X, b.rows, b.d, b.map, wave, (int64_t)gridDim.x * 4, lane);
-    if (blockIdx.x < kBoundsV) {
-      const RowMap ident{INT64_MAX / 2, 0, b.d, 1, 0};
-      vm = rows_norm_max(b.Wv, b.d, b.d, ident, wave, (int64_t)kBoundsV * 4, lane);
-    }
+    if (blockIdx.x < kBoundsV)
+      vm = rows_norm_max(b.Wqkv + (int64_t)2 * b.d * b.d, b.d, b.d, ident, wave,
+                         (int64_t)kBoundsV * 4, lane);
   }
+  if (blockIdx.x < kBoundsV)
+    qkm = rows_norm_max(b.Wqkv, 2 * b.d, b.d, ident, wave, (int64_t)kBoundsV * 4, lane);
   if (blockIdx.x < kBoundsO) {
     const int64_t n8 = (int64_t)b.d * b.d / 8;
     for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n8; i += (int64_t)kBoundsO * 256) {
       const bf16x8 v = reinterpret_cast<const bf16x8*>(b.Wo)[i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) om = fmaxf(om, fabsf((float)v[e]));
+      for (int e = 0; e < 8; ++e) om = max_or_inf(om, fabsf((float)v[e]));
     }
   }
   xm = block_max(xm, red);
   vm = block_max(vm, red);
   om = block_max(om, red);
+  qkm = block_max(qkm, red);
   if (tid == 0) {
     b.part[blockIdx.x] = xm;
     if (blockIdx.x < kBoundsV) b.part[kBoundsX + blockIdx.x] = vm;
     if (blockIdx.x < kBoundsO) b.part[kBoundsX + kBoundsV + blockIdx.x] = om;
+    if (blockIdx.x < kBoundsV) b.part[kBoundsX + kBoundsV + kBoundsO + blockIdx.x] = qkm;
   }
 }
 
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int6
       float a = acc[u];
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
-      best = fmaxf(best, sqrtf(a));
+      best = max_or_inf(best, sqrtf(a));
     }
   }
   if (lane == 0) red[threadIdx.x >> 6] = best;
@@ -167,14 +175,37 @@ __global__ __launch_bounds__(256) void rownorm_max_kernel(const bf16* base, int6
   }
 }
 
+// The per-head QK-norm affines of a call (k_gamma / k_beta null in
+// descriptor mode, whose keys come from the cache) and whether the range bits
+// are ORed into the status word (keep) or replace it.
+struct AffineArgs {
+  const float* qg;
+  const float* qb;
+  const float* kg;
+  const float* kb;
+  int keep;
+  int desc;  // descriptor mode: the value bounds are the cache's (checked when they are loaded)
+};
+
+// Largest per-feature bound 8 |gamma| + |beta| over an [H][64] affine (a
+// LayerNorm-ed feature is at most sqrt(63) < 8 in magnitude); +inf if an entry
+// is not finite.  Result in every thread of the workgroup.
+__device__ __forceinline__ float affine_bound(const float* g, const float* b, int n, float* red) {
+  float a = 0.f;
+  if (g)
+    for (int i = threadIdx.x; i < n; i += 256) a = max_or_inf(a, 8.f * fabsf(g[i]) + fabsf(b[i]));
+  return block_max(a, red);
+}
+
 // Wo (bf16) -> fp16 * 2^s with s chosen from max|Wo| so the largest entry
 // lands near 2^14; exact for every entry within 2^-24 of the largest.  Every
 // workgroup reduces the |Wo| partial maxima itself; workgroup 0 also writes
-// the scalars: the three bounds and cleared key norms (the QKV epilogue
-// takes their maximum).  nx = X partials written by the bounds kernel.
+// the scalars: the three bounds, cleared key norms (the QKV epilogue takes
+// their maximum) and the range status.  nx = X partials written by the
+// bounds kernel.
 __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t n8,
                                                          const float* part, int nx, Scalars* sc,
-                                                         int H, f16* out) {
+                                                         int H, f16* out, AffineArgs af) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const float woabs = block_max(tid < kBoundsO ? part[kBoundsX + kBoundsV + tid] : 0.f, red);
@@ -183,11 +214,32 @@ __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t
     for (int i = tid; i < nx; i += 256) xm = fmaxf(xm, part[i]);
     xm = block_max(xm, red);
     const float vm = block_max(tid < kBoundsV ? part[kBoundsX + tid] : 0.f, red);
+    const float qkm =
+        block_max(tid < kBoundsV ? part[kBoundsX + kBoundsV + kBoundsO + tid] : 0.f, red);
+    const float aq = affine_bound(af.qg, af.qb, H * kDh, red);
+    const float ak = affine_bound(af.kg, af.kb, H * kDh, red);
     if (tid == 0) {
       sc->xnorm = xm;
       sc->wvnorm = vm;
       sc->woabs = woabs;
       sc->pad = 0.f;
+      // Every bound is +inf when its input holds a non-finite value.
+      uint32_t bits = 0;
+      if (!(xm < INFINITY)) bits |= VGGT_ATTN_RANGE_X;
+      if (!(vm < INFINITY) || !(qkm < INFINITY)) bits |= VGGT_ATTN_RANGE_WQKV;
+      if (!(woabs < INFINITY)) bits |= VGGT_ATTN_RANGE_WO;
+      // q / k features are at most 8 |gamma| + |beta| after the LayerNorm:
+      // keep them well inside fp16 (65504)
+      if (!(aq < 32768.f) || !(ak < 32768.f)) bits |= VGGT_ATTN_RANGE_AFFINE;
+      if (!bits && !af.desc) {
+        // v and Wo need a power-of-two scale within 2^+-60; |y| is at most
+        // d max|o| max|Wo| <= d max||x|| max||w_v|| max|Wo| and must stay
+        // below bf16's largest value
+        if (range_exponent_clamped(xm * vm) || range_exponent_clamped(woabs) ||
+            (double)xm * vm * woabs * (H * kDh) >= 3.0e38)
+          bits |= VGGT_ATTN_RANGE_SCALE;
+      }
+      sc->status = bits | (af.keep ? sc->status : 0u);
     }
     for (int i = tid; i < H; i += 256) sc->kmax[i] = 0.f;
   }
@@ -264,13 +316,14 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   Scalars* sc = ws_scalars(p, a);
   const bool sub = p.mode == VGGT_ATTN_MODE_SUBSAMPLED;
   // Descriptor mode: no values are projected here; the bounds of the cached
-  // values are copied in after the Wo conversion (launch_desc_load).
+  // values are copied in after the Wo conversion (launch_desc_load).  X's
+  // rows are still checked for non-finite values (its queries).
   const bool desc = p.mode == VGGT_ATTN_MODE_DESCRIPTOR;
   BoundsArgs b;
-  b.X = desc ? nullptr : a.X;
+  b.X = a.X;
   b.rows = p.rows;
   b.map = p.map;
-  b.Wv = a.Wqkv + (int64_t)2 * p.d * p.d;
+  b.Wqkv = a.Wqkv;
   b.Wo = a.Wo;
   b.d = p.d;
   b.part = reinterpret_cast<float*>(a.ws + p.off_bounds);
@@ -279,12 +332,14 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   b.base = p.base;
   b.sums = sub ? ws_sums(p, a) : nullptr;
   b.nsums = sub ? 128 * p.H : 0;
-  int grid = desc ? kBoundsO : grid_for(p.rows, 16, kBoundsX);
+  int grid = grid_for(p.rows, 16, kBoundsX);
   if (grid < kBoundsO) grid = kBoundsO;
   hipLaunchKernelGGL(bounds_kernel, dim3(grid), dim3(256), 0, st, b);
   const int64_t n8 = (int64_t)p.d * p.d / 8;
+  const AffineArgs af{a.qg, a.qb, desc ? nullptr : a.kg, desc ? nullptr : a.kb,
+                      p.keep_status ? 1 : 0, desc ? 1 : 0};
   hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
-                     n8, (const float*)b.part, grid, sc, p.H, ws_wo(p, a));
+                     n8, (const float*)b.part, grid, sc, p.H, ws_wo(p, a), af);
   if (desc) return launch_desc_load(p, a, st);
   return hipGetLastError();
 }

@@ -9,8 +9,9 @@
 //
 // Everything is checked on the host before the first launch, so a rejected
 // call enqueues nothing.  The whole forward is then 2 * n_layers block calls
-// and residual updates on one stream; the block output Y lives in the
-// workspace, ahead of the block workspace that every call reuses.
+// and residual updates on one stream; the block workspace that every call
+// reuses starts the workspace (so its range status word is the schedule's:
+// every block after the first ORs its bits in), the block output Y follows.
 #include "entry.h"
 
 namespace vggt {
@@ -85,8 +86,8 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
   const int d = shape->d;
   const size_t nx = (size_t)rows * d * 2;
   char* ws = reinterpret_cast<char*>(workspace);
-  void* Y = ws;
-  void* bws = ws + y_bytes(shape);
+  void* bws = ws;
+  void* Y = ws + blk;
   const int ncache = caches ? __builtin_popcountll(sc.cached_layers) : 0;
   const size_t ncb = (size_t)ncache * nx * 2;
   // state is X itself or disjoint from it; state and the caches stay clear of
@@ -136,6 +137,7 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
         o.sub_h = sc.sub_h;
         o.sub_w = sc.sub_w;
       }
+      o.keep_status = l > 0 || half > 0;
       const void* in = (l == 0 && half == 0) ? X : state;
       st = run(mode, o, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, shape, in, w.Wqkv, w.Wo,
                w.q_gamma, w.q_beta, w.k_gamma, w.k_beta, Y, bws, blk, stream);
