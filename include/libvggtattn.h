@@ -80,6 +80,8 @@ extern "C" {
                                      range, subsampling window < 1, row window outside the set,
                                      descriptor count outside the cache; from
                                      vggt_attn_range_status: a value range bit is set */
+#define VGGT_ATTN_ESCRATCH   (-7) /* vggt_attn_block_noalloc: the call needs more workspace than
+                                     VGGT_ATTN_STATIC_SCRATCH_BYTES */
 
 /* Value range bits, found on the device by a call's first stage and kept in
    the 32-bit status word at byte VGGT_ATTN_STATUS_OFFSET of its workspace. */
@@ -337,6 +339,31 @@ size_t vggt_attn_schedule_workspace_bytes(const vggt_attn_shape* shape,
 int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedule* sched,
                            const vggt_attn_block_weights* blocks, const void* X, void* state,
                            void* caches, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+   For callers that cannot allocate device memory -- code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc: the block
+   call of `mode` (VGGT_ATTN_MODE_FRAME, _GLOBAL or _REGISTER; anything else
+   is EINVAL) with the same arguments as vggt_attn_frame / _global /
+   _global_register minus the workspace, which is instead a static device
+   array of the library, VGGT_ATTN_STATIC_SCRATCH_BYTES bytes on every device
+   the library runs on, held until the process ends.  The call allocates
+   nothing (no hipMalloc, no allocating library routine) and computes exactly
+   what the block call of that mode computes with a workspace of its own.
+   Calls whose workspace need (vggt_attn_workspace_bytes) exceeds the array
+   return VGGT_ATTN_ESCRATCH before anything is enqueued (e.g. 128 MiB holds
+   register mode up to 500+ frames and global mode up to 9 frames of
+   26 x 39 patches at d = 1024).  All other checks and status codes are the
+   block call's.  Every call on a device shares that device's array: calls
+   that overlap in time on one device (different streams, or several host
+   threads) race; order them on one stream.  Nothing needs clearing between
+   calls.  The first call on a device looks the array's address up (one HIP
+   symbol query, no allocation). */
+#define VGGT_ATTN_STATIC_SCRATCH_BYTES (128u << 20)
+int vggt_attn_block_noalloc(int mode, const vggt_attn_shape* shape, const void* X,
+                            const void* Wqkv, const void* Wo, const float* q_gamma,
+                            const float* q_beta, const float* k_gamma, const float* k_beta,
+                            void* Y, void* stream);
 
 /* Value range check of the last call that used `workspace` (any block call
    or stage sequence above, including descriptor attention, or a whole

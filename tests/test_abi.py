@@ -154,7 +154,7 @@ def test_stage_errors():
 
 
 def test_status_strings():
-    for code in (B.OK, B.EINVAL, B.ESHAPE, B.EALIGN, B.EWORKSPACE, B.EHIP, B.ERANGE):
+    for code in (B.OK, B.EINVAL, B.ESHAPE, B.EALIGN, B.EWORKSPACE, B.EHIP, B.ERANGE, B.ESCRATCH):
         assert B.status_str(code) and B.status_str(code) != "unknown status"
     assert B.status_str(12345) == "unknown status"
     assert B.vggt_attn_version() >= 10000
@@ -425,3 +425,41 @@ def test_descriptor_attend_errors():
     assert B.vggt_attn_stage(B.MODE_DESCRIPTOR, B.STAGE_CORE, s, *a, 0x10000000, 1 << 30,
                              None) == B.EINVAL
 
+
+# ----------------------------------------------------------------------------
+# The entry point without a caller workspace
+# ----------------------------------------------------------------------------
+
+def test_noalloc_argument_errors():
+    """vggt_attn_block_noalloc: every check, the static scratch's size
+    included, returns before the first HIP call (no GPU here)."""
+    s = B.make_shape(**TINY)
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    for mode in (B.MODE_SUBSAMPLED, B.MODE_DESCRIPTOR, 7, -1):
+        assert B.vggt_attn_block_noalloc(mode, s, *a, None) == B.EINVAL
+    a0 = list(a)
+    a0[0] = 0
+    assert B.vggt_attn_block_noalloc(B.MODE_GLOBAL, s, *a0, None) == B.EINVAL
+    a1 = list(a)
+    a1[7] = a1[0]  # Y == X outside register mode
+    assert B.vggt_attn_block_noalloc(B.MODE_FRAME, s, *a1, None) == B.EINVAL
+    bad = B.make_shape(**dict(TINY, T=80))
+    assert B.vggt_attn_block_noalloc(B.MODE_GLOBAL, bad, *a, None) == B.ESHAPE
+    a2 = list(a)
+    a2[0] += 8  # X misaligned
+    assert B.vggt_attn_block_noalloc(B.MODE_GLOBAL, s, *a2, None) == B.EALIGN
+    # beyond the static scratch: the global block of 100 frames
+    far = [(i + 1) << 40 for i in range(8)]
+    assert B.vggt_attn_block_noalloc(B.MODE_GLOBAL, shape(), *far, None) == B.ESCRATCH
+    assert B.vggt_attn_block_noalloc(B.MODE_FRAME, shape(S=24), *far, None) == B.ESCRATCH
+
+
+def test_noalloc_scratch_covers_the_documented_sizes():
+    """The header promises register mode past 500 frames and global mode up
+    to 9 frames of 26 x 39 patches at d = 1024 within the static scratch."""
+    assert B.vggt_attn_workspace_bytes(B.MODE_REGISTER, shape(S=500)) <= B.STATIC_SCRATCH_BYTES
+    assert B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, shape(S=9)) <= B.STATIC_SCRATCH_BYTES
+    assert B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, shape(S=10)) > B.STATIC_SCRATCH_BYTES
+    txt = open(HEADER).read()
+    m = re.search(r"#define VGGT_ATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_SCRATCH_BYTES

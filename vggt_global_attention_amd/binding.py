@@ -13,7 +13,8 @@ import contextlib
 
 from .build import LIB, TUNE_LIB
 
-OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+STATIC_SCRATCH_BYTES = 128 << 20
 MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR = 0, 1, 2, 3, 4
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
 STATUS_OFFSET = 16
@@ -27,7 +28,8 @@ EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_desc_cache_bytes", "vggt_attn_desc_cache_init", "vggt_attn_desc_append",
            "vggt_attn_desc_attend", "vggt_attn_desc_attend_stage",
            "vggt_attn_residual", "vggt_attn_schedule_workspace_bytes", "vggt_attn_schedule_run",
-           "vggt_attn_range_status", "vggt_attn_status_str", "vggt_attn_version")
+           "vggt_attn_range_status", "vggt_attn_block_noalloc", "vggt_attn_status_str",
+           "vggt_attn_version")
 
 
 class vggt_attn_shape(ctypes.Structure):
@@ -145,6 +147,8 @@ def _load(path: str) -> ctypes.CDLL:
                                          ctypes.POINTER(vggt_attn_block_weights), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
+    L.vggt_attn_block_noalloc.restype = ctypes.c_int
+    L.vggt_attn_block_noalloc.argtypes = [ctypes.c_int] + _CALL_ARGS[:9] + [ctypes.c_void_p]
     L.vggt_attn_range_status.restype = ctypes.c_int
     L.vggt_attn_range_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32),
                                          ctypes.c_void_p]
@@ -258,6 +262,12 @@ def vggt_attn_schedule_run(shape, sched, blocks, X, state, caches, workspace, wo
     """`blocks` is a ctypes array of vggt_attn_block_weights (2 * n_layers)."""
     return _call("vggt_attn_schedule_run", ctypes.byref(shape), ctypes.byref(sched), blocks, X,
                  state, caches, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_block_noalloc(mode, shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y,
+                            stream) -> int:
+    return _call("vggt_attn_block_noalloc", mode, ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
+                 q_beta, k_gamma, k_beta, Y, stream)
 
 
 def vggt_attn_range_status(workspace, stream) -> tuple:

@@ -543,6 +543,9 @@ const char* vggt_attn_status_str(int status) {
       return "value out of range: rope_base / ln_eps must be finite and > 0, pos_offset in "
              "0..65535, sub_h / sub_w >= 1, row window inside the set; or (range status) a "
              "non-finite input or a bound beyond fp16 range";
+    case VGGT_ATTN_ESCRATCH:
+      return "the call needs more workspace than the static scratch of vggt_attn_block_noalloc "
+             "(VGGT_ATTN_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
