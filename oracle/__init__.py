@@ -26,3 +26,10 @@ from .avggt_sga import (  # noqa: F401
     sga_attention,
     sga_attention_rows,
 )
+from .httm import (  # noqa: F401
+    HttmParams,
+    httm_attention,
+    httm_attention_rows,
+    fragile_rows,
+    merged_length,
+)
