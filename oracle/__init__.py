@@ -30,6 +30,6 @@ from .httm import (  # noqa: F401
     HttmParams,
     httm_attention,
     httm_attention_rows,
-    fragile_rows,
+    fragile,
     merged_length,
 )

@@ -30,7 +30,12 @@ page's order:
    by).  A source's best destination is the one of highest similarity (ties:
    the first); the r sources of highest best-similarity (ties: the first)
    merge into their best destinations, the others stay (a block with at most
-   r sources merges them all).
+   r sources merges them all).  These are decisions taken from floating
+   point, so the oracle takes them in the kernels' precision: keys rounded to
+   fp16 (to nearest, ties to even), their products summed in fp32 in feature
+   order (`similarities`, an exact emulation: every product of two fp16
+   values is exact in fp32, and an fp32 sum rounded from fp64 is the
+   correctly rounded fp32 sum).  Everything else is fp64.
 3. Head-wise merging.  Each head decides on its own keys.  A merged token is
    a destination together with the sources merged into it; its query, key and
    value are the means over its members and its size n is their count.
@@ -95,6 +100,21 @@ def merged_length(S: int, grid_h: int, grid_w: int, hp: HttmParams) -> int:
     return N - sum(min(hp.r, len(src)) for _, src in blocks(S, grid_h, grid_w, hp))
 
 
+def fp16(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def similarities(ka: np.ndarray, kb: np.ndarray) -> np.ndarray:
+    """fp32 dot products, summed in feature order, of fp16 keys: ka [..., s, F]
+    against kb [..., d, F] -> [..., s, d] (values of fp32)."""
+    a, b = fp16(ka), fp16(kb)
+    acc = np.zeros(a.shape[:-1] + (b.shape[-2],), dtype=np.float32)
+    for f in range(a.shape[-1]):
+        prod = a[..., :, None, f] * b[..., None, :, f]   # exact: 11-bit x 11-bit significands
+        acc = (acc.astype(np.float64) + prod).astype(np.float32)
+    return acc.astype(np.float64)
+
+
 def block_decisions(kh: np.ndarray, dst: np.ndarray, src: np.ndarray, r: int):
     """Point 2 for the blocks of one shape and one head: dst [B, nd] and src
     [B, ns] token indices; returns (best destination position per source,
@@ -102,7 +122,7 @@ def block_decisions(kh: np.ndarray, dst: np.ndarray, src: np.ndarray, r: int):
     B, ns = src.shape
     if ns == 0:
         return np.zeros((B, 0), dtype=np.int64), np.zeros((B, 0), dtype=bool)
-    sim = np.einsum("bsf,bdf->bsd", kh[src], kh[dst])   # [B, sources, destinations]
+    sim = similarities(kh[src], kh[dst])                 # [B, sources, destinations]
     best = np.argmax(sim, axis=2)                        # first of equal maxima
     score = np.take_along_axis(sim, best[..., None], axis=2)[..., 0]
     order = np.argsort(-score, axis=1, kind="stable")    # ties: the earlier source
@@ -207,51 +227,85 @@ def httm_attention_rows(X: np.ndarray, p: OracleParams, hp: HttmParams, rows,
     """Y at the flat rows `rows`: merging and keys over the whole set, the
     queries of only the merged tokens those rows belong to."""
     S, T, d = _check(X, p)
+    N = S * T
     rows = np.asarray(rows, dtype=np.int64)
-    f = _qkv(X, p)
-    O = np.empty((len(rows), p.H, p.Dh))
+    f = _qkv(X, p, want=("k", "v"))
+    heads = []
+    members = np.zeros(N, dtype=bool)          # tokens whose query some merged query needs
     for h in range(p.H):
         owner, n = head_owner(f["k"][:, h], S, p.grid_h, p.grid_w, hp)
         need, back = np.unique(owner[rows], return_inverse=True)
-        og = merged_attention(f["q"][:, h], f["k"][:, h], f["v"][:, h], owner, n, need)
+        members |= np.isin(owner, need)
+        heads.append((owner, n, need, back))
+    q = np.zeros((N, p.H, p.Dh))
+    idx = np.flatnonzero(members)
+    q[idx] = _project(X.reshape(N, d).astype(np.float64)[idx], idx % T, p, want=("q",))["q"]
+    O = np.empty((len(rows), p.H, p.Dh))
+    for h, (owner, n, need, back) in enumerate(heads):
+        og = merged_attention(q[:, h], f["k"][:, h], f["v"][:, h], owner, n, need)
         O[:, h] = og[back]
     return O.reshape(len(rows), d) @ p.Wo.T
 
 
-def fragile_rows(X: np.ndarray, p: OracleParams, hp: HttmParams, rel: float = 2.0 ** -9):
-    """Tokens whose merged token could differ under a perturbation of every
-    similarity s(a, b) by up to rel * sum_i |k_a,i| |k_b,i| -- the size of the
-    differences a computation of the keys in 16-bit storage and fp32
-    arithmetic can make.  A block is fragile in a head when a source's best
-    destination, or the split between the r merged sources and the rest, is
-    decided by less than the similarities' perturbations; all its tokens are
-    then fragile (in every head: a token's output row mixes all heads).
-    Boolean [S*T]."""
+def fragile(X: np.ndarray, p: OracleParams, hp: HttmParams, rel: float = 2.0 ** -8,
+            terms: int = 2, rows=None):
+    """(token, head) pairs whose merged token a GPU computation could make
+    differ from the oracle's.  The kernels decide from the same fp16 keys and
+    fp32 sums as `similarities` wherever their fp16 keys equal the oracle's
+    rounding of its fp64 keys; a key element can come out one fp16 unit (at
+    most 2^-10 of it) apart where their fp32 arithmetic lands on the other
+    side of a rounding boundary.  A decision is fragile when it is closer than
+    rel times the sum of the `terms` largest |k_a,i k_b,i| of each of the two
+    similarities involved (room for a few such elements): a source's best
+    destination against its runner-up, or the split between the r merged
+    sources of a block and the rest.  All tokens of such a block are flagged
+    in that head.  Boolean [S*T, H], or [len(rows), H] for the flat token
+    indices `rows` (then only the blocks holding them are looked at)."""
     S, T, d = _check(X, p)
-    k = _qkv(X, p, want=("k",))["k"]
-    frag = np.zeros(S * T, dtype=bool)
+    N = S * T
+    shapes, _, _ = _block_shapes(S, p.grid_h, p.grid_w, hp)
+    if rows is None:
+        k = _qkv(X, p, want=("k",))["k"]
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        hit = np.zeros(N, dtype=bool)
+        hit[rows] = True
+        keep = []
+        for ids, dst, src in shapes:
+            sel = hit[dst].any(axis=1) | hit[src].any(axis=1)
+            keep.append((ids[sel], dst[sel], src[sel]))
+        shapes = keep
+        need = np.unique(np.concatenate([np.concatenate([dst.ravel(), src.ravel()])
+                                         for _, dst, src in shapes] + [np.zeros(0, np.int64)]))
+        k = np.zeros((N, p.H, p.Dh))
+        if len(need):
+            Xf = X.reshape(N, d).astype(np.float64)
+            k[need] = _project(Xf[need], need % T, p, want=("k",))["k"]
+    frag = np.zeros((N, p.H), dtype=bool)
     for h in range(p.H):
-        kh = k[:, h]
-        ka = np.abs(kh)
-        for dst, src in blocks(S, p.grid_h, p.grid_w, hp):
-            if len(src) == 0:
+        kh16 = fp16(k[:, h])
+        for ids, dst, src in shapes:
+            B, ns = src.shape
+            nd = dst.shape[1]
+            if ns == 0:
                 continue
-            sim = kh[src] @ kh[dst].T
-            eps = rel * (ka[src] @ ka[dst].T)
-            best = np.argmax(sim, axis=1)
-            i = np.arange(len(src))
-            score, e_best = sim[i, best], eps[i, best]
-            bad = False
-            if len(dst) > 1:
-                others = (sim + eps) - (score - e_best)[:, None]
-                others[i, best] = -np.inf
-                bad = bool((others >= 0).any())
-            r = min(hp.r, len(src))
-            if not bad and 0 < r < len(src):
-                order = sorted(range(len(src)), key=lambda j: (-score[j], j))
-                top, rest = np.array(order[:r]), np.array(order[r:])
-                bad = (score[top] - e_best[top]).min() <= (score[rest] + e_best[rest]).max()
-            if bad:
-                frag[dst] = True
-                frag[src] = True
-    return frag
+            sim = similarities(kh16[src], kh16[dst])                  # [B, ns, nd]
+            prod = np.abs(kh16[src][:, :, None, :] * kh16[dst][:, None, :, :])
+            eps = rel * np.sort(prod, axis=-1)[..., -terms:].sum(axis=-1)
+            best = np.argmax(sim, axis=2)
+            score = np.take_along_axis(sim, best[..., None], axis=2)[..., 0]
+            e_best = np.take_along_axis(eps, best[..., None], axis=2)[..., 0]
+            bad = np.zeros(B, dtype=bool)
+            if nd > 1:
+                gap = (score - e_best)[..., None] - (sim + eps)
+                np.put_along_axis(gap, best[..., None], np.inf, axis=2)
+                bad |= (gap <= 0).any(axis=(1, 2))
+            r = min(hp.r, ns)
+            if 0 < r < ns:
+                order = np.argsort(-score, axis=1, kind="stable")
+                lo = np.take_along_axis(score - e_best, order[:, :r], axis=1).min(axis=1)
+                hi = np.take_along_axis(score + e_best, order[:, r:], axis=1).max(axis=1)
+                bad |= lo <= hi
+            frag[dst[bad].ravel(), h] = True
+            frag[src[bad].ravel(), h] = True
+    return frag if rows is None else frag[rows]

@@ -7,6 +7,8 @@ oracle's reading is pinned by:
 * a pure-Python per-token construction of the same reading (blocks,
   similarities, best destinations, the r best sources, means, size-weighted
   softmax, unmerging), written without the oracle's vectorised code;
+* the similarity emulation (fp16 keys, fp32 sums in feature order) against
+  NumPy's own float32 arithmetic;
 * r = 0: exactly the global block;
 * exact duplicates: with every frame run made of identical frames, a uniform
   QK-norm gain and no shift, every source's best destination is its own twin
@@ -52,12 +54,19 @@ def bf_httm(X, p, hp):
                                [(s, t) for s in run[1:] for t in cells]))
     out = {}
     for h in range(H):
-        key = lambda tok: feats[tok][h][1]  # noqa: E731
+        # decisions in the kernels' precision: fp16 keys, fp32 sums in feature order
+        key = lambda tok: [float(np.float16(x)) for x in feats[tok][h][1]]  # noqa: E731
+
+        def sim32(ka, kb):
+            acc = np.float32(0.0)
+            for x, y in zip(ka, kb):
+                acc = np.float32(acc + np.float32(x) * np.float32(y))
+            return float(acc)
         groups = [[(s, t)] for s in range(S) for t in range(17)]
         for dst, src in blocks:
             best, score = [], []
             for a in src:
-                sims = [sum(x * y for x, y in zip(key(a), key(b))) for b in dst]
+                sims = [sim32(key(a), key(b)) for b in dst]
                 j = max(range(len(dst)), key=lambda i: (sims[i], -i))
                 best.append(j)
                 score.append(sims[j])
@@ -83,6 +92,23 @@ def bf_httm(X, p, hp):
         o = [z for hh in heads for z in hh]
         Y[s, t] = [sum(p.Wo[j][i] * o[i] for i in range(d)) for j in range(d)]
     return Y
+
+
+def test_similarities_are_fp32_sums_of_fp16_products():
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((3, 5, 64)) * 3
+    b = rng.standard_normal((3, 4, 64)) * 3
+    got = httm.similarities(a, b)
+    a16, b16 = a.astype(np.float16).astype(np.float32), b.astype(np.float16).astype(np.float32)
+    for i in range(3):
+        for s_ in range(5):
+            for d_ in range(4):
+                acc = np.float32(0.0)
+                for f in range(64):
+                    acc = np.float32(acc + a16[i, s_, f] * b16[i, d_, f])
+                assert got[i, s_, d_] == float(acc)
+    # and not the fp64 dot of the unrounded keys
+    assert not np.array_equal(got, np.einsum("bsf,bdf->bsd", a, b))
 
 
 def close(a, b, tol=1e-12):
@@ -169,19 +195,28 @@ def test_rows_variant_matches_full():
     assert close(httm.httm_attention_rows(X, p, hp, rows), y[rows])
 
 
-def test_fragile_rows_flag_a_tie():
+def test_fragile_flags_a_near_tie():
     """Copying one destination's token state onto its neighbour cell gives two
     destinations whose keys differ only by a one-cell rotation: the sources'
-    best destination is then decided by a hair and the block's tokens are
-    flagged (more tokens than before)."""
+    best destination is then decided by a hair, and the block's tokens are
+    flagged in more heads than before."""
     X, p = small_case(S=2, gh=1, gw=4, d=64, H=2, seed=11)
     hp = httm.HttmParams(2, 1, 2, 1)
     T = X.shape[1]
-    frag0 = httm.fragile_rows(X, p, hp)
-    X[0, 18] = X[0, 17]            # window 0's two destinations: nearly equal keys
-    frag = httm.fragile_rows(X, p, hp)
-    assert frag[[17, 18, T + 17, T + 18]].all()
+    frag0 = httm.fragile(X, p, hp)
+    X[0, 18] = X[0, 17]
+    frag = httm.fragile(X, p, hp)
+    assert frag.shape == (2 * T, 2)
     assert frag0.sum() < frag.sum()
+    assert not frag[:17].any() and not frag[T:T + 17].any()   # special tokens never merge
+
+
+def test_fragile_rows_form_matches_full():
+    X, p = small_case(S=5, gh=3, gw=7, d=128, H=2, seed=12)
+    hp = httm.HttmParams(3, 2, 3, 4)
+    full = httm.fragile(X, p, hp)
+    rows = np.array([0, 17, 30, 40, 2 * X.shape[1] + 20, 4 * X.shape[1] + 37])
+    assert np.array_equal(httm.fragile(X, p, hp, rows=rows), full[rows])
 
 
 # ----------------------------------------------------------------------------
