@@ -118,7 +118,10 @@ def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None):
         blk = api.RowsBlock(d["X"], w.H, w.grid_h, w.grid_w, rows[0], rows[1])
         Y = torch.empty((rows[1], w.d), dtype=d["X"].dtype, device=d["X"].device)
     else:
-        blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
+        if mode == "merged":
+            blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, merge=sub)
+        else:
+            blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
         Y = torch.empty_like(d["X"])
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -603,23 +606,31 @@ def main():
         out["roofline"]["kernel"] = "CORE stage: K/V gather + discarded sums + attn_kernel<SGA>"
     if not a.no_extra and a.workload == "s100" and a.mode == "global":
         extra = {}
-        for name, mode, esub in (("s24", "global", (1, 1)), ("s24", "frame", (1, 1)),
-                                 ("s500", "frame", (1, 1)), ("s500", "register", (1, 1)),
-                                 ("s100", "subsampled", (3, 3)),
-                                 ("s300", "subsampled", (3, 3))):
+        httm = (4, 2, 3, 12)   # 4-frame runs, 2 x 3 windows, 12 of 18 sources merged
+        runs = (("s24", (("global", (1, 1)), ("frame", (1, 1)))),
+                ("s500", (("frame", (1, 1)), ("register", (1, 1)))),
+                ("s100", (("subsampled", (3, 3)), ("merged", httm))),
+                ("s300", (("global", (1, 1)), ("subsampled", (3, 3)), ("merged", httm))))
+        for name, modes in runs:
             ww = configs.WORKLOADS[name]
-            print(f"[bench] extra {name} {mode} {esub}", file=sys.stderr, flush=True)
-            if name == a.workload:
-                dd = d
-            else:
-                _, dd = gpu_inputs(ww)
-            m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub)
-            key = f"{name}_{mode}" + (f"{esub[0]}x{esub[1]}" if mode == "subsampled" else "")
-            extra[key] = {"ms_per_layer": m2, "tflops": ww.flop(mode, esub) / m2 / 1e9,
-                          "core_ms": c2,
-                          "core_tflops": ww.attention_flop(mode, esub) / c2 / 1e9}
-            if mode == "subsampled":
-                extra[key]["kept_keys"] = ww.kept_keys(*esub)
+            dd = d if name == a.workload else gpu_inputs(ww)[1]
+            for mode, esub in modes:
+                print(f"[bench] extra {name} {mode} {esub}", file=sys.stderr, flush=True)
+                m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub)
+                key = f"{name}_{mode}"
+                if mode == "subsampled":
+                    key += f"{esub[0]}x{esub[1]}"
+                elif mode == "merged":
+                    key += "_F{}w{}x{}r{}".format(*esub)
+                # merged mode: FLOP of the attention over the merged tokens
+                # (the merge and unmerge kernels run inside core_ms)
+                extra[key] = {"ms_per_layer": m2, "tflops": ww.flop(mode, esub) / m2 / 1e9,
+                              "core_ms": c2,
+                              "core_tflops": ww.attention_flop(mode, esub) / c2 / 1e9}
+                if mode == "subsampled":
+                    extra[key]["kept_keys"] = ww.kept_keys(*esub)
+                if mode == "merged":
+                    extra[key]["merged_tokens"] = ww.merged_tokens(*esub)
             if dd is not d:
                 del dd
             torch.cuda.empty_cache()

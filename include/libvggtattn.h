@@ -102,6 +102,7 @@ extern "C" {
 #define VGGT_ATTN_MODE_REGISTER 2
 #define VGGT_ATTN_MODE_SUBSAMPLED 3 /* global mode, AVGGT subsampled keys / values */
 #define VGGT_ATTN_MODE_DESCRIPTOR 4 /* every token attends to a descriptor key / value cache */
+#define VGGT_ATTN_MODE_MERGED     5 /* global mode, HTTM head-wise temporal token merging */
 
 /* Stages of one call, in order (see vggt_attn_stage). */
 #define VGGT_ATTN_STAGE_PREP 0 /* range bounds, RoPE table, fp16 copy of Wo */
@@ -164,6 +165,44 @@ int vggt_attn_global_subsampled(const vggt_attn_shape* shape, int32_t sub_h, int
                                 const float* q_gamma, const float* q_beta,
                                 const float* k_gamma, const float* k_beta, void* Y,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Global mode with HTTM head-wise temporal token merging ("HTTM: Head-wise
+   Temporal Token Merging for Faster VGGT", 10100.com, sections 02, 04, 05):
+   merging shortens the query, key and value sequences, every head merging on
+   its own, inside spatio-temporal blocks.  The page names the parts, not the
+   rule; this call's reading:
+     - blocks: frames in consecutive runs of `frames` (the last run may be
+       shorter) x the patch grid in windows of win_h x win_w cells (row-major,
+       cut by the grid edge); the 17 special tokens of every frame never merge;
+     - per head and block: destinations = the run's first frame's patches,
+       sources = the other frames' patches (frame by frame, row-major); a
+       source's similarity to a destination is the dot product of their
+       normalised, rotated keys in that head (fp16 keys, fp32 sum in feature
+       order); each source takes its most similar destination (ties: the
+       first), and the r sources of highest similarity (ties: the first)
+       merge into theirs;
+     - a merged token's query, key and value are its members' means; in the
+       softmax a merged key counts n times (weight n exp(logit), n = members);
+       every token takes its merged token's output, per head; heads
+       concatenated, times Wo^T.
+   r = 0 is the global block (up to the fp32 summation order).  Requires
+   frames, win_h, win_w >= 1, r >= 0 and min(frames, S) * min(win_h, grid_h) *
+   grid_w <= 400 (else VGGT_ATTN_ERANGE).  Workspace:
+   vggt_attn_workspace_bytes(VGGT_ATTN_MODE_MERGED) (covers every parameter
+   choice). */
+int vggt_attn_global_merged(const vggt_attn_shape* shape, int32_t frames, int32_t win_h,
+                            int32_t win_w, int32_t r, const void* X, const void* Wqkv,
+                            const void* Wo, const float* q_gamma, const float* q_beta,
+                            const float* k_gamma, const float* k_beta, void* Y, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* One stage of vggt_attn_global_merged, as vggt_attn_stage (the CORE stage
+   merges, attends and unmerges). */
+int vggt_attn_merged_stage(int stage, const vggt_attn_shape* shape, int32_t frames, int32_t win_h,
+                           int32_t win_w, int32_t r, const void* X, const void* Wqkv,
+                           const void* Wo, const float* q_gamma, const float* q_beta,
+                           const float* k_gamma, const float* k_beta, void* Y, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Rows [row_begin, row_begin + row_count) of the global block's output: the
    queries of those tokens (flat index s*T + t) attend to every token of the

@@ -463,3 +463,45 @@ def test_noalloc_scratch_covers_the_documented_sizes():
     txt = open(HEADER).read()
     m = re.search(r"#define VGGT_ATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
     assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_SCRATCH_BYTES
+
+
+# ----------------------------------------------------------------------------
+# Merged mode (HTTM)
+# ----------------------------------------------------------------------------
+
+def merged_fn(frames, wh, ww, r):
+    def fn(s, *rest):
+        return B.vggt_attn_global_merged(s, frames, wh, ww, r, *rest)
+    return fn
+
+
+def test_merged_workspace_bytes():
+    s = shape()
+    m = B.vggt_attn_workspace_bytes(B.MODE_MERGED, s)
+    g = B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, s)
+    # the merged queries / keys / values and sizes come on top of the global layout
+    assert m > g + 3 * 16 * 103100 * 64 * 2
+
+
+@pytest.mark.parametrize("params,code", [
+    ((0, 2, 3, 4), B.ERANGE),     # no frames per block
+    ((2, 0, 3, 4), B.ERANGE),     # no window rows
+    ((2, 2, 0, 4), B.ERANGE),     # no window columns
+    ((2, 2, 3, -1), B.ERANGE),    # negative merges
+    ((11, 1, 3, 4), B.ERANGE),    # 11 frames x 1 row x 39 columns = 429 > 400 strip tokens
+])
+def test_merged_parameter_errors(params, code):
+    s = shape()
+    far = [(i + 1) << 40 for i in range(8)]
+    ws = B.vggt_attn_workspace_bytes(B.MODE_MERGED, s)
+    assert merged_fn(*params)(s, *far, 1 << 46, ws, None) == code
+
+
+def test_merged_stage_errors():
+    s = B.make_shape(**TINY)
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    ws = B.vggt_attn_workspace_bytes(B.MODE_MERGED, s)
+    assert B.vggt_attn_merged_stage(9, s, 2, 2, 2, 1, *a, 0x10000000, ws, None) == B.EINVAL
+    assert B.vggt_attn_stage(B.MODE_MERGED, B.STAGE_CORE, s, *a, 0x10000000, ws, None) == B.EINVAL
+    assert B.vggt_attn_merged_stage(B.STAGE_CORE, s, 2, 2, 2, 1, *a, 0x10000000, 16, None) == \
+        B.EWORKSPACE

@@ -11,7 +11,8 @@ import torch
 from . import binding as B
 
 _ENTRY = {"frame": "vggt_attn_frame", "global": "vggt_attn_global",
-          "register": "vggt_attn_global_register", "subsampled": "vggt_attn_global_subsampled"}
+          "register": "vggt_attn_global_register", "subsampled": "vggt_attn_global_subsampled",
+          "merged": "vggt_attn_global_merged"}
 
 
 def shape_of(X: torch.Tensor, H: int, grid_h: int, grid_w: int, rope_base=100.0,
@@ -50,11 +51,14 @@ class Block:
     """One attention block configuration with its workspace, reusable across calls."""
 
     def __init__(self, mode: str, X: torch.Tensor, H: int, grid_h: int, grid_w: int,
-                 rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None, sub=(1, 1)):
+                 rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None, sub=(1, 1),
+                 merge=(2, 1, 1, 0)):
         if mode not in _ENTRY:
             raise ValueError(f"unknown mode {mode!r}")
         self.mode = mode
         self.sub = (int(sub[0]), int(sub[1]))  # subsampled mode: (sub_h, sub_w) windows
+        # merged mode: (frames per block, window rows, window columns, merges per block)
+        self.merge = tuple(int(x) for x in merge)
         self.shape = shape_of(X, H, grid_h, grid_w, rope_base, ln_eps, pos_offset)
         need = workspace_bytes(mode, self.shape)
         if workspace is None:
@@ -74,6 +78,9 @@ class Block:
         if self.mode == "subsampled":
             st = B.vggt_attn_global_subsampled(args[0], *self.sub, *args[1:],
                                                _stream_handle(stream))
+        elif self.mode == "merged":
+            st = B.vggt_attn_global_merged(args[0], *self.merge, *args[1:],
+                                           _stream_handle(stream))
         else:
             st = getattr(B, _ENTRY[self.mode])(*args, _stream_handle(stream))
         if st != B.OK:
@@ -85,6 +92,9 @@ class Block:
         if self.mode == "subsampled":
             st = B.vggt_attn_subsampled_stage(stage, args[0], *self.sub, *args[1:],
                                               _stream_handle(stream))
+        elif self.mode == "merged":
+            st = B.vggt_attn_merged_stage(stage, args[0], *self.merge, *args[1:],
+                                          _stream_handle(stream))
         else:
             st = B.vggt_attn_stage(B.MODES[self.mode], stage, *args, _stream_handle(stream))
         if st != B.OK:
@@ -125,8 +135,9 @@ class RowsBlock:
 
 
 def attention(mode: str, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, H: int, grid_h: int,
-              grid_w: int, Y=None, stream=None, sub=(1, 1), **shape_kw):
-    """One call of the block in `mode` ('frame', 'global', 'register' or 'subsampled';
-    `sub` = (sub_h, sub_w) windows of the subsampled mode)."""
-    blk = Block(mode, X, H, grid_h, grid_w, sub=sub, **shape_kw)
+              grid_w: int, Y=None, stream=None, sub=(1, 1), merge=(2, 1, 1, 0), **shape_kw):
+    """One call of the block in `mode` ('frame', 'global', 'register', 'subsampled' or
+    'merged'; `sub` = (sub_h, sub_w) windows of the subsampled mode, `merge` = (frames,
+    window rows, window columns, merges per block) of the merged mode)."""
+    blk = Block(mode, X, H, grid_h, grid_w, sub=sub, merge=merge, **shape_kw)
     return blk(X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y=Y, stream=stream)

@@ -15,16 +15,18 @@ from .build import LIB, TUNE_LIB
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, ERANGE, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 STATIC_SCRATCH_BYTES = 128 << 20
-MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR = 0, 1, 2, 3, 4
+MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR, MODE_MERGED = \
+    0, 1, 2, 3, 4, 5
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
 STATUS_OFFSET = 16
 RANGE_X, RANGE_WQKV, RANGE_WO, RANGE_AFFINE, RANGE_SCALE = 1, 2, 4, 8, 16
 MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
-         "subsampled": MODE_SUBSAMPLED, "descriptor": MODE_DESCRIPTOR}
+         "subsampled": MODE_SUBSAMPLED, "descriptor": MODE_DESCRIPTOR, "merged": MODE_MERGED}
 
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_global_rows",
            "vggt_attn_stage", "vggt_attn_subsampled_stage", "vggt_attn_global_rows_stage",
+           "vggt_attn_global_merged", "vggt_attn_merged_stage",
            "vggt_attn_desc_cache_bytes", "vggt_attn_desc_cache_init", "vggt_attn_desc_append",
            "vggt_attn_desc_attend", "vggt_attn_desc_attend_stage",
            "vggt_attn_residual", "vggt_attn_schedule_workspace_bytes", "vggt_attn_schedule_run",
@@ -116,6 +118,11 @@ def _load(path: str) -> ctypes.CDLL:
     L.vggt_attn_global_subsampled.argtypes = sub
     L.vggt_attn_subsampled_stage.restype = ctypes.c_int
     L.vggt_attn_subsampled_stage.argtypes = [ctypes.c_int] + sub
+    mrg = [ctypes.POINTER(vggt_attn_shape)] + [ctypes.c_int32] * 4 + _CALL_ARGS[1:]
+    L.vggt_attn_global_merged.restype = ctypes.c_int
+    L.vggt_attn_global_merged.argtypes = mrg
+    L.vggt_attn_merged_stage.restype = ctypes.c_int
+    L.vggt_attn_merged_stage.argtypes = [ctypes.c_int] + mrg
     win = [ctypes.POINTER(vggt_attn_shape), ctypes.c_int64, ctypes.c_int64] + _CALL_ARGS[1:]
     L.vggt_attn_global_rows.restype = ctypes.c_int
     L.vggt_attn_global_rows.argtypes = win
@@ -205,6 +212,18 @@ def vggt_attn_subsampled_stage(stage, shape, sub_h, sub_w, X, Wqkv, Wo, q_gamma,
                                k_gamma, k_beta, Y, workspace, workspace_bytes, stream) -> int:
     return _call("vggt_attn_subsampled_stage", stage, ctypes.byref(shape), sub_h, sub_w, X, Wqkv,
                  Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_global_merged(shape, frames, win_h, win_w, r, X, Wqkv, Wo, q_gamma, q_beta,
+                            k_gamma, k_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_global_merged", ctypes.byref(shape), frames, win_h, win_w, r, X, Wqkv,
+                 Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_merged_stage(stage, shape, frames, win_h, win_w, r, X, Wqkv, Wo, q_gamma, q_beta,
+                           k_gamma, k_beta, Y, workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_merged_stage", stage, ctypes.byref(shape), frames, win_h, win_w, r, X,
+                 Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
 
 
 def vggt_attn_global_rows(shape, row_begin, row_count, X, Wqkv, Wo, q_gamma, q_beta, k_gamma,

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libvggtattn.so")
 # sweeps and for the tests that force a choice.  Never the product library.
 TUNE_LIB = os.path.join(PKG, "libvggtattn_tune.so")
 SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip", "subsample.hip",
-           "desc.hip", "schedule.cpp", "static_scratch.hip"]
+           "desc.hip", "schedule.cpp", "static_scratch.hip", "merge.hip"]
 
 # Packed fp32 VALU ops are kept out of every kernel on purpose.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

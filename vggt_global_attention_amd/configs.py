@@ -48,12 +48,29 @@ class Workload:
         sub_h x sub_w window, in every frame."""
         return self.S * (N_SPECIAL + (-(-self.grid_h // sub_h)) * (-(-self.grid_w // sub_w)))
 
+    def merged_tokens(self, frames: int, win_h: int, win_w: int, r: int) -> int:
+        """Length of the merged sequence of HTTM merging: blocks of `frames`
+        consecutive frames x win_h x win_w patch cells (cut at the ends), the
+        first frame's patches of a block its destinations, the rest its
+        sources, min(r, sources) merges per block; special tokens stay."""
+        m = self.N
+        for f0 in range(0, self.S, frames):
+            nf = min(frames, self.S - f0)
+            for r0 in range(0, self.grid_h, win_h):
+                for c0 in range(0, self.grid_w, win_w):
+                    cells = min(win_h, self.grid_h - r0) * min(win_w, self.grid_w - c0)
+                    m -= min(r, (nf - 1) * cells)
+        return m
+
     def attention_flop(self, mode: str, sub=(1, 1)) -> float:
         """4 * sum(L^2) * d over the attention sets of one block (2 FLOP per MAC);
         subsampled mode: 4 * N * (kept keys) * d (the two per-row extra columns
-        are not counted)."""
+        are not counted); merged mode (sub = the four merge parameters): 4 M^2 d
+        over the M merged tokens."""
         if mode == "subsampled":
             return 4.0 * self.N * self.kept_keys(*sub) * self.d
+        if mode == "merged":
+            return 4.0 * self.merged_tokens(*sub) ** 2 * self.d
         if mode == "frame":
             return 4.0 * self.S * self.T ** 2 * self.d
         if mode == "global":

@@ -52,7 +52,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   if (!s || !p) return VGGT_ATTN_EINVAL;
   if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
       mode != VGGT_ATTN_MODE_REGISTER && mode != VGGT_ATTN_MODE_SUBSAMPLED &&
-      mode != VGGT_ATTN_MODE_DESCRIPTOR)
+      mode != VGGT_ATTN_MODE_DESCRIPTOR && mode != VGGT_ATTN_MODE_MERGED)
     return VGGT_ATTN_EINVAL;
   if (s->S < 1 || s->H < 1 || s->d < 1 || s->grid_h < 0 || s->grid_w < 0) return VGGT_ATTN_ESHAPE;
   if (s->d != s->H * kDh || s->d % kGemmBN != 0) return VGGT_ATTN_ESHAPE;
@@ -65,6 +65,16 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   if (s->pos_offset < 0 || s->pos_offset > 65535) return VGGT_ATTN_ERANGE;
   const bool subsampled = mode == VGGT_ATTN_MODE_SUBSAMPLED;
   const bool desc = mode == VGGT_ATTN_MODE_DESCRIPTOR;
+  const bool merged = mode == VGGT_ATTN_MODE_MERGED;
+  // merged mode: frames == 0 sizes the workspace for the largest merged set
+  // (nothing merges); a call passes its blocks and merges
+  const bool msize = merged && o.httm_frames == 0;
+  if (merged && !msize) {
+    if (o.httm_frames < 1 || o.httm_wh < 1 || o.httm_ww < 1 || o.httm_r < 0) return VGGT_ATTN_ERANGE;
+    const int64_t nf = o.httm_frames < s->S ? o.httm_frames : s->S;
+    const int64_t wh = o.httm_wh < s->grid_h ? o.httm_wh : s->grid_h;
+    if (nf * wh * s->grid_w > kMergeStripMax) return VGGT_ATTN_ERANGE;
+  }
   if (desc && (o.desc_capacity < 0 || o.desc_capacity >= ((int64_t)1 << 31) ||
                o.desc_count < 0 || o.desc_count > o.desc_capacity))
     return VGGT_ATTN_ERANGE;
@@ -90,7 +100,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   p->keep_status = o.keep_status;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
-  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {
     p->nseq = 1;
     p->L = (int)N;
     p->seq_stride = round_up(N, kAttnBK);
@@ -135,6 +145,34 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     // the subsampled kernel has a single tile shape
     p->attn_qb = 2;
     p->attn_waves = 8;
+  } else if (merged) {
+    // queries, keys and values: the merged tokens (as many as the tokens when
+    // only sizing)
+    int64_t M = N;
+    if (!msize) {
+      const int F = o.httm_frames, r = o.httm_r;
+      const int nwr = s->grid_w > 0 ? (s->grid_h + o.httm_wh - 1) / o.httm_wh : 0;
+      const int full = s->S / F, rest = s->S % F;
+      p->hper_run = merged_run_count(F, s->grid_h, s->grid_w, o.httm_wh, o.httm_ww, r, nwr);
+      M = (int64_t)kSpecial * s->S + full * p->hper_run +
+          (rest ? merged_run_count(rest, s->grid_h, s->grid_w, o.httm_wh, o.httm_ww, r, nwr) : 0);
+      p->hf = F;
+      p->hwh = o.httm_wh;
+      p->hww = o.httm_ww;
+      p->hr = r;
+      // a merged token has at most 1 + min(r, (F - 1) wh ww) members: its
+      // value sum carries 2^-hshift so that it stays inside fp16
+      const int64_t cells = (int64_t)(o.httm_wh < s->grid_h ? o.httm_wh : s->grid_h) *
+                            (o.httm_ww < s->grid_w ? o.httm_ww : s->grid_w);
+      const int64_t src = (int64_t)((F < s->S ? F : s->S) - 1) * cells;
+      const int64_t nmax = 1 + (src < r ? src : (int64_t)r);
+      while (((int64_t)1 << p->hshift) < nmax) ++p->hshift;
+    }
+    p->L = (int)M;
+    p->Lk = (int)M;
+    p->kv_rows = round_up(M, kKvAlign);
+    p->kv_seq_stride = round_up(M, kAttnBK);
+    p->nD = 0;
   } else if (desc) {
     // keys / values: the first desc_count entries of the caller's cache
     p->desc = desc_layout(s->H, o.desc_capacity > 0 ? o.desc_capacity : 1);
@@ -148,7 +186,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->kv_seq_stride = p->seq_stride;
     p->nD = 0;
   }
-  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {
     p->map = RowMap{p->rows, 0, (int32_t)N, 1, 0};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->map = RowMap{p->seq_stride, s->T, s->T, s->S, 0};
@@ -170,7 +208,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   // times as many, up to three per CU.  Both tiles compute every row the
   // same way, bit for bit.
   const int64_t cus = o.cus > 0 ? o.cus : 256;
-  if ((mode == VGGT_ATTN_MODE_GLOBAL || desc) && !tile_forced &&
+  if ((mode == VGGT_ATTN_MODE_GLOBAL || desc || merged) && !tile_forced &&
       (int64_t)(p->L - p->q0 + 511) / 512 * s->H < cus) {
     p->attn_qb = 1;
     p->attn_waves = 4;
@@ -207,6 +245,21 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->off_v = off;
     off += qkv;
   }
+  if (merged) {
+    // merged queries, keys, values and key sizes, kv_rows per head (sized for
+    // the largest set when only sizing), and every token's merged token
+    const size_t mq = (size_t)s->H * (size_t)p->kv_rows * kDh * 2;
+    p->off_qc = off;
+    off += mq;
+    p->off_kc = off;
+    off += mq;
+    p->off_vc = off;
+    off += mq;
+    p->off_nw = off;
+    off += round_up((int64_t)s->H * p->kv_rows * 2, 256);
+    p->off_owner = off;
+    off += round_up((int64_t)s->H * N * 4, 256);
+  }
   if (subsampled) {
     // compact keys / values sized for the largest kept set (sub_h = sub_w = 1:
     // every token), so the workspace size does not depend on the windows
@@ -230,7 +283,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   // which tile the device's CU count picks.
   p->split_cap = 0;
   p->off_split = off;
-  if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER || subsampled) {
+  if (mode == VGGT_ATTN_MODE_GLOBAL || mode == VGGT_ATTN_MODE_REGISTER || subsampled || merged) {
     int64_t ways = (p->Lk + kAttnBK - 1) / kAttnBK / kSplitMinTiles;
     if (ways > kSplitMaxWays) ways = kSplitMaxWays;
     if (ways >= 2) {
@@ -324,7 +377,9 @@ int run(int mode, const CallOpts& o, int first_stage, int last_stage,
       case VGGT_ATTN_STAGE_QKV: e = launch_qkv(plan, a, hs); break;
       case VGGT_ATTN_STAGE_CORE:
         if (plan.mode == VGGT_ATTN_MODE_SUBSAMPLED) e = launch_subsample(plan, a, hs);
+        if (plan.mode == VGGT_ATTN_MODE_MERGED) e = launch_merge(plan, a, hs);
         if (e == hipSuccess) e = launch_core(plan, a, hs);
+        if (e == hipSuccess && plan.mode == VGGT_ATTN_MODE_MERGED) e = launch_unmerge(plan, a, hs);
         break;
       case VGGT_ATTN_STAGE_OUT: e = launch_out(plan, a, hs); break;
     }
@@ -387,8 +442,9 @@ int vggt_attn_global_register(VGGT_ARGS) {
 
 int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {
   if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
-  // these modes need the windows / the cache: they have stage entries of their own
-  if (mode == VGGT_ATTN_MODE_SUBSAMPLED || mode == VGGT_ATTN_MODE_DESCRIPTOR)
+  // these modes need windows / a cache / blocks: they have stage entries of their own
+  if (mode == VGGT_ATTN_MODE_SUBSAMPLED || mode == VGGT_ATTN_MODE_DESCRIPTOR ||
+      mode == VGGT_ATTN_MODE_MERGED)
     return VGGT_ATTN_EINVAL;
   return run(mode, CallOpts(), stage, stage, VGGT_PASS);
 }
@@ -414,6 +470,34 @@ int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t 
   o.sub_h = sub_h;
   o.sub_w = sub_w;
   return run(VGGT_ATTN_MODE_SUBSAMPLED, o, stage, stage, VGGT_PASS);
+}
+
+static CallOpts merged_opts(int32_t frames, int32_t win_h, int32_t win_w, int32_t r) {
+  CallOpts o;
+  // 0 frames would mean "sizing only" to the planner: a call passes >= 1
+  o.httm_frames = frames < 1 ? -1 : frames;
+  o.httm_wh = win_h;
+  o.httm_ww = win_w;
+  o.httm_r = r;
+  return o;
+}
+
+int vggt_attn_global_merged(const vggt_attn_shape* shape, int32_t frames, int32_t win_h,
+                            int32_t win_w, int32_t r, const void* X, const void* Wqkv,
+                            const void* Wo, const float* q_gamma, const float* q_beta,
+                            const float* k_gamma, const float* k_beta, void* Y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return run(VGGT_ATTN_MODE_MERGED, merged_opts(frames, win_h, win_w, r), VGGT_ATTN_STAGE_PREP,
+             VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_merged_stage(int stage, const vggt_attn_shape* shape, int32_t frames, int32_t win_h,
+                           int32_t win_w, int32_t r, const void* X, const void* Wqkv,
+                           const void* Wo, const float* q_gamma, const float* q_beta,
+                           const float* k_gamma, const float* k_beta, void* Y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT) return VGGT_ATTN_EINVAL;
+  return run(VGGT_ATTN_MODE_MERGED, merged_opts(frames, win_h, win_w, r), stage, stage, VGGT_PASS);
 }
 
 int vggt_attn_global_rows(const vggt_attn_shape* shape, int64_t row_begin, int64_t row_count,

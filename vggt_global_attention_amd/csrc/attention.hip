@@ -102,6 +102,9 @@ struct AttnArgs {
   // [units][BQ] float2 (m, l), units = 8 * umax)
   int split_p, xcd_slots, umax;
   float* part;
+  // merged mode only: the size of every merged key, [H][kv_rows] (0 past the
+  // set); key j enters the softmax with weight nw[j] exp(logit)
+  const f16* nw;
 };
 
 // LDS tiles are 64 rows x 128 bytes.  An MFMA operand read takes one 16-byte
@@ -236,14 +239,14 @@ __device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t se
 // needed (below) the max of every row that is not settled moves or pins its
 // reference first -- to the exact running max while `eager`, else only when
 // the tile's max exceeds m + kTau; then P = 2^S in fp16 into pf, and the row
-// sums.  KB = 2 (a short last tile of at most 32 keys): key
-// blocks 0 and 1 only, which hold keys 0..31, and the first PV step; the
-// other probabilities are exactly zero, so the result is the same bit for
-// bit.
-template <bool MASK, int KB, int NB>
-__device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const char* Ks, int lane,
-                                           int valid, bool first, bool eager,
-                                           f16x8 (&pf)[NB][2]) {
+// sums (W: each key weighted by its size from the LDS tile Ns, else by 1).
+// KB = 2 (a short last tile of at most 32 keys): key blocks 0 and 1 only,
+// which hold keys 0..31, and the first PV step; the other probabilities are
+// exactly zero, so the result is the same bit for bit.
+template <bool MASK, int KB, bool W, int NB>
+__device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const char* Ks,
+                                           const f16* Ns, int lane, int valid, bool first,
+                                           bool eager, f16x8 (&pf)[NB][2]) {
   static_assert(KB == 4 || KB == 2, "whole tile or its first 32 keys");
   constexpr int NC = KB / 2;  // 32-key PV steps
   const int g = lane >> 4;
@@ -303,6 +306,15 @@ __device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const c
     }
     R.track = __ballot(unsettled) != 0;
   }
+  // W: row-sum weights of the lane's keys (key block kb holds keys key0(kb) .. +3)
+  f16x4 wk[W ? KB : 1];
+  if constexpr (W) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key0 = 32 * (kb >> 1) + 16 * (g >> 1) + 8 * (kb & 1) + 4 * (g & 1);
+      wk[kb] = *reinterpret_cast<const f16x4*>(Ns + key0);
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
@@ -317,20 +329,25 @@ __device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const c
           const f16x2 h2 = __builtin_convertvector(e2, f16x2);
           v[4 * half + i] = h2[0];
           v[4 * half + i + 1] = h2[1];
-          R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
+          if constexpr (W) {
+            const f16x2 w2 = {wk[2 * c + half][i], wk[2 * c + half][i + 1]};
+            R.l[qb] = __builtin_amdgcn_fdot2(h2, w2, R.l[qb], false);
+          } else {
+            R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
+          }
         }
       pf[qb][c] = v;
     }
 }
 
 // One 64-key tile: its probabilities (tile_probs), then O^T += V^T P^T.
-template <bool MASK, int KB = 4, int NB>
+template <bool MASK, int KB = 4, bool W = false, int NB>
 __device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const char* Ks,
-                                         const char* Vs, int lane, int valid, bool first,
-                                         bool eager) {
+                                         const char* Vs, const f16* Ns, int lane, int valid,
+                                         bool first, bool eager) {
   constexpr int NC = KB / 2;  // 32-key PV steps
   f16x8 pf[NB][2];
-  tile_probs<MASK, KB>(R, ln, Ks, lane, valid, first, eager, pf);
+  tile_probs<MASK, KB, W>(R, ln, Ks, Ns, lane, valid, first, eager, pf);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -527,10 +544,12 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // K / V^T tiles are double buffered in LDS and copied one tile ahead by the
 // load unit (global_load_lds, no register staging), with one workgroup
 // barrier per tile.
-template <int QB, int NW, bool SGA>
+template <int QB, int NW, bool SGA, bool W>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
   __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];
+  // W (merged mode): the sizes of the tile's 64 keys, double buffered with K / V
+  __shared__ __attribute__((aligned(16))) f16 smem_n[2][W ? 64 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -547,6 +566,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   f16* qh = p.q + (int64_t)bc.h * p.rows * kDh;
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
+  const f16* nh = W ? p.nw + (int64_t)bc.h * p.kv_rows + kv0 : nullptr;
 
   // the wave's QB * 32 queries as 2 QB blocks of 16 (16x16x32 tile)
   using LanesT = Lanes;
@@ -585,6 +605,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       lds_dma16(gk[i] + (int64_t)tile * 64 * kDh, &smem[buf][0][0] + (wave * KI + i) * 1024);
       lds_dma16(gv[i] + (int64_t)tile * 64, &smem[buf][1][0] + (wave * KI + i) * 1024);
     }
+    // the 64 key sizes (128 bytes): eight lanes of wave 0
+    if (W && wave == 0 && lane < 8) lds_dma16(nh + (int64_t)tile * 64 + lane * 8, &smem_n[buf][0]);
   };
   auto land = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS
@@ -600,7 +622,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     constexpr int BUF = decltype(buf_c)::value;
     issue(t + 1, BUF ^ 1);
     if (active)
-      tile_run<false>(R, ln, smem[BUF][0], smem[BUF][1], lane, 64, t == t0, t - t0 < kEagerTiles);
+      tile_run<false, 4, W>(R, ln, smem[BUF][0], smem[BUF][1], smem_n[BUF], lane, 64, t == t0,
+                            t - t0 < kEagerTiles);
     land();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -626,7 +649,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     for (; t < t1 - 1; ++t) {
       issue(t + 1, ((t - t0) & 1) ^ 1);
       if (active)
-        tile_run<false>(R, lb, smem[0][0], smem[0][1], lane, 64, t == t0, t - t0 < kEagerTiles);
+        tile_run<false, 4, W>(R, lb, smem[0][0], smem[0][1], smem_n[(t - t0) & 1], lane, 64,
+                              t == t0, t - t0 < kEagerTiles);
       land();
       lb.flip(2 * 64 * 128);  // the other buffer
     }
@@ -639,10 +663,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     LanesT lb = ln;
     lb.flip(((t - t0) & 1) * 2 * 64 * 128);
     const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
+    const f16* Ns = smem_n[(t - t0) & 1];
     if (NW == 4 && last_valid <= 32) {
-      tile_run<true, 2>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first, eager);
+      tile_run<true, 2, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
     } else {
-      tile_run<true>(R, lb, smem[0][0], smem[0][1], lane, last_valid, first, eager);
+      tile_run<true, 4, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
     }
   }
   // the diagonal and mean columns enter once per row: in its last key range
@@ -758,14 +783,16 @@ static SplitPlan choose_split(const Plan& p, int64_t W, int ntiles, int per_cu) 
   return sp;
 }
 
-template <int QB, int NW, bool SGA>
+template <int QB, int NW, bool SGA, bool W = false>
 static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   constexpr int BQ = NW * QB * 32;
   AttnArgs g{};
-  g.q = ws_q(p, a);
+  // merged mode: the merged queries, keys and values, kv_rows rows per head
+  g.q = W ? ws_qc(p, a) : ws_q(p, a);
   g.k = ws_kloop(p, a);
   g.vt = ws_vloop(p, a);
-  g.rows = p.rows;
+  g.rows = W ? p.kv_rows : p.rows;
+  g.nw = W ? ws_nw(p, a) : nullptr;
   g.seq_stride = p.seq_stride;
   g.kv_rows = p.kv_rows;
   g.kv_seq_stride = p.kv_seq_stride;
@@ -794,7 +821,7 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
     static std::atomic<int> occupancy{0};
     int per_cu = occupancy.load(std::memory_order_relaxed);
     if (per_cu == 0) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA>,
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA, W>,
                                                        NW * 64, 0) != hipSuccess)
         per_cu = -1;
       occupancy.store(per_cu, std::memory_order_relaxed);
@@ -805,7 +832,8 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.xcd_slots = sp.xcd_slots;
   g.umax = sp.umax;
   g.part = reinterpret_cast<float*>(a.ws + p.off_split);
-  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA>), dim3((unsigned)sp.grid), dim3(NW * 64), 0, st, g);
+  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA, W>), dim3((unsigned)sp.grid), dim3(NW * 64), 0, st,
+                     g);
   if (sp.P > 1) {
     const int tail_max = sp.umax / sp.P;
     hipLaunchKernelGGL(attn_merge_kernel<BQ>, dim3((unsigned)(kXcds * tail_max * (BQ / 16))),
@@ -816,6 +844,10 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
 
 hipError_t launch_core(const Plan& p, const Ptrs& a, hipStream_t st) {
   if (p.mode == VGGT_ATTN_MODE_SUBSAMPLED) return launch_attn_t<2, 8, true>(p, a, st);
+  if (p.mode == VGGT_ATTN_MODE_MERGED) {
+    if (p.attn_waves == 8) return launch_attn_t<2, 8, false, true>(p, a, st);
+    return launch_attn_t<1, 4, false, true>(p, a, st);
+  }
   if (p.attn_waves == 8) {
     if (p.attn_qb == 2) return launch_attn_t<2, 8, false>(p, a, st);
     if (p.attn_qb == 1) return launch_attn_t<1, 8, false>(p, a, st);

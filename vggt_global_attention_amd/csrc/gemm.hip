@@ -63,6 +63,8 @@ struct GemmArgs {
   int f_off;             // QKV: feature index (in [q|k|v]) of A's first row
   int64_t dst_off;       // QKV: workspace row w is stored at row w + dst_off
   int real_only;         // QKV: rows without a token write nothing
+  int v_rows;            // QKV: store v token-major, [H][rows][64] like q and k (the merged
+                         // mode's merge stage reads it so), instead of transposed
   RowMap map;            // QKV: workspace row -> X row; OUT: workspace row -> Y row
   FastDiv dgrp, dT, dgw; // division by map.grp_stride, T and gw
   int T, gw, off, d;
@@ -179,6 +181,19 @@ __device__ __forceinline__ void load_affine(const float* gam, const float* bet, 
     }
 }
 
+// v of one (token, head) in the lane's feature order (as ln_rope_f16 leaves
+// q and k), times the range scale vs, to fp16.
+__device__ __forceinline__ void v_rows_f16(const f32x16& a0, const f32x16& a1, float vs,
+                                           f16x4 (&o)[2][4]) {
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) {
+    const f32x4 v0 = {a0[4 * rq] * vs, a0[4 * rq + 1] * vs, a0[4 * rq + 2] * vs, a0[4 * rq + 3] * vs};
+    const f32x4 v1 = {a1[4 * rq] * vs, a1[4 * rq + 1] * vs, a1[4 * rq + 2] * vs, a1[4 * rq + 3] * vs};
+    o[0][rq] = __builtin_convertvector(v0, f16x4);
+    o[1][rq] = __builtin_convertvector(v1, f16x4);
+  }
+}
+
 enum { kEpiQKV = 0, kEpiOut = 1 };
 
 template <int EPI>
@@ -243,6 +258,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
         block(std::true_type());
       } else {
         block(std::false_type());
+      }
+    } else if (g.v_rows) {
+      const float vs = __builtin_amdgcn_ldexpf(1.f, range_exponent(g.sc->xnorm * g.sc->wvnorm));
+      f16* dst = g.vt + (int64_t)hd * g.rows * kDh;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int64_t w = mbase + tb * 32 + j;
+        f16x4 o[2][4];
+        v_rows_f16(acc[0][tb], acc[1][tb], vs, o);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
+                o[fb][rq];
       }
     } else {
       const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
@@ -312,8 +342,33 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
     const int fq = fbase + g.f_off;
     const int blk = fq / g.d;  // 0: q, 1: k, 2: v
     const int hd = (fq - blk * g.d) / kDh;
-    if (blk == 2 && (g.real_only || (g.dst_off & 15) != 0)) {
+    if (blk == 2 && !g.v_rows && (g.real_only || (g.dst_off & 15) != 0)) {
       gemm_epilogue<EPI, TB>(g, acc, mbase, fbase, j, h, lane);
+      return;
+    }
+    if (blk == 2 && g.v_rows) {
+      // v token-major: the rows of q / k without LayerNorm and RoPE, scaled
+      const float vs = __builtin_amdgcn_ldexpf(1.f, range_exponent(g.sc->xnorm * g.sc->wvnorm));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int tl = tb * 32 + j;
+        f16x4 o[2][4];
+        v_rows_f16(acc[0][tb], acc[1][tb], vs, o);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
+                o[fb][rq];
+      }
+      lds_wave_sync();
+      f16* dst = g.vt + (int64_t)hd * g.rows * kDh;
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * 128 + ((c ^ (tl & 7)) << 4));
+        *reinterpret_cast<u32x4*>(dst + (mbase + tl + g.dst_off) * kDh + c * 8) = v;
+      }
       return;
     }
     if (blk < 2) {
@@ -895,6 +950,7 @@ static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   g.m_first = 0;
   g.q_lo = p.q0;
   g.q_hi = p.window ? p.L : p.rows;
+  g.v_rows = p.mode == VGGT_ATTN_MODE_MERGED ? 1 : 0;
   set_divisors(g);
   return g;
 }

@@ -51,6 +51,9 @@ struct CallOpts {
   // the prep stage ORs its range bits into the workspace's status word
   // instead of replacing it (the blocks of a schedule after the first)
   bool keep_status = false;
+  // merged mode: frames per block, window rows / columns, merges per block
+  // (frames == 0: only sizing the workspace, for the largest merged set)
+  int httm_frames = 0, httm_wh = 0, httm_ww = 0, httm_r = 0;
 };
 
 // Descriptor key / value cache (caller-owned device buffer, 256-byte
@@ -107,9 +110,15 @@ struct Plan {
   // of workgroups runs as key ranges that a merge kernel combines.
   int split_cap;
   bool keep_status;    // see CallOpts
+  // merged mode (HTTM): blocks of hf frames x hwh x hww cells, hr merges per
+  // block; the merged set has M tokens per head (L = Lk = M, kv_rows rows per
+  // head in the merged buffers); merged values carry an extra 2^-hshift
+  int hf, hwh, hww, hr, hshift;
+  int64_t hper_run;    // merged tokens of a run of hf frames
   // workspace carve-up (byte offsets)
   size_t off_scal, off_bounds, off_rope, off_wo, off_q, off_k, off_v;
   size_t off_kc, off_vc, off_sums, off_part;  // subsampled mode only (else 0)
+  size_t off_qc, off_nw, off_owner;           // merged mode only (kc / vc too; else 0)
   size_t off_split;    // [split_cap][BQ][64] fp32 O, then [split_cap][BQ] float2 (m, l)
   DescLayout desc;     // descriptor mode: layout of the key / value cache
   size_t total;
@@ -165,14 +174,25 @@ inline f16* ws_wo(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(
 inline f16* ws_q(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_q); }
 inline f16* ws_k(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_k); }
 inline f16* ws_v(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_v); }
-// keys / values the attention loop streams (compact copies in subsampled mode)
+// keys / values the attention loop streams (compact copies in subsampled and
+// merged mode)
+inline bool compact_kv(const Plan& p) {
+  return p.mode == VGGT_ATTN_MODE_SUBSAMPLED || p.mode == VGGT_ATTN_MODE_MERGED;
+}
 inline f16* ws_kloop(const Plan& p, const Ptrs& a) {
   if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return reinterpret_cast<f16*>(a.cache + p.desc.off_k);
-  return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_kc : p.off_k));
+  return reinterpret_cast<f16*>(a.ws + (compact_kv(p) ? p.off_kc : p.off_k));
 }
 inline f16* ws_vloop(const Plan& p, const Ptrs& a) {
   if (p.mode == VGGT_ATTN_MODE_DESCRIPTOR) return reinterpret_cast<f16*>(a.cache + p.desc.off_v);
-  return reinterpret_cast<f16*>(a.ws + (p.mode == VGGT_ATTN_MODE_SUBSAMPLED ? p.off_vc : p.off_v));
+  return reinterpret_cast<f16*>(a.ws + (compact_kv(p) ? p.off_vc : p.off_v));
+}
+// merged mode: merged queries (then their outputs) [H][kv_rows][64], key
+// sizes [H][kv_rows] fp16, merged token of every token [H][S*T] int32
+inline f16* ws_qc(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_qc); }
+inline f16* ws_nw(const Plan& p, const Ptrs& a) { return reinterpret_cast<f16*>(a.ws + p.off_nw); }
+inline int32_t* ws_owner(const Plan& p, const Ptrs& a) {
+  return reinterpret_cast<int32_t*>(a.ws + p.off_owner);
 }
 inline float* ws_sums(const Plan& p, const Ptrs& a) {
   return reinterpret_cast<float*>(a.ws + p.off_sums);
@@ -203,5 +223,33 @@ hipError_t launch_rownorm_max(const bf16* X, int64_t rows, int d, RowMap map, fl
 // Subsampled mode: gather the kept tokens' keys / values and sum the
 // discarded ones (first half of the CORE stage).
 hipError_t launch_subsample(const Plan& p, const Ptrs& a, hipStream_t st);
+
+// Merged mode (merge.hip): merge every head's tokens into the merged
+// queries, keys and values (before the attention kernel), and give every
+// token its merged token's output (after it).
+hipError_t launch_merge(const Plan& p, const Ptrs& a, hipStream_t st);
+hipError_t launch_unmerge(const Plan& p, const Ptrs& a, hipStream_t st);
+
+// Merged mode: merged tokens of one block of nf frames and nd cells per
+// frame with r merges (a block has (nf - 1) nd sources), and of the blocks of
+// the first `wrows` window rows of a frame run of nf frames.  The same
+// arithmetic on the host (the set's size) and on the device (where a strip's
+// merged tokens start).
+__host__ __device__ inline int64_t merged_block_count(int nf, int nd, int r) {
+  const int64_t ns = (int64_t)(nf - 1) * nd;
+  return (int64_t)nf * nd - (ns < r ? ns : (int64_t)r);
+}
+__host__ __device__ inline int64_t merged_run_count(int nf, int gh, int gw, int wh, int ww, int r,
+                                                     int wrows) {
+  int64_t c = 0;
+  for (int wr = 0; wr < wrows; ++wr) {
+    const int rh = gh - wr * wh < wh ? gh - wr * wh : wh;
+    for (int c0 = 0; c0 < gw; c0 += ww) c += merged_block_count(nf, rh * (gw - c0 < ww ? gw - c0 : ww), r);
+  }
+  return c;
+}
+// A strip (one frame run x one window row, every window column) is merged by
+// one workgroup holding the strip's keys in LDS: at most this many tokens.
+constexpr int kMergeStripMax = 400;
 
 }  // namespace vggt
