@@ -68,8 +68,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="s100")
     ap.add_argument("--mode", default="global",
-                    choices=["global", "frame", "register", "subsampled"])
+                    choices=["global", "frame", "register", "subsampled", "merged"])
     ap.add_argument("--sub", default="3x3", help="subsampled mode: windows sub_h x sub_w")
+    ap.add_argument("--merge", default="4,2,3,12",
+                    help="merged mode: frames per block, window rows, window columns, merges per block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other modes / sizes")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="query rows in the CPU sample")
@@ -153,7 +155,10 @@ def loop_stage(w, mode, d, stage, steps, sub=(1, 1)):
     from vggt_global_attention_amd import api
     from vggt_global_attention_amd import binding as B
     st = {"prep": B.STAGE_PREP, "qkv": B.STAGE_QKV, "core": B.STAGE_CORE, "out": B.STAGE_OUT}
-    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
+    if mode == "merged":
+        blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, merge=sub)
+    else:
+        blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
     args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
     Y = torch.empty_like(d["X"])
     blk(*args, Y=Y)
@@ -553,7 +558,11 @@ def main():
                           "data": "synthetic (seeded; no trained weights)"}), flush=True)
         return
     w = configs.WORKLOADS[a.workload]
-    sub = tuple(int(x) for x in a.sub.lower().split("x")) if a.mode == "subsampled" else (1, 1)
+    sub = (1, 1)
+    if a.mode == "subsampled":
+        sub = tuple(int(x) for x in a.sub.lower().split("x"))
+    elif a.mode == "merged":
+        sub = tuple(int(x) for x in a.merge.split(","))
     print(f"[bench] generating inputs for {w.name} (S={w.S}, N={w.N})", file=sys.stderr, flush=True)
     inp, d = gpu_inputs(w)
     if a.power:
@@ -600,6 +609,10 @@ def main():
                      "traffic_unit": "bytes per launch (FETCH_SIZE*2.0 + WRITE_SIZE*1.0)",
                      "flop_per_launch": attn_flop, "ms_per_launch": core_ms},
     }
+    if a.mode == "merged":
+        out["config"]["merge"] = list(sub)
+        out["config"]["merged_tokens"] = w.merged_tokens(*sub)
+        out["roofline"]["kernel"] = "CORE stage: merge + attn_kernel<W> + unmerge"
     if a.mode == "subsampled":
         out["config"]["sub"] = list(sub)
         out["config"]["kept_keys"] = w.kept_keys(*sub)

@@ -547,9 +547,14 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 template <int QB, int NW, bool SGA, bool W>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];
-  // W (merged mode): the sizes of the tile's 64 keys, double buffered with K / V
-  __shared__ __attribute__((aligned(16))) f16 smem_n[2][W ? 64 : 8];
+  // K / V^T tiles [buffer][K, V^T][64 rows x 128 bytes], then in merged mode
+  // (W) the sizes of the tile's 64 keys, 1 KB per buffer (the first 128
+  // bytes used; see issue()).  One LDS object: with a second one the
+  // compiler waits for every outstanding LDS copy, the next tile's too,
+  // before a tile's first LDS read.
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * 64 * 128 + (W ? 2 * 1024 : 0)];
+  auto& smem = *reinterpret_cast<char (*)[2][2][64 * 128]>(smem_raw);
+  f16* const sizes_lds = reinterpret_cast<f16*>(smem_raw + 2 * 2 * 64 * 128);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -605,8 +610,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       lds_dma16(gk[i] + (int64_t)tile * 64 * kDh, &smem[buf][0][0] + (wave * KI + i) * 1024);
       lds_dma16(gv[i] + (int64_t)tile * 64, &smem[buf][1][0] + (wave * KI + i) * 1024);
     }
-    // the 64 key sizes (128 bytes): eight lanes of wave 0
-    if (W && wave == 0 && lane < 8) lds_dma16(nh + (int64_t)tile * 64 + lane * 8, &smem_n[buf][0]);
+    // the 64 key sizes (128 bytes): every lane of every wave copies chunk
+    // i % 8 to slot i, so slots 0..7 hold the sizes (the waves write the
+    // same bytes; no branch around the copy)
+    if (W) lds_dma16(nh + (int64_t)tile * 64 + (lane & 7) * 8, sizes_lds + buf * 512);
   };
   auto land = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS
@@ -622,7 +629,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     constexpr int BUF = decltype(buf_c)::value;
     issue(t + 1, BUF ^ 1);
     if (active)
-      tile_run<false, 4, W>(R, ln, smem[BUF][0], smem[BUF][1], smem_n[BUF], lane, 64, t == t0,
+      tile_run<false, 4, W>(R, ln, smem[BUF][0], smem[BUF][1], sizes_lds + BUF * 512, lane, 64, t == t0,
                             t - t0 < kEagerTiles);
     land();
     __builtin_amdgcn_sched_barrier(0);
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     for (; t < t1 - 1; ++t) {
       issue(t + 1, ((t - t0) & 1) ^ 1);
       if (active)
-        tile_run<false, 4, W>(R, lb, smem[0][0], smem[0][1], smem_n[(t - t0) & 1], lane, 64,
+        tile_run<false, 4, W>(R, lb, smem[0][0], smem[0][1], sizes_lds + ((t - t0) & 1) * 512, lane, 64,
                               t == t0, t - t0 < kEagerTiles);
       land();
       lb.flip(2 * 64 * 128);  // the other buffer
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     LanesT lb = ln;
     lb.flip(((t - t0) & 1) * 2 * 64 * 128);
     const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
-    const f16* Ns = smem_n[(t - t0) & 1];
+    const f16* Ns = sizes_lds + ((t - t0) & 1) * 512;
     if (NW == 4 && last_valid <= 32) {
       tile_run<true, 2, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
     } else {

@@ -22,8 +22,9 @@
 //
 // One workgroup per (strip, head), a strip being one frame run x one window
 // row with all its windows: the strip's keys sit in LDS for the similarities
-// (at most kMergeStripMax tokens), its merged tokens are contiguous, so their
-// value columns are written to the transposed value buffer as whole runs.
+// (at most kMergeStripMax tokens), then its values and its queries for the
+// member sums; its merged tokens are contiguous, so their value columns are
+// written to the transposed value buffer as whole runs.
 #include "plan.h"
 
 namespace vggt {
@@ -40,7 +41,7 @@ struct MergeArgs {
   int64_t rows, kv_rows, M, per_run;
   int S, T, gh, gw;
   int F, wh, ww, r, shift;
-  int nwr, nstrips;  // window rows, strips (frame runs x window rows)
+  int nwr;           // window rows (0 without patches)
 };
 
 // Place of merged token x in the transposed value buffer (bits 2 and 3
@@ -56,8 +57,9 @@ __global__ __launch_bounds__(256) void httm_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) f16 keys[kMergeStripMax * kKeyStride];
   __shared__ float score[kMergeStripMax];
   __shared__ short best[kMergeStripMax];
-  __shared__ short pos[kMergeStripMax];
   __shared__ unsigned char merged[kMergeStripMax];
+  __shared__ short mlist[kMergeStripMax];       // strip tokens in member order
+  __shared__ short mstart[kMergeStripMax + 1];  // first mlist slot of each local merged token
   const int h = blockIdx.y, item = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t N = (int64_t)a.S * a.T;
@@ -71,36 +73,50 @@ __global__ __launch_bounds__(256) void httm_merge_kernel(MergeArgs a) {
   int32_t* own = a.owner + (int64_t)h * N;
   const float vscale = __builtin_amdgcn_ldexpf(1.f, -a.shift);
 
-  if (item < a.S) {
-    // the special tokens of frame `item`: merged tokens item * 17 + t, size 1
-    for (int t = wave; t < kSpecial; t += 4) {
-      const int64_t tok = (int64_t)item * a.T + t, m = (int64_t)item * kSpecial + t;
-      qch[m * kDh + lane] = qh[tok * kDh + lane];
-      kch[m * kDh + lane] = kh[tok * kDh + lane];
-      vch[(int64_t)lane * a.kv_rows + vslot(m)] = (f16)((float)vh[tok * kDh + lane] * vscale);
-      if (lane == 0) {
+  // workgroup (frame run fr, window row wr); the window-row-0 workgroup of a
+  // run also passes the run's special tokens through, the first one also
+  // pads the merged set
+  const int nwr1 = a.nwr > 0 ? a.nwr : 1;
+  const int fr = item / nwr1, wr = item - fr * nwr1;
+  const int f0 = fr * a.F, nf = a.S - f0 < a.F ? a.S - f0 : a.F;
+  if (wr == 0) {
+    // special tokens: merged token s * 17 + t, size 1
+    for (int idx = tid; idx < nf * kSpecial * 8; idx += 256) {
+      const int sl = idx >> 3, c = idx & 7, fi = sl / kSpecial, t = sl - fi * kSpecial;
+      const int64_t tok = (int64_t)(f0 + fi) * a.T + t, m = (int64_t)(f0 + fi) * kSpecial + t;
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(qh + tok * kDh + c * 8);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kh + tok * kDh + c * 8);
+      const f16x8 vv = *reinterpret_cast<const f16x8*>(vh + tok * kDh + c * 8);
+      *reinterpret_cast<u32x4*>(qch + m * kDh + c * 8) = qv;
+      *reinterpret_cast<u32x4*>(kch + m * kDh + c * 8) = kv;
+      const int64_t col = vslot(m);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vch[(int64_t)(c * 8 + e) * a.kv_rows + col] = (f16)((float)vv[e] * vscale);
+      if (c == 0) {
         nwh[m] = (f16)1.f;
         own[tok] = (int32_t)m;
       }
     }
-    return;
-  }
-  if (item == a.S + a.nstrips) {
-    // the attention kernel reads whole 64-key tiles: merged tokens M .. the
-    // tile's end are finite zeros of size 0
-    const int64_t end = (a.M + kAttnBK - 1) / kAttnBK * kAttnBK;
-    for (int64_t m = a.M + wave; m < end; m += 4) {
-      qch[m * kDh + lane] = (f16)0.f;
-      kch[m * kDh + lane] = (f16)0.f;
-      vch[(int64_t)lane * a.kv_rows + vslot(m)] = (f16)0.f;
-      if (lane == 0) nwh[m] = (f16)0.f;
+    if (fr == 0) {
+      // the attention kernel reads whole 64-key tiles: merged tokens M ..
+      // the tile's end are finite zeros of size 0
+      const int64_t end = (a.M + kAttnBK - 1) / kAttnBK * kAttnBK;
+      const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int64_t idx = tid; idx < (end - a.M) * 8; idx += 256) {
+        const int64_t m = a.M + (idx >> 3);
+        const int c = (int)(idx & 7);
+        *reinterpret_cast<f16x8*>(qch + m * kDh + c * 8) = z;
+        *reinterpret_cast<f16x8*>(kch + m * kDh + c * 8) = z;
+        const int64_t col = vslot(m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vch[(int64_t)(c * 8 + e) * a.kv_rows + col] = (f16)0.f;
+        if (c == 0) nwh[m] = (f16)0.f;
+      }
     }
-    return;
   }
+  if (a.nwr == 0) return;  // no patches: nothing merges
 
-  // strip: frame run fr, window row wr
-  const int strip = item - a.S, fr = strip / a.nwr, wr = strip - fr * a.nwr;
-  const int f0 = fr * a.F, nf = a.S - f0 < a.F ? a.S - f0 : a.F;
+  // the strip: frame run fr x window row wr, every window column
   const int r0 = wr * a.wh, rh = a.gh - r0 < a.wh ? a.gh - r0 : a.wh;
   const int gw = a.gw, ww = a.ww;
   const int nt = nf * rh * gw;            // strip tokens: local (i * rh + row) * gw + col
@@ -111,12 +127,37 @@ __global__ __launch_bounds__(256) void httm_merge_kernel(MergeArgs a) {
     const int i = l / nd_row, rest = l - i * nd_row, row = rest / gw, col = rest - row * gw;
     return (int64_t)(f0 + i) * a.T + kSpecial + (int64_t)(r0 + row) * gw + col;
   };
-  // 1. the strip's keys into LDS (16 bytes per step)
-  for (int idx = tid; idx < nt * 8; idx += 256) {
-    const int l = idx >> 3, c = idx & 7;
-    *reinterpret_cast<u32x4*>(&keys[l * kKeyStride + c * 8]) =
-        *reinterpret_cast<const u32x4*>(kh + token_of(l) * kDh + c * 8);
+  // the strip's rows of one head's k, v or q into LDS, row stride kKeyStride
+  auto stage = [&](const f16* src) {
+    constexpr int kBatch = 4;
+    for (int i0 = tid; i0 < nt * 8; i0 += 256 * kBatch) {
+      u32x4 x[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int idx = i0 + b * 256;
+        if (idx < nt * 8) x[b] = *reinterpret_cast<const u32x4*>(src + token_of(idx >> 3) * kDh + (idx & 7) * 8);
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int idx = i0 + b * 256;
+        if (idx < nt * 8) *reinterpret_cast<u32x4*>(&keys[(idx >> 3) * kKeyStride + (idx & 7) * 8]) = x[b];
+      }
+    }
+  };
+  // 1. the strip's keys into LDS; its values and queries into registers
+  //    meanwhile (thread tid holds chunks tid + 256 b), for the member sums
+  constexpr int kPre = (kMergeStripMax * 8 + 255) / 256;
+  u32x4 vpre[kPre], qpre[kPre];
+#pragma unroll
+  for (int b = 0; b < kPre; ++b) {
+    const int idx = tid + b * 256;
+    if (idx < nt * 8) {
+      const int64_t off = token_of(idx >> 3) * kDh + (idx & 7) * 8;
+      vpre[b] = *reinterpret_cast<const u32x4*>(vh + off);
+      qpre[b] = *reinterpret_cast<const u32x4*>(qh + off);
+    }
   }
+  stage(kh);
   __syncthreads();
   // 2. every source's most similar destination of its window (sequential
   //    fp32 sum over the features; the fp16 products are exact in fp32)
@@ -125,16 +166,22 @@ __global__ __launch_bounds__(256) void httm_merge_kernel(MergeArgs a) {
     const int c0 = col / ww * ww, cw = gw - c0 < ww ? gw - c0 : ww;
     float bs = 0.f;
     int bj = -1;
+    float ks[8][8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f16x8 x = *reinterpret_cast<const f16x8*>(&keys[l * kKeyStride + c * 8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ks[c][e] = (float)x[e];
+    }
     for (int dr = 0; dr < rh; ++dr)
       for (int dc = 0; dc < cw; ++dc) {
         const f16* kd = &keys[(dr * gw + c0 + dc) * kKeyStride];
-        const f16* ks = &keys[l * kKeyStride];
         float sim = 0.f;
-        for (int c = 0; c < kDh; c += 8) {
-          const f16x8 x = *reinterpret_cast<const f16x8*>(ks + c);
-          const f16x8 y = *reinterpret_cast<const f16x8*>(kd + c);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sim = fmaf((float)x[e], (float)y[e], sim);
+        for (int c = 0; c < 8; ++c) {
+          const f16x8 y = *reinterpret_cast<const f16x8*>(kd + c * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sim = fmaf(ks[c][e], (float)y[e], sim);
         }
         if (bj < 0 || sim > bs) {
           bs = sim;
@@ -162,89 +209,120 @@ __global__ __launch_bounds__(256) void httm_merge_kernel(MergeArgs a) {
     merged[l] = rank < a.r ? 1 : 0;
   }
   __syncthreads();
-  // 4. merged token of every strip token: window base + destination, or
-  //    window base + destinations + rank among the window's unmerged sources
+  // 4. every strip token's merged token, and the member lists: mlist holds
+  //    the strip's tokens merged token by merged token, each in member order
+  //    (its destination, then its sources in frame, row, column order), and
+  //    mstart[x] is where local merged token x begins.  A window's merged
+  //    tokens: its destinations (each with the sources merged into it), then
+  //    its unmerged sources; its member slots begin at the strip tokens of
+  //    the windows before it.
+  int cnt = 0;
+  for (int c = 0; c < gw; c += ww) cnt += (int)merged_block_count(nf, rh * (gw - c < ww ? gw - c : ww), a.r);
   for (int l = tid; l < nt; l += 256) {
     const int i = l / nd_row, rest = l - i * nd_row, row = rest / gw, col = rest - row * gw;
     const int c0 = col / ww * ww, cw = gw - c0 < ww ? gw - c0 : ww, nd = rh * cw;
-    int64_t b0 = base;
-    for (int c = 0; c < c0; c += ww) b0 += merged_block_count(nf, rh * (gw - c < ww ? gw - c : ww), a.r);
-    int64_t m;
+    const int ns = (nf - 1) * nd, nm = ns < a.r ? ns : a.r;
+    int xw = 0;  // local index of the window's first merged token
+    for (int c = 0; c < c0; c += ww) xw += (int)merged_block_count(nf, rh * (gw - c < ww ? gw - c : ww), a.r);
+    const int wstart = nf * rh * c0;
+    const bool src_merged = i > 0 && merged[l];
+    const int me = i == 0 ? -1 : ((i - 1) * rh + row) * cw + (col - c0);
+    const int j = i == 0 ? row * cw + (col - c0) : (src_merged ? best[l] : -1);
+    int below = 0, same_before = 0, unmerged_before = 0;
+    for (int i2 = 1; i2 < nf; ++i2)
+      for (int r2 = 0; r2 < rh; ++r2)
+        for (int q2 = 0; q2 < cw; ++q2) {
+          const int l2 = i2 * nd_row + r2 * gw + c0 + q2;
+          const int other = ((i2 - 1) * rh + r2) * cw + q2;
+          if (merged[l2]) {
+            const int b2 = best[l2];
+            below += b2 < j ? 1 : 0;
+            same_before += (b2 == j && other < me) ? 1 : 0;
+          } else {
+            unmerged_before += other < me ? 1 : 0;
+          }
+        }
+    int x, slot;
     if (i == 0) {
-      m = b0 + row * cw + (col - c0);
-    } else if (merged[l]) {
-      m = b0 + best[l];
+      x = xw + j;
+      slot = wstart + j + below;
+      mstart[x] = (short)slot;
+    } else if (src_merged) {
+      x = xw + j;
+      slot = wstart + j + below + 1 + same_before;
     } else {
-      const int me = ((i - 1) * rh + row) * cw + (col - c0);
-      int before = 0;
-      for (int i2 = 1; i2 < nf; ++i2)
-        for (int r2 = 0; r2 < rh; ++r2)
-          for (int q2 = 0; q2 < cw; ++q2) {
-            const int l2 = i2 * nd_row + r2 * gw + c0 + q2;
-            const int other = ((i2 - 1) * rh + r2) * cw + q2;
-            before += (other < me && !merged[l2]) ? 1 : 0;
-          }
-      pos[l] = (short)before;
-      m = b0 + nd + before;
+      x = xw + nd + unmerged_before;
+      slot = wstart + nd + nm + unmerged_before;
+      mstart[x] = (short)slot;
     }
-    own[token_of(l)] = (int32_t)m;
+    mlist[slot] = (short)l;
+    own[token_of(l)] = (int32_t)(base + x);
+  }
+  if (tid == 0) mstart[cnt] = (short)nt;
+  __syncthreads();
+  // 5. the strip's merged tokens, from rows staged in LDS (the keys still
+  //    there, then the values, then the queries): every staging copy is one
+  //    16-byte load per thread and step, all in flight together.  Member
+  //    sums in member order (the destination, then its sources in frame,
+  //    row, column order), in fp32.
+  f16* rows_lds = keys;  // [nt][kKeyStride]
+  // member sum of 8 features (chunk c) of local merged token m from the
+  // staged rows; returns the member count
+  auto chunk_sum = [&](int m, int c, float* acc) -> int {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const int k0 = mstart[m], k1 = mstart[m + 1];
+    for (int k = k0; k < k1; ++k) {
+      const f16x8 x = *reinterpret_cast<const f16x8*>(&rows_lds[mlist[k] * kKeyStride + c * 8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
+    }
+    return k1 - k0;
+  };
+  auto unstage = [&](const u32x4* pre) {
+#pragma unroll
+    for (int b = 0; b < kPre; ++b) {
+      const int idx = tid + b * 256;
+      if (idx < nt * 8) *reinterpret_cast<u32x4*>(&rows_lds[(idx >> 3) * kKeyStride + (idx & 7) * 8]) = pre[b];
+    }
+  };
+  // 5a. key means (the keys are still staged); item = 8 m + chunk
+  for (int idx = tid; idx < cnt * 8; idx += 256) {
+    const int m = idx >> 3, c = idx & 7;
+    float acc[8];
+    const float inv = 1.f / (float)chunk_sum(m, c, acc);
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16)(acc[e] * inv);
+    *reinterpret_cast<f16x8*>(kch + (base + m) * kDh + c * 8) = o;
   }
   __syncthreads();
-  // 5. the strip's merged tokens: one wave each, lane = feature.  Members:
-  //    a destination and the sources merged into it, or one unmerged source.
-  int64_t cnt = 0;
-  for (int c = 0; c < gw; c += ww) cnt += merged_block_count(nf, rh * (gw - c < ww ? gw - c : ww), a.r);
-  f16* vstage = keys;  // [64][cnt]: the value sums, staged for whole-run stores
-  for (int m = wave; m < cnt; m += 4) {
-    // find the window and the slot inside it
-    int c0 = 0, cw = 0;
-    int64_t slot = m;
-    for (; c0 < gw; c0 += ww) {
-      cw = gw - c0 < ww ? gw - c0 : ww;
-      const int64_t n = merged_block_count(nf, rh * cw, a.r);
-      if (slot < n) break;
-      slot -= n;
-    }
-    const int nd = rh * cw;
-    float sq = 0.f, sk = 0.f, sv = 0.f;
-    int n = 0;
-    auto add = [&](int l) {
-      const int64_t tok = token_of(l);
-      sq += (float)qh[tok * kDh + lane];
-      sk += (float)kh[tok * kDh + lane];
-      sv += (float)vh[tok * kDh + lane];
-      ++n;
-    };
-    if (slot < nd) {
-      const int j = (int)slot, dr = j / cw, dc = j - dr * cw;
-      add(dr * gw + c0 + dc);
-      for (int i2 = 1; i2 < nf; ++i2)
-        for (int r2 = 0; r2 < rh; ++r2)
-          for (int q2 = 0; q2 < cw; ++q2) {
-            const int l2 = i2 * nd_row + r2 * gw + c0 + q2;
-            if (merged[l2] && best[l2] == j) add(l2);
-          }
-    } else {
-      const int want = (int)(slot - nd);
-      for (int i2 = 1; i2 < nf; ++i2)
-        for (int r2 = 0; r2 < rh; ++r2)
-          for (int q2 = 0; q2 < cw; ++q2) {
-            const int l2 = i2 * nd_row + r2 * gw + c0 + q2;
-            if (!merged[l2] && pos[l2] == want) add(l2);
-          }
-    }
-    const float inv = 1.f / (float)n;
-    qch[(base + m) * kDh + lane] = (f16)(sq * inv);
-    kch[(base + m) * kDh + lane] = (f16)(sk * inv);
-    vstage[lane * cnt + m] = (f16)(sv * vscale);
-    if (lane == 0) nwh[base + m] = (f16)(float)n;
+  // 5b. value sums x 2^-shift into the transposed buffer and the sizes; item =
+  //     chunk * cnt + m, so a wave's lanes write consecutive merged tokens
+  //     (whole runs of each feature row)
+  unstage(vpre);
+  __syncthreads();
+  for (int idx = tid; idx < cnt * 8; idx += 256) {
+    const int c = idx / cnt, m = idx - c * cnt;
+    float acc[8];
+    const int n = chunk_sum(m, c, acc);
+    const int64_t col = vslot(base + m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vch[(int64_t)(c * 8 + e) * a.kv_rows + col] = (f16)(acc[e] * vscale);
+    if (c == 0) nwh[base + m] = (f16)(float)n;
   }
   __syncthreads();
-  // 6. value columns: runs of the strip's merged tokens per feature row
-  for (int64_t idx = tid; idx < kDh * cnt; idx += 256) {
-    const int f = (int)(idx / cnt);
-    const int64_t m = idx - f * cnt;
-    vch[(int64_t)f * a.kv_rows + vslot(base + m)] = vstage[f * cnt + m];
+  // 5c. query means; item = 8 m + chunk
+  unstage(qpre);
+  __syncthreads();
+  for (int idx = tid; idx < cnt * 8; idx += 256) {
+    const int m = idx >> 3, c = idx & 7;
+    float acc[8];
+    const float inv = 1.f / (float)chunk_sum(m, c, acc);
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16)(acc[e] * inv);
+    *reinterpret_cast<f16x8*>(qch + (base + m) * kDh + c * 8) = o;
   }
 }
 
@@ -292,8 +370,8 @@ hipError_t launch_merge(const Plan& p, const Ptrs& a, hipStream_t st) {
   m.r = p.hr;
   m.shift = p.hshift;
   m.nwr = p.gw > 0 ? (p.gh + p.hwh - 1) / p.hwh : 0;
-  m.nstrips = (p.S + p.hf - 1) / p.hf * m.nwr;
-  hipLaunchKernelGGL(httm_merge_kernel, dim3((unsigned)(p.S + m.nstrips + 1), (unsigned)p.H),
+  const int runs = (p.S + p.hf - 1) / p.hf;
+  hipLaunchKernelGGL(httm_merge_kernel, dim3((unsigned)(runs * (m.nwr > 0 ? m.nwr : 1)), (unsigned)p.H),
                      dim3(256), 0, st, m);
   return hipGetLastError();
 }
