@@ -108,7 +108,7 @@ def gpu_inputs(w):
     return inp, {k: inp[k].to("cuda").contiguous() for k in keys}
 
 
-def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None):
+def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None, operands="fp16"):
     """ms per full call and ms per attention-core stage, both with HIP events
     on the stream the library launches on (torch's current stream).  rows =
     (begin, count): the query-row window of the global block instead."""
@@ -123,7 +123,7 @@ def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None):
         if mode == "merged":
             blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, merge=sub)
         else:
-            blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
+            blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub, operands=operands)
         Y = torch.empty_like(d["X"])
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -450,9 +450,12 @@ def host_info():
     return {"cpu_model": model, "nproc": os.cpu_count(), "blas": blas}
 
 
-def cpu_baseline(w, inp, n_rows):
+def cpu_baseline(w, inp, n_rows, outputs=None):
     """The fp64 oracle on a bounded sample of the same layer: k/v for all N
-    tokens, then q, attention and output projection for n_rows query rows."""
+    tokens, then q, attention and output projection for n_rows query rows.
+    outputs: {name: Y [S, T, d] on the host} of GPU calls on the same inputs,
+    whose errors on the sampled rows are reported (relL1 = sum|err| /
+    sum|ref|, max|err| / max|ref|, mean|err| / max|ref|)."""
     import numpy as np
     import torch
     import oracle
@@ -468,8 +471,15 @@ def cpu_baseline(w, inp, n_rows):
     X = inp["X"].to(torch.float64).numpy()
     rows = synth.sample_rows(w, n_rows).numpy()
     t0 = time.perf_counter()
-    oracle.global_attention_rows(X, p, rows, threads=threads)
+    ref = oracle.global_attention_rows(X, p, rows, threads=threads)
     dt = time.perf_counter() - t0
+    errors = {}
+    for name, Y in (outputs or {}).items():
+        y = Y.reshape(-1, w.d)[torch.from_numpy(rows)].to(torch.float64).numpy()
+        err = np.abs(y - ref)
+        errors[name] = {"relL1": float(err.sum() / np.abs(ref).sum()),
+                        "max_over_max": float(err.max() / np.abs(ref).max()),
+                        "mean_over_max": float(err.mean() / np.abs(ref).max())}
     n, d = w.N, w.d
     flop = 4.0 * n * d * d + len(rows) * (2.0 * d * d + 4.0 * n * d + 2.0 * d * d)
     full_s = dt * (w.flop("global") / flop)
@@ -478,7 +488,8 @@ def cpu_baseline(w, inp, n_rows):
             "sample": f"{w.name} global layer: k/v for all {n} tokens + {len(rows)} sampled query "
                       f"rows (q, attention over all keys, Wo); {flop / 1e12:.3f} TFLOP in {dt:.1f} s; "
                       f"full layer extrapolates to {full_s / 60:.0f} min",
-            "ms_per_step_extrapolated": full_s * 1e3}
+            "ms_per_step_extrapolated": full_s * 1e3,
+            "sample_errors": errors}
 
 
 def cpu_full():
@@ -580,6 +591,17 @@ def main():
         return
     print(f"[bench] timing {a.mode} ({a.warmup} warmup + {a.steps} steps)", file=sys.stderr, flush=True)
     ms, core_ms = time_block(w, a.mode, d, a.steps, a.warmup, sub)
+    # global layer: its output with fp16 and with bf16 attention operands, for
+    # the error report of the CPU baseline leg (after the timed region)
+    outputs = {}
+    if a.mode == "global" and not a.no_cpu:
+        from vggt_global_attention_amd import api
+        args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+        for ops in ("fp16", "bf16"):
+            blk = api.Block("global", d["X"], w.H, w.grid_h, w.grid_w, operands=ops)
+            outputs[f"{ops}_operands"] = blk(*args).cpu()
+            del blk
+        torch.cuda.empty_cache()
     flop = w.flop(a.mode, sub)
     attn_flop = w.attention_flop(a.mode, sub)
     achieved = attn_flop / (core_ms * 1e-3) / 1e12
@@ -620,21 +642,27 @@ def main():
     if not a.no_extra and a.workload == "s100" and a.mode == "global":
         extra = {}
         httm = (4, 2, 3, 12)   # 4-frame runs, 2 x 3 windows, 12 of 18 sources merged
-        runs = (("s24", (("global", (1, 1)), ("frame", (1, 1)))),
-                ("s500", (("frame", (1, 1)), ("register", (1, 1)))),
-                ("s100", (("subsampled", (3, 3)), ("merged", httm))),
-                ("s300", (("global", (1, 1)), ("subsampled", (3, 3)), ("merged", httm))))
+        # (mode, sub / merge parameters, attention operand type)
+        runs = (("s24", (("global", (1, 1), "fp16"), ("frame", (1, 1), "fp16"))),
+                ("s500", (("frame", (1, 1), "fp16"), ("frame", (1, 1), "bf16"),
+                          ("register", (1, 1), "fp16"))),
+                ("s100", (("global", (1, 1), "bf16"), ("subsampled", (3, 3), "fp16"),
+                          ("merged", httm, "fp16"))),
+                ("s300", (("global", (1, 1), "fp16"), ("subsampled", (3, 3), "fp16"),
+                          ("merged", httm, "fp16"))))
         for name, modes in runs:
             ww = configs.WORKLOADS[name]
             dd = d if name == a.workload else gpu_inputs(ww)[1]
-            for mode, esub in modes:
-                print(f"[bench] extra {name} {mode} {esub}", file=sys.stderr, flush=True)
-                m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub)
+            for mode, esub, ops in modes:
+                print(f"[bench] extra {name} {mode} {esub} {ops}", file=sys.stderr, flush=True)
+                m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub, operands=ops)
                 key = f"{name}_{mode}"
                 if mode == "subsampled":
                     key += f"{esub[0]}x{esub[1]}"
                 elif mode == "merged":
                     key += "_F{}w{}x{}r{}".format(*esub)
+                if ops == "bf16":
+                    key += "_bf16ops"
                 # merged mode: FLOP of the attention over the merged tokens
                 # (the merge and unmerge kernels run inside core_ms)
                 extra[key] = {"ms_per_layer": m2, "tflops": ww.flop(mode, esub) / m2 / 1e9,
@@ -668,7 +696,7 @@ def main():
         out["extra"] = extra
     if not a.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_rows, outputs)
     print(json.dumps(out), flush=True)
 
 

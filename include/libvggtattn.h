@@ -109,6 +109,7 @@ extern "C" {
 #define VGGT_ATTN_STAGE_QKV  1 /* QKV projection + per-head QK LayerNorm + 2D RoPE */
 #define VGGT_ATTN_STAGE_CORE 2 /* softmax(q k^T / sqrt(Dh)) v for every set and head */
 #define VGGT_ATTN_STAGE_OUT  3 /* output projection (+ register-mode patch copy) */
+#define VGGT_ATTN_STAGE_ALL  (-1) /* all four (vggt_attn_bf16ops) */
 
 typedef struct vggt_attn_shape {
   int32_t S;          /* frames */
@@ -233,6 +234,24 @@ int vggt_attn_stage(int mode, int stage, const vggt_attn_shape* shape, const voi
                     const void* Wqkv, const void* Wo, const float* q_gamma,
                     const float* q_beta, const float* k_gamma, const float* k_beta,
                     void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The frame, global and register blocks with bf16 attention operands: the
+   computation of vggt_attn_frame / vggt_attn_global /
+   vggt_attn_global_register, but q, k and v are stored in bf16, the
+   probabilities and O are rounded to bf16, and the output projection reads O
+   and Wo (times the same exact power of two) in bf16 -- bf16 x bf16 MFMA with
+   fp32 accumulation throughout, the precision the HTTM article (10100.com,
+   section 05) runs its attention in.  The default calls keep these operands
+   in fp16 (11-bit significands against bf16's 8): with bf16 operands the
+   error of Y against the exact block is about 2.5x larger (relative L1 near
+   4e-3 instead of 1.5e-3).  mode: VGGT_ATTN_MODE_FRAME, _GLOBAL or _REGISTER
+   (else VGGT_ATTN_EINVAL); stage: one VGGT_ATTN_STAGE_* or
+   VGGT_ATTN_STAGE_ALL for the whole call.  Workspace, checks and status as
+   the mode's default call. */
+int vggt_attn_bf16ops(int mode, int stage, const vggt_attn_shape* shape, const void* X,
+                      const void* Wqkv, const void* Wo, const float* q_gamma,
+                      const float* q_beta, const float* k_gamma, const float* k_beta,
+                      void* Y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of vggt_attn_global_subsampled, as vggt_attn_stage. */
 int vggt_attn_subsampled_stage(int stage, const vggt_attn_shape* shape, int32_t sub_h,

@@ -47,6 +47,15 @@ def metrics(y, ref) -> dict:
 TOL_MAX = 1e-2
 TOL_RELL1 = 2e-3
 
+# Bar of the bf16-operand variant (q, k, v, P, O, Wo copy in bf16): its
+# rounding alone gives relL1 ~4.1e-3, max/max ~6e-3 and mean/max ~6e-4 in the
+# CPU emulation of test_precision_budget (which checks these figures), so it
+# is held to relL1 <= 6e-3, max <= 1.5e-2 and -- the mean-absolute reading of
+# "mean relative error" -- mean|err|/max|ref| <= 1e-3.
+BF16OPS_RELL1 = 6e-3
+BF16OPS_MAX = 1.5e-2
+BF16OPS_MEAN = 1e-3
+
 
 def assert_parity(y, ref, label="", tol_rel=TOL_RELL1, tol_max=TOL_MAX):
     m = metrics(y, ref)

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "libvggtattn.h")
 def header_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(vggt_attn_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(vggt_attn_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_boundary():
@@ -151,6 +151,21 @@ def test_stage_errors():
     assert B.vggt_attn_stage(B.MODE_GLOBAL, 9, s, *a, 0x10000000, 1 << 30, None) == B.EINVAL
     assert B.vggt_attn_stage(5, B.STAGE_CORE, s, *a, 0x10000000, 1 << 30, None) == B.EINVAL
     assert B.vggt_attn_stage(B.MODE_GLOBAL, B.STAGE_CORE, s, *a, 0x10000000, 16, None) == B.EWORKSPACE
+
+
+def test_bf16ops_errors():
+    """The bf16-operand entry checks like the default calls, serves the frame,
+    global and register modes only, and takes a stage or STAGE_ALL."""
+    s = B.make_shape(**TINY)
+    a = [FAKE[k] for k in ("X", "Wqkv", "Wo", "qg", "qb", "kg", "kb", "Y")]
+    ws = 0x10000000
+    for mode in (B.MODE_SUBSAMPLED, B.MODE_DESCRIPTOR, B.MODE_MERGED, 9):
+        assert B.vggt_attn_bf16ops(mode, B.STAGE_ALL, s, *a, ws, 1 << 30, None) == B.EINVAL
+    for mode in (B.MODE_FRAME, B.MODE_GLOBAL, B.MODE_REGISTER):
+        assert B.vggt_attn_bf16ops(mode, 7, s, *a, ws, 1 << 30, None) == B.EINVAL
+        assert B.vggt_attn_bf16ops(mode, -2, s, *a, ws, 1 << 30, None) == B.EINVAL
+        assert B.vggt_attn_bf16ops(mode, B.STAGE_ALL, s, *a, ws, 16, None) == B.EWORKSPACE
+        assert B.vggt_attn_bf16ops(mode, B.STAGE_CORE, s, 0, *a[1:], ws, 1 << 30, None) == B.EINVAL
 
 
 def test_status_strings():

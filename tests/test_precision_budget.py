@@ -86,6 +86,17 @@ def test_library_design_fits_the_bar(case):
     assert plain_bf16 > 2e-3, plain_bf16
 
 
+def test_bf16_operand_variant_bar(case):
+    """The bf16-operand variant rounds q, k, v, P, O (and Y) to bf16: its bar
+    (helpers.BF16OPS_*) sits a third or more above what that rounding costs."""
+    from helpers import BF16OPS_MAX, BF16OPS_MEAN, BF16OPS_RELL1, metrics
+    X, p, ref = case
+    m = metrics(emulate(X, p, bf16, bf16, bf16, bf16, bf16, bf16), ref)
+    assert 3e-3 < m["relL1"] < BF16OPS_RELL1 / 1.3, m
+    assert m["max_over_max"] < BF16OPS_MAX / 1.3, m
+    assert m["mean_over_max"] < BF16OPS_MEAN / 1.3, m
+
+
 # ----------------------------------------------------------------------------
 # The attention kernel's softmax reference rule, emulated on the CPU
 # ----------------------------------------------------------------------------

@@ -52,10 +52,16 @@ class Block:
 
     def __init__(self, mode: str, X: torch.Tensor, H: int, grid_h: int, grid_w: int,
                  rope_base=100.0, ln_eps=1e-5, pos_offset=0, workspace=None, sub=(1, 1),
-                 merge=(2, 1, 1, 0)):
+                 merge=(2, 1, 1, 0), operands="fp16"):
         if mode not in _ENTRY:
             raise ValueError(f"unknown mode {mode!r}")
+        if operands not in ("fp16", "bf16"):
+            raise ValueError(f"unknown attention operand type {operands!r}")
+        if operands == "bf16" and mode not in ("frame", "global", "register"):
+            raise ValueError("bf16 attention operands serve the frame, global and register modes")
         self.mode = mode
+        # attention operands (q, k, v, P, O, Wo copy): fp16, or the bf16 variant
+        self.bf16 = operands == "bf16"
         self.sub = (int(sub[0]), int(sub[1]))  # subsampled mode: (sub_h, sub_w) windows
         # merged mode: (frames per block, window rows, window columns, merges per block)
         self.merge = tuple(int(x) for x in merge)
@@ -81,6 +87,9 @@ class Block:
         elif self.mode == "merged":
             st = B.vggt_attn_global_merged(args[0], *self.merge, *args[1:],
                                            _stream_handle(stream))
+        elif self.bf16:
+            st = B.vggt_attn_bf16ops(B.MODES[self.mode], B.STAGE_ALL, *args,
+                                     _stream_handle(stream))
         else:
             st = getattr(B, _ENTRY[self.mode])(*args, _stream_handle(stream))
         if st != B.OK:
@@ -95,6 +104,8 @@ class Block:
         elif self.mode == "merged":
             st = B.vggt_attn_merged_stage(stage, args[0], *self.merge, *args[1:],
                                           _stream_handle(stream))
+        elif self.bf16:
+            st = B.vggt_attn_bf16ops(B.MODES[self.mode], stage, *args, _stream_handle(stream))
         else:
             st = B.vggt_attn_stage(B.MODES[self.mode], stage, *args, _stream_handle(stream))
         if st != B.OK:

@@ -18,6 +18,7 @@ STATIC_SCRATCH_BYTES = 128 << 20
 MODE_FRAME, MODE_GLOBAL, MODE_REGISTER, MODE_SUBSAMPLED, MODE_DESCRIPTOR, MODE_MERGED = \
     0, 1, 2, 3, 4, 5
 STAGE_PREP, STAGE_QKV, STAGE_CORE, STAGE_OUT = 0, 1, 2, 3
+STAGE_ALL = -1
 STATUS_OFFSET = 16
 RANGE_X, RANGE_WQKV, RANGE_WO, RANGE_AFFINE, RANGE_SCALE = 1, 2, 4, 8, 16
 MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
@@ -25,7 +26,8 @@ MODES = {"frame": MODE_FRAME, "global": MODE_GLOBAL, "register": MODE_REGISTER,
 
 EXPORTS = ("vggt_attn_workspace_bytes", "vggt_attn_frame", "vggt_attn_global",
            "vggt_attn_global_register", "vggt_attn_global_subsampled", "vggt_attn_global_rows",
-           "vggt_attn_stage", "vggt_attn_subsampled_stage", "vggt_attn_global_rows_stage",
+           "vggt_attn_stage", "vggt_attn_bf16ops", "vggt_attn_subsampled_stage",
+           "vggt_attn_global_rows_stage",
            "vggt_attn_global_merged", "vggt_attn_merged_stage",
            "vggt_attn_desc_cache_bytes", "vggt_attn_desc_cache_init", "vggt_attn_desc_append",
            "vggt_attn_desc_attend", "vggt_attn_desc_attend_stage",
@@ -113,6 +115,8 @@ def _load(path: str) -> ctypes.CDLL:
         f.argtypes = _CALL_ARGS
     L.vggt_attn_stage.restype = ctypes.c_int
     L.vggt_attn_stage.argtypes = [ctypes.c_int, ctypes.c_int] + _CALL_ARGS
+    L.vggt_attn_bf16ops.restype = ctypes.c_int
+    L.vggt_attn_bf16ops.argtypes = [ctypes.c_int, ctypes.c_int] + _CALL_ARGS
     sub = [ctypes.POINTER(vggt_attn_shape), ctypes.c_int32, ctypes.c_int32] + _CALL_ARGS[1:]
     L.vggt_attn_global_subsampled.restype = ctypes.c_int
     L.vggt_attn_global_subsampled.argtypes = sub
@@ -199,6 +203,12 @@ def vggt_attn_global_register(shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_be
 def vggt_attn_stage(mode, stage, shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y,
                     workspace, workspace_bytes, stream) -> int:
     return _call("vggt_attn_stage", mode, stage, ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
+                 q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
+
+
+def vggt_attn_bf16ops(mode, stage, shape, X, Wqkv, Wo, q_gamma, q_beta, k_gamma, k_beta, Y,
+                      workspace, workspace_bytes, stream) -> int:
+    return _call("vggt_attn_bf16ops", mode, stage, ctypes.byref(shape), X, Wqkv, Wo, q_gamma,
                  q_beta, k_gamma, k_beta, Y, workspace, workspace_bytes, stream)
 
 

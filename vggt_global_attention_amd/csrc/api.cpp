@@ -98,6 +98,12 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   p->base = s->rope_base;
   p->eps = s->ln_eps;
   p->keep_status = o.keep_status;
+  // the bf16-operand variant serves the plain sets: frame, global (also a
+  // query window of it) and register
+  if (o.bf16_ops && mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
+      mode != VGGT_ATTN_MODE_REGISTER)
+    return VGGT_ATTN_EINVAL;
+  p->bf16_ops = o.bf16_ops;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {
@@ -438,6 +444,18 @@ int vggt_attn_global(VGGT_ARGS) {
 
 int vggt_attn_global_register(VGGT_ARGS) {
   return run(VGGT_ATTN_MODE_REGISTER, CallOpts(), VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+}
+
+int vggt_attn_bf16ops(int mode, int stage, VGGT_ARGS) {
+  if (mode != VGGT_ATTN_MODE_FRAME && mode != VGGT_ATTN_MODE_GLOBAL &&
+      mode != VGGT_ATTN_MODE_REGISTER)
+    return VGGT_ATTN_EINVAL;
+  if (stage != VGGT_ATTN_STAGE_ALL && (stage < VGGT_ATTN_STAGE_PREP || stage > VGGT_ATTN_STAGE_OUT))
+    return VGGT_ATTN_EINVAL;
+  CallOpts o;
+  o.bf16_ops = true;
+  if (stage == VGGT_ATTN_STAGE_ALL) return run(mode, o, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, VGGT_PASS);
+  return run(mode, o, stage, stage, VGGT_PASS);
 }
 
 int vggt_attn_stage(int mode, int stage, VGGT_ARGS) {

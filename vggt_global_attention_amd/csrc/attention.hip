@@ -139,9 +139,9 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) 
 // O^T blocks are 16 features x 16 queries: accumulator i of block db holds
 // feature 16 db + 4g + i.
 // ---------------------------------------------------------------------------
-template <int NB>  // 16-row query blocks per wave
+template <int NB, typename T8 = f16x8>  // 16-row query blocks per wave, operand type
 struct Rows {
-  f16x8 qf[NB][2];  // B operand of S^T: q[row 16 qb + r][32 dc + 8 g .. +7]
+  T8 qf[NB][2];     // B operand of S^T: q[row 16 qb + r][32 dc + 8 g .. +7]
   float bound[NB];  // upper bound of every logit of the row (-inf: no row)
   float m[NB];      // reference the logits are taken relative to
   float l[NB];      // partial row sum (this lane's keys)
@@ -199,8 +199,8 @@ struct Lanes {
   }
 };
 
-template <int NB>
-__device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t seq0, int qloc0, int L,
+template <int NB, typename T8, typename T>
+__device__ __forceinline__ void rows_init(Rows<NB, T8>& R, const T* qh, int64_t seq0, int qloc0, int L,
                                           int lane, float kmax) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -211,9 +211,9 @@ __device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t se
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc) {
       if (ok) {
-        R.qf[qb][dc] = *reinterpret_cast<const f16x8*>(qh + (seq0 + row) * kDh + dc * 32 + g * 8);
+        R.qf[qb][dc] = *reinterpret_cast<const T8*>(qh + (seq0 + row) * kDh + dc * 32 + g * 8);
       } else {
-        R.qf[qb][dc] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        R.qf[qb][dc] = __builtin_bit_cast(T8, u32x4{0u, 0u, 0u, 0u});
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -243,20 +243,24 @@ __device__ __forceinline__ void rows_init(Rows<NB>& R, const f16* qh, int64_t se
 // KB = 2 (a short last tile of at most 32 keys): key blocks 0 and 1 only,
 // which hold keys 0..31, and the first PV step; the other probabilities are
 // exactly zero, so the result is the same bit for bit.
-template <bool MASK, int KB, bool W, int NB>
-__device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const char* Ks,
+template <bool MASK, int KB, bool W, int NB, typename T8>
+__device__ __forceinline__ void tile_probs(Rows<NB, T8>& R, const Lanes& ln, const char* Ks,
                                            const f16* Ns, int lane, int valid, bool first,
-                                           bool eager, f16x8 (&pf)[NB][2]) {
+                                           bool eager, T8 (&pf)[NB][2]) {
   static_assert(KB == 4 || KB == 2, "whole tile or its first 32 keys");
+  constexpr bool B16 = std::is_same<T8, bf16x8>::value;
+  static_assert(!(W && B16), "size-weighted rows run on fp16 operands");
+  typedef typename Ops16<B16>::T T;
+  typedef typename Ops16<B16>::T2 T2;
   constexpr int NC = KB / 2;  // 32-key PV steps
   const int g = lane >> 4;
   f32x4 S[KB][NB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    f16x8 kf[2];
+    T8 kf[2];
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc)
-      kf[dc] = *reinterpret_cast<const f16x8*>(Ks + ln.ka[kb & 1][dc] + (kb >> 1) * 4096);
+      kf[dc] = *reinterpret_cast<const T8*>(Ks + ln.ka[kb & 1][dc] + (kb >> 1) * 4096);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
       f32x4 c = R.negm[qb];
@@ -319,21 +323,21 @@ __device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const c
   for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      f16x8 v;
+      T8 v;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const f32x2 e2 = {__builtin_amdgcn_exp2f(S[2 * c + half][qb][i]),
                             __builtin_amdgcn_exp2f(S[2 * c + half][qb][i + 1])};
-          const f16x2 h2 = __builtin_convertvector(e2, f16x2);
+          const T2 h2 = __builtin_convertvector(e2, T2);
           v[4 * half + i] = h2[0];
           v[4 * half + i + 1] = h2[1];
           if constexpr (W) {
             const f16x2 w2 = {wk[2 * c + half][i], wk[2 * c + half][i + 1]};
-            R.l[qb] = __builtin_amdgcn_fdot2(h2, w2, R.l[qb], false);
+            R.l[qb] = dot2_acc(h2, w2, R.l[qb]);
           } else {
-            R.l[qb] = __builtin_amdgcn_fdot2(h2, f16x2{(f16)1.f, (f16)1.f}, R.l[qb], false);
+            R.l[qb] = dot2_acc(h2, T2{(T)1.f, (T)1.f}, R.l[qb]);
           }
         }
       pf[qb][c] = v;
@@ -341,18 +345,18 @@ __device__ __forceinline__ void tile_probs(Rows<NB>& R, const Lanes& ln, const c
 }
 
 // One 64-key tile: its probabilities (tile_probs), then O^T += V^T P^T.
-template <bool MASK, int KB = 4, bool W = false, int NB>
-__device__ __forceinline__ void tile_run(Rows<NB>& R, const Lanes& ln, const char* Ks,
+template <bool MASK, int KB = 4, bool W = false, int NB, typename T8>
+__device__ __forceinline__ void tile_run(Rows<NB, T8>& R, const Lanes& ln, const char* Ks,
                                          const char* Vs, const f16* Ns, int lane, int valid,
                                          bool first, bool eager) {
   constexpr int NC = KB / 2;  // 32-key PV steps
-  f16x8 pf[NB][2];
+  T8 pf[NB][2];
   tile_probs<MASK, KB, W>(R, ln, Ks, Ns, lane, valid, first, eager, pf);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const f16x8 vf = *reinterpret_cast<const f16x8*>(Vs + ln.va[db & 1][c] + (db >> 1) * 4096);
+      const T8 vf = *reinterpret_cast<const T8*>(Vs + ln.va[db & 1][c] + (db >> 1) * 4096);
 #pragma unroll
       for (int qb = 0; qb < NB; ++qb) R.O[db][qb] = mfma16x16x32(vf, pf[qb][c], R.O[db][qb]);
     }
@@ -447,8 +451,8 @@ __device__ __forceinline__ void sga_columns(Rows<NB>& R, const AttnArgs& p, int 
   }
 }
 
-template <int NB>
-__device__ __forceinline__ void rows_store(const Rows<NB>& R, f16* qh, int64_t seq0, int qloc0, int L,
+template <int NB, typename T8, typename T>
+__device__ __forceinline__ void rows_store(const Rows<NB, T8>& R, T* qh, int64_t seq0, int qloc0, int L,
                                            int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -458,17 +462,17 @@ __device__ __forceinline__ void rows_store(const Rows<NB>& R, f16* qh, int64_t s
     if (row < L) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        f16x4 o;
+        typename Ops16<std::is_same<T, bf16>::value>::T4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (f16)(R.O[db][qb][i] * inv);
-        *reinterpret_cast<f16x4*>(qh + (seq0 + row) * kDh + db * 16 + 4 * g) = o;
+        for (int i = 0; i < 4; ++i) o[i] = (T)(R.O[db][qb][i] * inv);
+        *reinterpret_cast<decltype(o)*>(qh + (seq0 + row) * kDh + db * 16 + 4 * g) = o;
       }
     }
   }
 }
 
-template <int NB>
-__device__ __forceinline__ void rows_store_partial(const Rows<NB>& R, float* po, float2* pml, int lrow0,
+template <int NB, typename T8>
+__device__ __forceinline__ void rows_store_partial(const Rows<NB, T8>& R, float* po, float2* pml, int lrow0,
                                                    int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -544,9 +548,11 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // K / V^T tiles are double buffered in LDS and copied one tile ahead by the
 // load unit (global_load_lds, no register staging), with one workgroup
 // barrier per tile.
-template <int QB, int NW, bool SGA, bool W>
+template <int QB, int NW, bool SGA, bool W, bool B16>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
+  static_assert(!(B16 && (SGA || W)), "the bf16-operand variant serves plain sets");
+  typedef typename Ops16<B16>::T T;  // q, k, v, P and O
   // K / V^T tiles [buffer][K, V^T][64 rows x 128 bytes], then in merged mode
   // (W) the sizes of the tile's 64 keys, 1 KB per buffer (the first 128
   // bytes used; see issue()).  One LDS object: with a second one the
@@ -568,14 +574,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   const int L = p.L;
   const int qloc0 = p.q0 + bc.qt * BQ + wave * QB * 32;
   const bool active = __builtin_amdgcn_readfirstlane(qloc0) < L;
-  f16* qh = p.q + (int64_t)bc.h * p.rows * kDh;
+  T* qh = reinterpret_cast<T*>(p.q) + (int64_t)bc.h * p.rows * kDh;
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
   const f16* nh = W ? p.nw + (int64_t)bc.h * p.kv_rows + kv0 : nullptr;
 
   // the wave's QB * 32 queries as 2 QB blocks of 16 (16x16x32 tile)
   using LanesT = Lanes;
-  Rows<2 * QB> R;
+  Rows<2 * QB, typename Ops16<B16>::T8> R;
   rows_init(R, qh, seq0, qloc0, L, lane, p.sc->kmax[bc.h]);
 
   // key tiles [t0, t1): all of them, or one key range of a split workgroup
@@ -678,7 +684,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
     }
   }
   // the diagonal and mean columns enter once per row: in its last key range
-  if (SGA && active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, lane);
+  if constexpr (SGA) {
+    if (active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, lane);
+  }
   if (kSplit && bc.unit >= 0) {
     // a key range of a split workgroup: unnormalised state for the merge
     float* po = p.part + (int64_t)bc.unit * BQ * kDh;
@@ -696,7 +704,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
 // stored in fp16 in place of the row's q like an unsplit workgroup.  Blocks:
 // (XCD x, tail workgroup i of x, 16 rows); 16 threads per row, 4 features
 // each.
-template <int BQ>
+template <int BQ, bool B16>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   constexpr int per_wg = BQ / 16;
   const int tail_max = p.umax / p.split_p;
@@ -725,11 +733,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
     for (int e4 = 0; e4 < 4; ++e4) o[e4] = fmaf(w, oi[e4], o[e4]);
   }
   const float inv = 1.f / l;
-  f16x4 out;
+  typedef typename Ops16<B16>::T T;
+  typename Ops16<B16>::T4 out;
 #pragma unroll
-  for (int e4 = 0; e4 < 4; ++e4) out[e4] = (f16)(o[e4] * inv);
-  f16* qh = p.q + (int64_t)c.h * p.rows * kDh;
-  *reinterpret_cast<f16x4*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
+  for (int e4 = 0; e4 < 4; ++e4) out[e4] = (T)(o[e4] * inv);
+  T* qh = reinterpret_cast<T*>(p.q) + (int64_t)c.h * p.rows * kDh;
+  *reinterpret_cast<decltype(out)*>(qh + ((int64_t)c.s * p.seq_stride + row) * kDh + f) = out;
 }
 
 // Split tail.  Each XCD walks a contiguous range of the W workgroups on its
@@ -790,7 +799,7 @@ static SplitPlan choose_split(const Plan& p, int64_t W, int ntiles, int per_cu) 
   return sp;
 }
 
-template <int QB, int NW, bool SGA, bool W = false>
+template <int QB, int NW, bool SGA, bool W = false, bool B16 = false>
 static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   constexpr int BQ = NW * QB * 32;
   AttnArgs g{};
@@ -828,7 +837,7 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
     static std::atomic<int> occupancy{0};
     int per_cu = occupancy.load(std::memory_order_relaxed);
     if (per_cu == 0) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA, W>,
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<QB, NW, SGA, W, B16>,
                                                        NW * 64, 0) != hipSuccess)
         per_cu = -1;
       occupancy.store(per_cu, std::memory_order_relaxed);
@@ -839,11 +848,11 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.xcd_slots = sp.xcd_slots;
   g.umax = sp.umax;
   g.part = reinterpret_cast<float*>(a.ws + p.off_split);
-  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA, W>), dim3((unsigned)sp.grid), dim3(NW * 64), 0, st,
-                     g);
+  hipLaunchKernelGGL((attn_kernel<QB, NW, SGA, W, B16>), dim3((unsigned)sp.grid), dim3(NW * 64), 0,
+                     st, g);
   if (sp.P > 1) {
     const int tail_max = sp.umax / sp.P;
-    hipLaunchKernelGGL(attn_merge_kernel<BQ>, dim3((unsigned)(kXcds * tail_max * (BQ / 16))),
+    hipLaunchKernelGGL((attn_merge_kernel<BQ, B16>), dim3((unsigned)(kXcds * tail_max * (BQ / 16))),
                        dim3(256), 0, st, g);
   }
   return hipGetLastError();
@@ -854,6 +863,17 @@ hipError_t launch_core(const Plan& p, const Ptrs& a, hipStream_t st) {
   if (p.mode == VGGT_ATTN_MODE_MERGED) {
     if (p.attn_waves == 8) return launch_attn_t<2, 8, false, true>(p, a, st);
     return launch_attn_t<1, 4, false, true>(p, a, st);
+  }
+  if (p.bf16_ops) {
+    // the bf16-operand variant of the plain sets (global, frame, register)
+    if (p.attn_waves == 8) {
+      if (p.attn_qb == 2) return launch_attn_t<2, 8, false, false, true>(p, a, st);
+      if (p.attn_qb == 1) return launch_attn_t<1, 8, false, false, true>(p, a, st);
+    } else {
+      if (p.attn_qb == 2) return launch_attn_t<2, 4, false, false, true>(p, a, st);
+      if (p.attn_qb == 1) return launch_attn_t<1, 4, false, false, true>(p, a, st);
+    }
+    return hipErrorInvalidValue;
   }
   if (p.attn_waves == 8) {
     if (p.attn_qb == 2) return launch_attn_t<2, 8, false>(p, a, st);

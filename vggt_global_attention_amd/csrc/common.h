@@ -77,6 +77,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// c + a.x b.x + a.y b.y in fp32 (v_dot2 of two 16-bit pairs)
+__device__ __forceinline__ float dot2_acc(f16x2 a, f16x2 b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+__device__ __forceinline__ float dot2_acc(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// 16-bit operand types of the attention core and the output projection:
+// fp16 (the default path) or bf16 (the bf16-operand variant).
+template <bool B16>
+struct Ops16 {
+  typedef f16 T;
+  typedef f16x2 T2;
+  typedef f16x4 T4;
+  typedef f16x8 T8;
+};
+template <>
+struct Ops16<true> {
+  typedef bf16 T;
+  typedef bf16x2 T2;
+  typedef bf16x4 T4;
+  typedef bf16x8 T8;
+};
+
 __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }

@@ -114,11 +114,12 @@ constexpr float kQScale = 0.18033688011112042f;
 // half pairs with i + 16, registers r and r + 8 of the lane) and fp16
 // conversion into o[fb][rq] = features fb*32 + 8*rq + 4*h .. +3.  NORM: also
 // the squared L2 norm of the fp16 vector, summed over the lane pair.
-template <bool NORM>
-__device__ __forceinline__ void ln_rope_f16(const f32x16& a0, const f32x16& a1,
-                                            const float (&gm)[2][16], const float (&bt)[2][16],
-                                            float eps, const float2* rope, int2 pos, int h,
-                                            f16x4 (&o)[2][4], float& n2) {
+template <bool NORM, typename T4>
+__device__ __forceinline__ void ln_rope_16(const f32x16& a0, const f32x16& a1,
+                                           const float (&gm)[2][16], const float (&bt)[2][16],
+                                           float eps, const float2* rope, int2 pos, int h,
+                                           T4 (&o)[2][4], float& n2) {
+  typedef decltype(T4{}.xy) T2;
   float y[2][16];
   float s1 = 0.f;
 #pragma unroll
@@ -157,11 +158,11 @@ __device__ __forceinline__ void ln_rope_f16(const f32x16& a0, const f32x16& a1,
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const f32x4 v = {y[fb][4 * rq], y[fb][4 * rq + 1], y[fb][4 * rq + 2], y[fb][4 * rq + 3]};
-      o[fb][rq] = __builtin_convertvector(v, f16x4);
+      o[fb][rq] = __builtin_convertvector(v, T4);
       if (NORM) {
-        const f16x2 lo = {o[fb][rq][0], o[fb][rq][1]}, hi = {o[fb][rq][2], o[fb][rq][3]};
-        n2 = __builtin_amdgcn_fdot2(lo, lo, n2, false);
-        n2 = __builtin_amdgcn_fdot2(hi, hi, n2, false);
+        const T2 lo = {o[fb][rq][0], o[fb][rq][1]}, hi = {o[fb][rq][2], o[fb][rq][3]};
+        n2 = dot2_acc(lo, lo, n2);
+        n2 = dot2_acc(hi, hi, n2);
       }
     }
   if (NORM) n2 += __shfl_xor(n2, 32);
@@ -181,30 +182,32 @@ __device__ __forceinline__ void load_affine(const float* gam, const float* bet, 
     }
 }
 
-// v of one (token, head) in the lane's feature order (as ln_rope_f16 leaves
-// q and k), times the range scale vs, to fp16.
-__device__ __forceinline__ void v_rows_f16(const f32x16& a0, const f32x16& a1, float vs,
-                                           f16x4 (&o)[2][4]) {
+// v of one (token, head) in the lane's feature order (as ln_rope_16 leaves
+// q and k), times the range scale vs, to the operand type.
+template <typename T4>
+__device__ __forceinline__ void v_rows_16(const f32x16& a0, const f32x16& a1, float vs,
+                                          T4 (&o)[2][4]) {
 #pragma unroll
   for (int rq = 0; rq < 4; ++rq) {
     const f32x4 v0 = {a0[4 * rq] * vs, a0[4 * rq + 1] * vs, a0[4 * rq + 2] * vs, a0[4 * rq + 3] * vs};
     const f32x4 v1 = {a1[4 * rq] * vs, a1[4 * rq + 1] * vs, a1[4 * rq + 2] * vs, a1[4 * rq + 3] * vs};
-    o[0][rq] = __builtin_convertvector(v0, f16x4);
-    o[1][rq] = __builtin_convertvector(v1, f16x4);
+    o[0][rq] = __builtin_convertvector(v0, T4);
+    o[1][rq] = __builtin_convertvector(v1, T4);
   }
 }
 
-enum { kEpiQKV = 0, kEpiOut = 1 };
+// Epilogues: the QKV projection and the output projection, each for fp16
+// (default) or bf16 (the bf16-operand variant) attention operands: q, k and
+// v stored in that type, the output projection's O and Wo read in it.
+enum { kEpiQKV = 0, kEpiOut = 1, kEpiQKVB = 2, kEpiOutB = 3 };
+constexpr bool epi_qkv(int e) { return e == kEpiQKV || e == kEpiQKVB; }
+constexpr bool epi_b16(int e) { return e == kEpiQKVB || e == kEpiOutB; }
 
 template <int EPI>
-struct GemmTypes;
-template <>
-struct GemmTypes<kEpiQKV> {
-  typedef bf16x8 V8;
-};
-template <>
-struct GemmTypes<kEpiOut> {
-  typedef f16x8 V8;
+struct GemmTypes {
+  // MFMA operands: X and Wqkv are bf16; O and Wo are the attention operand type
+  typedef typename std::conditional<epi_qkv(EPI) || epi_b16(EPI), bf16x8, f16x8>::type V8;
+  typedef Ops16<epi_b16(EPI)> Out;  // QKV: the stored q, k, v
 };
 
 __device__ __forceinline__ int swz(int row, int col) {
@@ -218,7 +221,10 @@ __device__ __forceinline__ int swz(int row, int col) {
 template <int EPI, int TB>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2][TB],
                                               int64_t mbase, int fbase, int j, int h, int lane) {
-  if (EPI == kEpiQKV) {
+  typedef typename GemmTypes<EPI>::Out::T OT;
+  typedef typename GemmTypes<EPI>::Out::T2 OT2;
+  typedef typename GemmTypes<EPI>::Out::T4 OT4;
+  if (epi_qkv(EPI)) {
     const int fq = fbase + g.f_off;
     const int blk = fq / g.d;  // 0: q, 1: k, 2: v
     const int hd = (fq - blk * g.d) / kDh;
@@ -226,7 +232,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
       float gm[2][16], bt[2][16];
       load_affine((blk == 0 ? g.qg : g.kg) + hd * kDh, (blk == 0 ? g.qb : g.kb) + hd * kDh,
                   blk == 0 ? kQScale : 1.f, h, gm, bt);
-      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
+      OT* dst = reinterpret_cast<OT*>(blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
       auto block = [&](auto norm_c) {
         constexpr bool NORM = decltype(norm_c)::value;
         float kmx = 0.f;
@@ -234,16 +240,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
         for (int tb = 0; tb < TB; ++tb) {
           const int64_t w = mbase + tb * 32 + j;
           const int64_t src = row_src(g, w);
-          f16x4 o[2][4];
+          OT4 o[2][4];
           float n2;
-          ln_rope_f16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
-                            n2);
+          ln_rope_16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
+                           n2);
           if (!g.real_only || src >= 0) {
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
               for (int rq = 0; rq < 4; ++rq)
-                *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
+                *reinterpret_cast<OT4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
                     o[fb][rq];
           }
           if (NORM && src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
@@ -261,22 +267,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
       }
     } else if (g.v_rows) {
       const float vs = __builtin_amdgcn_ldexpf(1.f, range_exponent(g.sc->xnorm * g.sc->wvnorm));
-      f16* dst = g.vt + (int64_t)hd * g.rows * kDh;
+      OT* dst = reinterpret_cast<OT*>(g.vt) + (int64_t)hd * g.rows * kDh;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
-        f16x4 o[2][4];
-        v_rows_f16(acc[0][tb], acc[1][tb], vs, o);
+        OT4 o[2][4];
+        v_rows_16(acc[0][tb], acc[1][tb], vs, o);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
-            *reinterpret_cast<f16x4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
+            *reinterpret_cast<OT4*>(dst + (w + g.dst_off) * kDh + fb * 32 + 8 * rq + 4 * h) =
                 o[fb][rq];
       }
     } else {
       const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
-      f16* dst = g.vt + (int64_t)hd * kDh * g.rows;
+      OT* dst = reinterpret_cast<OT*>(g.vt) + (int64_t)hd * kDh * g.rows;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
@@ -291,7 +297,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            dst[(int64_t)e * g.rows + pos] = (f16)ldexpf(acc[fb][tb][r], kv);
+            dst[(int64_t)e * g.rows + pos] = (OT)ldexpf(acc[fb][tb][r], kv);
           }
       }
     }
@@ -338,7 +344,10 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
                                                      int64_t mbase, int fbase, int j, int h,
                                                      int lane, char* lds) {
   constexpr int TB = 4;
-  if (EPI == kEpiQKV) {
+  typedef typename GemmTypes<EPI>::Out::T OT;
+  typedef typename GemmTypes<EPI>::Out::T2 OT2;
+  typedef typename GemmTypes<EPI>::Out::T4 OT4;
+  if (epi_qkv(EPI)) {
     const int fq = fbase + g.f_off;
     const int blk = fq / g.d;  // 0: q, 1: k, 2: v
     const int hd = (fq - blk * g.d) / kDh;
@@ -352,13 +361,13 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int tl = tb * 32 + j;
-        f16x4 o[2][4];
-        v_rows_f16(acc[0][tb], acc[1][tb], vs, o);
+        OT4 o[2][4];
+        v_rows_16(acc[0][tb], acc[1][tb], vs, o);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
-            *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
+            *reinterpret_cast<OT4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
                 o[fb][rq];
       }
       lds_wave_sync();
@@ -384,16 +393,16 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
         for (int tb = 0; tb < TB; ++tb) {
           const int tl = tb * 32 + j;
           const int64_t src = row_src(g, mbase + tl);
-          f16x4 o[2][4];
+          OT4 o[2][4];
           float n2;
-          ln_rope_f16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
-                            n2);
+          ln_rope_16<NORM>(acc[0][tb], acc[1][tb], gm, bt, g.eps, g.rope, rope_pos(g, src), h, o,
+                           n2);
           // features fb*32 + 8*rq + 4*h .. +3: 16-byte chunk fb*4 + rq, half h
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq)
-              *reinterpret_cast<f16x4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
+              *reinterpret_cast<OT4*>(lds + tl * 128 + (((fb * 4 + rq) ^ (tl & 7)) << 4) + h * 8) =
                   o[fb][rq];
           if (NORM && src >= 0) kmx = fmaxf(kmx, sqrtf(n2));
         }
@@ -409,7 +418,7 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
         block(std::false_type());
       }
       lds_wave_sync();
-      f16* dst = (blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
+      OT* dst = reinterpret_cast<OT*>(blk == 0 ? g.q : g.k) + (int64_t)hd * g.rows * kDh;
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
         const int q = it * 64 + lane, tl = q >> 3, c = q & 7;
@@ -434,10 +443,10 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const f32x2 v = {acc[fb][tb][r] * vs, acc[fb][tb][r + 1] * vs};
-            const f16x2 o = __builtin_convertvector(v, f16x2);
+            const OT2 o = __builtin_convertvector(v, OT2);
             const int e0 = fb * 32 + 8 * (r >> 2) + (r & 3);  // feature minus 4*h
-            *reinterpret_cast<f16*>(base + e0 * 256) = o[0];
-            *reinterpret_cast<f16*>(base + (e0 + 1) * 256) = o[1];
+            *reinterpret_cast<OT*>(base + e0 * 256) = o[0];
+            *reinterpret_cast<OT*>(base + (e0 + 1) * 256) = o[1];
           }
       }
       lds_wave_sync();
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
   m0 += g.m_first;
   // query rows outside the window need no q (whole workgroup leaves)
-  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kGemmBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (epi_qkv(EPI) && n0 + g.f_off < g.d && (m0 + kGemmBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (int64_t)n0 * g.K;
   const uint16_t* Bbase = reinterpret_cast<const uint16_t*>(g.B);
@@ -530,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     const int c = tid + 256 * i, row = c >> 3, col = c & 7;
     soff[i] = swz(row, col);
     aptr[i] = A + (int64_t)row * g.K + col * 8;
-    if (EPI == kEpiQKV) {
+    if (epi_qkv(EPI)) {
       const int64_t src = row_src(g, m0 + row);
       bval[i] = src >= 0;
       bptr[i] = Bbase + (bval[i] ? src : 0) * g.K + col * 8;
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) A4[i] = *reinterpret_cast<const u32x4*>(aptr[i] + kt * kGemmBK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (EPI == kEpiQKV) {
+      if (epi_qkv(EPI)) {
         B4[i] = bval[i] ? *reinterpret_cast<const u32x4*>(bptr[i] + kt * kGemmBK) : u32x4{0, 0, 0, 0};
       } else {
         B4[i] = *reinterpret_cast<const u32x4*>(bptr[i] + (int64_t)kt * g.rows * kDh);
@@ -665,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
   }
   m0 += g.m_first;
   // query rows outside the window need no q (whole workgroup leaves)
-  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kDmaBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (epi_qkv(EPI) && n0 + g.f_off < g.d && (m0 + kDmaBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   // DMA sources of this lane: A rows (q*4 + wave)*16 + lane/4 (q < 2), B rows
   // likewise (q < 4); column chunk (lane%4) ^ ((lane/16) & 3).
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t w = m0 + (q * 4 + wave) * 16 + lrow;
-    if (EPI == kEpiQKV) {
+    if (epi_qkv(EPI)) {
       // rows without a token read X row 0: finite values whose outputs are
       // masked keys or never read
       const int64_t src = row_src(g, w);
@@ -695,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
     for (int q = 0; q < 2; ++q) dma16(aptr[q] + kt * kDmaBK, base + (q * 4 + wave) * 1024);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint16_t* src = EPI == kEpiQKV
+      const uint16_t* src = epi_qkv(EPI)
                                 ? bptr[q] + kt * kDmaBK
                                 : bptr[q] + (int64_t)(kt >> 1) * g.rows * kDh + (kt & 1) * kDmaBK;
       dma16(src, base + kAB + (q * 4 + wave) * 1024);
@@ -802,7 +811,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     n0 = (logical % ntn) * kWBN;
   }
   m0 += g.m_first;
-  if (EPI == kEpiQKV && n0 + g.f_off < g.d && (m0 + kWBM <= g.q_lo || m0 >= g.q_hi)) return;
+  if (epi_qkv(EPI) && n0 + g.f_off < g.d && (m0 + kWBM <= g.q_lo || m0 >= g.q_hi)) return;
 
   // DMA: instruction q of wave w covers rows (q*8 + w)*8 .. +7 (q < 4) of A
   // and of B; lane row lane/8.
@@ -817,7 +826,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     const int lcol = (lane & 7) ^ lrow ^ ((r0 >> 3) & 1);
     aptr[q] = A + (int64_t)(n0 + r0 + lrow) * g.K + lcol * 8;
     const int64_t w = m0 + r0 + lrow;
-    if (EPI == kEpiQKV) {
+    if (epi_qkv(EPI)) {
       const int64_t src = row_src(g, w);  // rows without a token read X row 0 (finite, unused)
       bptr[q] = Bb + (src >= 0 ? src : 0) * g.K + lcol * 8;
     } else {
@@ -830,7 +839,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     for (int q = 0; q < 4; ++q) dma16(aptr[q] + kt * kWBK, base + (q * 8 + wave) * 1024);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint16_t* src = EPI == kEpiQKV ? bptr[q] + kt * kWBK
+      const uint16_t* src = epi_qkv(EPI) ? bptr[q] + kt * kWBK
                                            : bptr[q] + (int64_t)kt * g.rows * kDh;
       dma16(src, base + kAB + (q * 8 + wave) * 1024);
     }
@@ -955,6 +964,19 @@ static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   return g;
 }
 
+// One GEMM launch of `blocks` workgroups with the kernel family `kind`
+// (2: 256 x 256 tiles, 1: DMA-fed, 0: plain).
+template <int EPI>
+static void launch_gemm(int kind, int blocks, const GemmArgs& g, hipStream_t st) {
+  if (kind == 2) {
+    hipLaunchKernelGGL(gemm_wide_kernel<EPI>, dim3(blocks), dim3(512), 0, st, g);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL(gemm_dma_kernel<EPI>, dim3(blocks), dim3(256), 0, st, g);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(blocks), dim3(256), 0, st, g);
+  }
+}
+
 hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   GemmArgs g = base_args(p, a);
   g.A = a.Wqkv;
@@ -964,15 +986,13 @@ hipError_t launch_qkv(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.K = p.d;
   const int kind = gemm_kind(p, g.Nf);
   g.fgroups = feature_groups(g.Nf, g.K, 2, kind == 2 ? kWBN : kGemmBN);
-  if (kind == 2) {
-    const int blocks = (int)(p.rows / kWBM) * (g.Nf / kWBN);
-    hipLaunchKernelGGL(gemm_wide_kernel<kEpiQKV>, dim3(blocks), dim3(512), 0, st, g);
-  } else if (kind == 1) {
-    const int blocks = (int)(p.rows / kDmaBM) * (g.Nf / kDmaBN);
-    hipLaunchKernelGGL(gemm_dma_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+  const int64_t bm = kind == 2 ? kWBM : kind == 1 ? kDmaBM : kGemmBM;
+  const int64_t bn = kind == 2 ? kWBN : kind == 1 ? kDmaBN : kGemmBN;
+  const int blocks = (int)(p.rows / bm) * (int)(g.Nf / bn);
+  if (p.bf16_ops) {
+    launch_gemm<kEpiQKVB>(kind, blocks, g, st);
   } else {
-    const int blocks = (int)(p.rows / kGemmBM) * (g.Nf / kGemmBN);
-    hipLaunchKernelGGL(gemm_kernel<kEpiQKV>, dim3(blocks), dim3(256), 0, st, g);
+    launch_gemm<kEpiQKV>(kind, blocks, g, st);
   }
   return hipGetLastError();
 }
@@ -1053,12 +1073,10 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   const int64_t hi = p.window ? (p.L + bm - 1) / bm * bm : p.rows;
   g.m_first = lo;
   const int blocks = (int)((hi - lo) / bm) * (g.Nf / bn);
-  if (kind == 2) {
-    hipLaunchKernelGGL(gemm_wide_kernel<kEpiOut>, dim3(blocks), dim3(512), 0, st, g);
-  } else if (kind == 1) {
-    hipLaunchKernelGGL(gemm_dma_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+  if (p.bf16_ops) {
+    launch_gemm<kEpiOutB>(kind, blocks, g, st);
   } else {
-    hipLaunchKernelGGL(gemm_kernel<kEpiOut>, dim3(blocks), dim3(256), 0, st, g);
+    launch_gemm<kEpiOut>(kind, blocks, g, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -51,6 +51,8 @@ struct CallOpts {
   // the prep stage ORs its range bits into the workspace's status word
   // instead of replacing it (the blocks of a schedule after the first)
   bool keep_status = false;
+  // bf16 attention operands (q, k, v, P, O and the Wo copy) instead of fp16
+  bool bf16_ops = false;
   // merged mode: frames per block, window rows / columns, merges per block
   // (frames == 0: only sizing the workspace, for the largest merged set)
   int httm_frames = 0, httm_wh = 0, httm_ww = 0, httm_r = 0;
@@ -110,6 +112,7 @@ struct Plan {
   // of workgroups runs as key ranges that a merge kernel combines.
   int split_cap;
   bool keep_status;    // see CallOpts
+  bool bf16_ops;       // see CallOpts
   // merged mode (HTTM): blocks of hf frames x hwh x hww cells, hr merges per
   // block; the merged set has M tokens per head (L = Lk = M, kv_rows rows per
   // head in the merged buffers); merged values carry an extra 2^-hshift

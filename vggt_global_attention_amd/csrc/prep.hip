@@ -185,6 +185,7 @@ struct AffineArgs {
   const float* kb;
   int keep;
   int desc;  // descriptor mode: the value bounds are the cache's (checked when they are loaded)
+  int bf16;  // the Wo copy in bf16 (bf16 attention operands), else fp16
 };
 
 // Largest per-feature bound 8 |gamma| + |beta| over an [H][64] affine (a
@@ -205,7 +206,7 @@ __device__ __forceinline__ float affine_bound(const float* g, const float* b, in
 // bounds kernel.
 __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t n8,
                                                          const float* part, int nx, Scalars* sc,
-                                                         int H, f16* out, AffineArgs af) {
+                                                         int H, void* out, AffineArgs af) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const float woabs = block_max(tid < kBoundsO ? part[kBoundsX + kBoundsV + tid] : 0.f, red);
@@ -247,10 +248,18 @@ __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
     bf16x8 v = reinterpret_cast<const bf16x8*>(wo)[i];
-    f16x8 o;
+    if (af.bf16) {
+      // exact: a power-of-two scale inside bf16's exponent range
+      bf16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (f16)ldexpf((float)v[e], s);
-    reinterpret_cast<f16x8*>(out)[i] = o;
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)ldexpf((float)v[e], s);
+      reinterpret_cast<bf16x8*>(out)[i] = o;
+    } else {
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (f16)ldexpf((float)v[e], s);
+      reinterpret_cast<f16x8*>(out)[i] = o;
+    }
   }
 }
 
@@ -337,7 +346,7 @@ hipError_t launch_prep(const Plan& p, const Ptrs& a, hipStream_t st) {
   hipLaunchKernelGGL(bounds_kernel, dim3(grid), dim3(256), 0, st, b);
   const int64_t n8 = (int64_t)p.d * p.d / 8;
   const AffineArgs af{a.qg, a.qb, desc ? nullptr : a.kg, desc ? nullptr : a.kb,
-                      p.keep_status ? 1 : 0, desc ? 1 : 0};
+                      p.keep_status ? 1 : 0, desc ? 1 : 0, p.bf16_ops ? 1 : 0};
   hipLaunchKernelGGL(wo_convert_kernel, dim3(grid_for(n8, 256, 2048)), dim3(256), 0, st, a.Wo,
                      n8, (const float*)b.part, grid, sc, p.H, ws_wo(p, a), af);
   if (desc) return launch_desc_load(p, a, st);
