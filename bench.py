@@ -487,7 +487,7 @@ def cpu_baseline(w, inp, n_rows, outputs=None):
             "host": host_info(),
             "sample": f"{w.name} global layer: k/v for all {n} tokens + {len(rows)} sampled query "
                       f"rows (q, attention over all keys, Wo); {flop / 1e12:.3f} TFLOP in {dt:.1f} s; "
-                      f"full layer extrapolates to {full_s / 60:.0f} min",
+                      f"full layer extrapolates to {full_s:.0f} s",
             "ms_per_step_extrapolated": full_s * 1e3,
             "sample_errors": errors}
 
