@@ -16,6 +16,12 @@ LIB = os.path.join(PKG, "libvggtattn.so")
 # variables that force tile, split and GEMM choices; see csrc/plan.h): for
 # sweeps and for the tests that force a choice.  Never the product library.
 TUNE_LIB = os.path.join(PKG, "libvggtattn_tune.so")
+# Host code (argument checks, planning, the schedule driver) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer, device code unchanged: for
+# the CPU-side ABI tests only (tests/test_host_sanitizers.py).
+SAN_LIB = os.path.join(PKG, "libvggtattn_san.so")
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+             "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "attention.hip", "subsample.hip",
            "desc.hip", "schedule.cpp", "static_scratch.hip", "merge.hip"]
 
@@ -37,6 +43,12 @@ def build(verbose: bool = False, extra_flags=(), tuning: bool = True) -> str:
     if tuning:
         _link(TUNE_LIB, verbose, (*extra_flags, "-DVGGT_ATTN_TUNING"))
     return _link(LIB, verbose, extra_flags)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The host-sanitizer build (SAN_LIB); load it only in a process that
+    preloads the compiler's ASan runtime."""
+    return _link(SAN_LIB, verbose, SAN_FLAGS)
 
 
 def _link(out: str, verbose: bool, extra_flags) -> str:
