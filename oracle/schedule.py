@@ -90,7 +90,7 @@ def inter_block(x: np.ndarray, p: OracleParams, mode: str, sub, threads=None) ->
 
 
 def run_schedule(X: np.ndarray, blocks: list, layer_scales: list, spec: Spec, threads=None,
-                 trace: bool = False):
+                 trace: bool = False, perturb=None):
     """The attention-only forward over `spec.n_layers` layers.
 
     X: [S, T, d] (exact bf16 values); blocks[2l] / blocks[2l+1]: OracleParams
@@ -98,16 +98,20 @@ def run_schedule(X: np.ndarray, blocks: list, layer_scales: list, spec: Spec, th
     Returns (state, caches) -- caches [n_cached, S, T, 2d] in increasing layer
     order -- and, with trace=True, also the list of (a_l, x_l) states of every
     layer (a_l after the frame block, x_l after the inter-frame block).
+    perturb(y, block_index) -> y, when given, replaces each block's exact
+    output before its bf16 rounding (a model of a computation with per-block
+    errors, for deriving how far such errors carry through the layers).
     """
+    keep = (lambda y, b: y) if perturb is None else perturb
     x = np.asarray(X, dtype=np.float64)
     T = x.shape[1]
     special = (np.arange(T) < N_SPECIAL)[None, :, None]
     caches, states = [], []
     for l in range(spec.n_layers):
-        y = round_bf16(frame_attention(x, blocks[2 * l], threads))
+        y = round_bf16(keep(frame_attention(x, blocks[2 * l], threads), 2 * l))
         a = round_bf16(x + layer_scales[2 * l] * y)
         mode = spec.inter_mode(l)
-        y = round_bf16(inter_block(a, blocks[2 * l + 1], mode, spec.sub, threads))
+        y = round_bf16(keep(inter_block(a, blocks[2 * l + 1], mode, spec.sub, threads), 2 * l + 1))
         upd = round_bf16(a + layer_scales[2 * l + 1] * y)
         x = np.where(special, upd, a) if mode == "register" else upd
         if l in spec.cached_layers:

@@ -16,10 +16,11 @@ Bars:
   scaled by the rounding noise.
 * End to end, the final state against the oracle's own composition: the
   per-block differences above do not simply add up -- a one-unit rounding
-  flip in a bf16 state feeds every later block, and the pages bound nothing
-  about how 48 random blocks amplify it.  This check is a sanity bound
-  (relL1 <= 5e-2, an order of magnitude above what was measured); the parity
-  bar of the schedule is the per-block check.
+  flip in a bf16 state feeds every later block.  The bound is derived with
+  the oracle: its composition with every block output perturbed at the
+  block bar (elementwise relative noise, relL1 ~2e-3 per block) shows how
+  far such errors carry through the layers (carried_error_bound); the GPU's
+  final state must stay within 1.25x that relL1 and 2x that max/max.
 """
 
 from __future__ import annotations
@@ -139,7 +140,24 @@ def split_caches(caches, d):
     return [(c[k][..., :d], c[k][..., d:]) for k in range(c.shape[0])]
 
 
-SANITY_RELL1 = 5e-2
+def carried_error_bound(X, params, scales, spec, seeds=3, a=4e-3):
+    """How far per-block errors at the block bar carry through the layers: the
+    oracle's composition with every block output multiplied by 1 + u, u
+    uniform in [-a, a] elementwise (a = 4e-3 gives each block relL1 ~2e-3,
+    the block bar), against the unperturbed composition; the largest relL1
+    and max/max over a few seeds.  Dominated by one-unit flips of the bf16
+    state that every later block then sees."""
+    ref, _ = osched.run_schedule(X, params, scales, spec)
+    worst = {"relL1": 0.0, "max_over_max": 0.0}
+    for seed in range(seeds):
+        rng = np.random.default_rng(seed)
+        st, _ = osched.run_schedule(
+            X, params, scales, spec,
+            perturb=lambda y, b: y * (1.0 + rng.uniform(-a, a, size=y.shape)))
+        m = metrics(st, ref)
+        for k in worst:
+            worst[k] = max(worst[k], m[k])
+    return ref, worst
 
 
 SCHED_TINY = configs.custom("sched_tiny", S=3, grid_h=4, grid_w=5, d=128, H=2, cid=61)
@@ -156,12 +174,15 @@ def test_schedule_24_layers_tiny():
     np.testing.assert_array_equal(states[-1][1], np64(state))
     ospec = osched.Spec(cached_layers=tuple(range(24)))
     local_block_checks(f64(X), states, params, scales, ospec, "24 layers")
-    # end to end against the oracle's own composition
-    ref, _ = osched.run_schedule(f64(X), params, scales, osched.Spec())
+    # end to end against the oracle's own composition, within what errors at
+    # the block bar in every block produce through the 48 blocks (1.25x the
+    # worst relL1 of the modelled compositions, 2x their max/max)
+    ref, carried = carried_error_bound(f64(X), params, scales, osched.Spec())
     m = metrics(np64(state), ref)
-    log(f"  end to end: {m}")
+    log(f"  end to end: {m}; block-bar errors carried through the layers: {carried}")
     assert m["nonfinite"] == 0
-    assert m["relL1"] <= SANITY_RELL1, m
+    assert m["relL1"] <= 1.25 * carried["relL1"], (m, carried)
+    assert m["max_over_max"] <= 2.0 * carried["max_over_max"], (m, carried)
     # the page's schedule with its four kept layers, in place: bitwise the same
     Xd = X.cuda()
     sch = S.Schedule(Xd, w.H, w.grid_h, w.grid_w, dev)

@@ -248,3 +248,18 @@ def test_unmutated_runner_passes_every_pin():
     _register_pin(r)
     _cache_pin(r)
     _sequential_pin(r)
+
+
+def test_perturb_hook_identity_is_the_composition():
+    """The perturbation hook (for deriving how far per-block errors carry)
+    changes nothing when it returns its input, and does change the result
+    when it scales a block."""
+    blocks, scales = make_blocks(6, seed=9)
+    X = make_x(2, seed=10)
+    spec = sg.Spec(n_layers=3, register_layers=(1,), cached_layers=(0, 2))
+    ref, c0 = sg.run_schedule(X, blocks, scales, spec, threads=1)
+    same, c1 = sg.run_schedule(X, blocks, scales, spec, threads=1, perturb=lambda y, b: y)
+    assert np.array_equal(ref, same) and np.array_equal(c0, c1)
+    other, _ = sg.run_schedule(X, blocks, scales, spec, threads=1,
+                               perturb=lambda y, b: y * (2.0 if b == 4 else 1.0))
+    assert not np.array_equal(ref, other)
