@@ -104,6 +104,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
       mode != VGGT_ATTN_MODE_REGISTER)
     return VGGT_ATTN_EINVAL;
   p->bf16_ops = o.bf16_ops;
+  p->patch_copy = !o.no_patch_copy;
   const int64_t R = (int64_t)s->S * kSpecial;
   int64_t cover;  // workspace rows the attention kernel may touch
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {

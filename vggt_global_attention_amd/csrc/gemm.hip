@@ -1080,7 +1080,8 @@ hipError_t launch_out(const Plan& p, const Ptrs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.mode == VGGT_ATTN_MODE_REGISTER && a.Y != a.X) return launch_patch_copy(p, a, st);
+  if (p.mode == VGGT_ATTN_MODE_REGISTER && a.Y != a.X && p.patch_copy)
+    return launch_patch_copy(p, a, st);
   return hipSuccess;
 }
 

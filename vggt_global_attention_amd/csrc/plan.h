@@ -53,6 +53,9 @@ struct CallOpts {
   bool keep_status = false;
   // bf16 attention operands (q, k, v, P, O and the Wo copy) instead of fp16
   bool bf16_ops = false;
+  // register mode, Y != X: leave Y's patch rows unwritten (the layer schedule
+  // reads only the special rows of a register block's output)
+  bool no_patch_copy = false;
   // merged mode: frames per block, window rows / columns, merges per block
   // (frames == 0: only sizing the workspace, for the largest merged set)
   int httm_frames = 0, httm_wh = 0, httm_ww = 0, httm_r = 0;
@@ -113,6 +116,7 @@ struct Plan {
   int split_cap;
   bool keep_status;    // see CallOpts
   bool bf16_ops;       // see CallOpts
+  bool patch_copy;     // register mode, Y != X: copy the patch rows (else see CallOpts)
   // merged mode (HTTM): blocks of hf frames x hwh x hww cells, hr merges per
   // block; the merged set has M tokens per head (L = Lk = M, kv_rows rows per
   // head in the merged buffers); merged values carry an extra 2^-hshift

@@ -264,25 +264,28 @@ __global__ __launch_bounds__(256) void wo_convert_kernel(const bf16* wo, int64_t
 }
 
 // Register mode, Y != X: copy the patch rows (tokens 17..T-1) of every frame.
-// Each thread moves four 16-byte chunks per step (loads first, then stores).
+// Blocks (x, y): x walks the frame's patch rows in 16-byte chunks, y the
+// frames; each thread moves four chunks per step (loads first, then stores),
+// consecutive lanes on consecutive chunks, and no index needs a division.
+// Non-temporal loads and stores: the gigabytes streamed through once would
+// only evict useful lines (s500 copy alone: 6.1 TB/s, against 5.6 with plain
+// accesses and 5.1 for the runtime's device-to-device copy).
 __global__ __launch_bounds__(256) void patch_copy_kernel(const bf16* X, bf16* Y, int S,
-                                                         int64_t frame_elems, int64_t skip_elems) {
-  const int64_t per = (frame_elems - skip_elems) / 8;  // 16-byte chunks per frame
-  const int64_t total = per * S;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < total; i0 += 4 * stride) {
-    u32x4 v[4];
-    int64_t off[4];
+                                                         int64_t frame_elems, int64_t skip_elems,
+                                                         int64_t per) {
+  const int64_t step = (int64_t)gridDim.x * 256 * 4;
+  for (int s = blockIdx.y; s < S; s += gridDim.y) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (int64_t)s * frame_elems + skip_elems);
+    u32x4* dst = reinterpret_cast<u32x4*>(Y + (int64_t)s * frame_elems + skip_elems);
+    for (int64_t c0 = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; c0 < per; c0 += step) {
+      u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * stride;
-      const int64_t s = i / per, c = i - s * per;
-      off[u] = i < total ? s * frame_elems + skip_elems + c * 8 : -1;
-      if (off[u] >= 0) v[u] = *reinterpret_cast<const u32x4*>(X + off[u]);
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u * 256 < per) v[u] = __builtin_nontemporal_load(src + c0 + u * 256);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u * 256 < per) __builtin_nontemporal_store(v[u], dst + c0 + u * 256);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (off[u] >= 0) *reinterpret_cast<u32x4*>(Y + off[u]) = v[u];
   }
 }
 
@@ -290,28 +293,33 @@ __global__ __launch_bounds__(256) void patch_copy_kernel(const bf16* X, bf16* Y,
 // index modulo `period` is below `active`, Z = X + gamma * Y per channel (fp32
 // fma, one rounding to bf16); other rows Z = X.  Optionally also writes Z into
 // a strided cache (row r at C + r * c_stride).  Eight channels per step.
+// `only_active`: the loop visits the active rows alone (Z == X and no cache:
+// the other rows would be copied onto themselves).
 __global__ __launch_bounds__(256) void residual_kernel(const bf16* X, const bf16* Y, bf16* Z,
                                                        int64_t rows, int d, const float* gamma,
                                                        int period, int active, bf16* C,
-                                                       int64_t c_stride) {
+                                                       int64_t c_stride, int only_active) {
   const int per_row = d / 8;
-  const int64_t total = rows * per_row;
+  const int64_t vrows = only_active ? rows / period * active : rows;  // visited rows
+  const int64_t total = vrows * per_row;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / per_row;
-    const int c = (int)(i - r * per_row) * 8;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(X + r * d + c);
+    const int64_t v = i / per_row;
+    const int c = (int)(i - v * per_row) * 8;
+    const int64_t r = only_active ? v / active * period + v % active : v;
+    // streamed once: non-temporal accesses (as the patch copy)
+    const bf16x8 x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(X + r * d + c));
     bf16x8 z = x;
     if ((int)(r % period) < active) {
-      const bf16x8 y = *reinterpret_cast<const bf16x8*>(Y + r * d + c);
+      const bf16x8 y = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(Y + r * d + c));
       const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + c);
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + c + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         z[e] = (bf16)fmaf(e < 4 ? g0[e & 3] : g1[e & 3], (float)y[e], (float)x[e]);
     }
-    *reinterpret_cast<bf16x8*>(Z + r * d + c) = z;
-    if (C) *reinterpret_cast<bf16x8*>(C + r * c_stride + c) = z;
+    __builtin_nontemporal_store(z, reinterpret_cast<bf16x8*>(Z + r * d + c));
+    if (C) __builtin_nontemporal_store(z, reinterpret_cast<bf16x8*>(C + r * c_stride + c));
   }
 }
 
@@ -363,18 +371,25 @@ hipError_t launch_rownorm_max(const bf16* X, int64_t rows, int d, RowMap map, fl
 hipError_t launch_patch_copy(const Plan& p, const Ptrs& a, hipStream_t st) {
   if (p.T <= kSpecial) return hipSuccess;
   const int64_t frame = (int64_t)p.T * p.d, skip = (int64_t)kSpecial * p.d;
-  const int64_t work = (frame - skip) / 8 * p.S;
-  hipLaunchKernelGGL(patch_copy_kernel, dim3(grid_for(work, 1024, 4096)), dim3(256), 0, st, a.X,
-                     a.Y, p.S, frame, skip);
+  const int64_t per = (frame - skip) / 8;  // 16-byte chunks per frame
+  // about 4 chunks per thread per frame (at most 2^20 blocks); frames spread
+  // over y (at most 65,535)
+  int64_t bx = (per + 256 * 4 - 1) / (256 * 4);
+  if (bx > (1 << 20)) bx = 1 << 20;
+  const int by = p.S < 65535 ? p.S : 65535;
+  hipLaunchKernelGGL(patch_copy_kernel, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, st, a.X,
+                     a.Y, p.S, frame, skip, per);
   return hipGetLastError();
 }
 
 hipError_t launch_residual(const bf16* X, const bf16* Y, bf16* Z, int64_t rows, int d,
                            const float* gamma, int period, int active, bf16* C, int64_t c_stride,
                            hipStream_t st) {
-  const int64_t work = rows * (d / 8);
+  // in place without a cache, rows outside the active ones stay as they are
+  const int only_active = (X == Z && C == nullptr && active < period && rows % period == 0) ? 1 : 0;
+  const int64_t work = (only_active ? rows / period * active : rows) * (d / 8);
   hipLaunchKernelGGL(residual_kernel, dim3(grid_for(work, 256, 8192)), dim3(256), 0, st, X, Y, Z,
-                     rows, d, gamma, period, active, C, c_stride);
+                     rows, d, gamma, period, active, C, c_stride, only_active);
   return hipGetLastError();
 }
 

@@ -138,6 +138,9 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
         o.sub_w = sc.sub_w;
       }
       o.keep_status = l > 0 || half > 0;
+      // the residual update below reads only the special rows of a register
+      // block's output: its patch rows are not copied
+      o.no_patch_copy = true;
       const void* in = (l == 0 && half == 0) ? X : state;
       st = run(mode, o, VGGT_ATTN_STAGE_PREP, VGGT_ATTN_STAGE_OUT, shape, in, w.Wqkv, w.Wo,
                w.q_gamma, w.q_beta, w.k_gamma, w.k_beta, Y, bws, blk, stream);
