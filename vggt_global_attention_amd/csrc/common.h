@@ -77,6 +77,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// v + (v of lane l ^ 32), the same bits on both lanes (fp32 addition is
+// commutative), through gfx950's v_permlane32_swap (a VALU op, no LDS).
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // c + a.x b.x + a.y b.y in fp32 (v_dot2 of two 16-bit pairs)
 __device__ __forceinline__ float dot2_acc(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);

@@ -124,7 +124,7 @@ __device__ __forceinline__ void ln_rope_16(const f32x16& a0, const f32x16& a1,
   float s1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s1 += a0[r] + a1[r];
-  const float mean = (s1 + __shfl_xor(s1, 32)) * (1.f / kDh);
+  const float mean = add_xor32(s1) * (1.f / kDh);
   float s2 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -133,7 +133,7 @@ __device__ __forceinline__ void ln_rope_16(const f32x16& a0, const f32x16& a1,
     s2 = fmaf(y[0][r], y[0][r], s2);
     s2 = fmaf(y[1][r], y[1][r], s2);
   }
-  const float var = (s2 + __shfl_xor(s2, 32)) * (1.f / kDh);
+  const float var = add_xor32(s2) * (1.f / kDh);
   const float rstd = __builtin_amdgcn_rsqf(var + eps);
 #pragma unroll
   for (int fb = 0; fb < 2; ++fb)
@@ -165,7 +165,7 @@ __device__ __forceinline__ void ln_rope_16(const f32x16& a0, const f32x16& a1,
         n2 = dot2_acc(hi, hi, n2);
       }
     }
-  if (NORM) n2 += __shfl_xor(n2, 32);
+  if (NORM) n2 = add_xor32(n2);
 }
 
 // gamma / beta of the wave's head in the lane's feature order, times the
