@@ -71,19 +71,23 @@ def test_schedule_graph_replay():
     replay_and_check(g, (state, caches), ref, "schedule")
 
 
-@pytest.mark.parametrize("mode", ["global", "frame", "register", "subsampled"])
-def test_block_graph_replay(mode):
+@pytest.mark.parametrize("mode,ops", [("global", "fp16"), ("frame", "fp16"), ("register", "fp16"),
+                                     ("subsampled", "fp16"), ("merged", "fp16"),
+                                     ("global", "bf16")])
+def test_block_graph_replay(mode, ops):
     """One block call of 24 frames. The global block runs a split tail (key
-    ranges and the merge kernel), captured like any other launch."""
+    ranges and the merge kernel), captured like any other launch; the merged
+    block's merge and unmerge kernels and the bf16-operand variant too."""
     w = configs.WORKLOADS["s24"]
     d = to_dev(synth.make_inputs(w))
     sub = (3, 3) if mode == "subsampled" else (1, 1)
-    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub)
+    blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub, merge=(4, 2, 3, 12),
+                    operands=ops)
     args = [d[k] for k in ("X", "Wqkv", "Wo", "q_gamma", "q_beta", "k_gamma", "k_beta")]
     Y = torch.empty_like(d["X"])
     blk(*args, Y=Y)
     torch.cuda.synchronize()
     ref = Y.clone()
-    log(f"[case] graph of one {mode} block, s24")
+    log(f"[case] graph of one {mode} block ({ops} operands), s24")
     g = capture(lambda: blk(*args, Y=Y))
-    replay_and_check(g, (Y,), (ref,), mode)
+    replay_and_check(g, (Y,), (ref,), f"{mode}/{ops}")

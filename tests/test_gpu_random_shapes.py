@@ -71,3 +71,41 @@ def test_random_shape_all_modes(name, i, S, gh, gw, d, off, sub):
     rows = np.arange(begin, begin + count)
     ref = oracle.global_attention_rows(X, p, rows)
     assert_parity(np64(y), ref, f"{name}/rows")
+
+
+@pytest.mark.parametrize("name,i,S,gh,gw,d,off,sub", SHAPES, ids=[s[0] for s in SHAPES])
+def test_random_shape_bf16_operands_and_merged(name, i, S, gh, gw, d, off, sub):
+    """The same shapes through the bf16-operand variant (its own bar) and
+    the HTTM merged mode with random blocks and merge counts (per (token,
+    head) against the oracle with Wo = I, near-tie pairs excluded)."""
+    from oracle import httm as ohttm
+    from helpers import BF16OPS_MAX, BF16OPS_MEAN, BF16OPS_RELL1, metrics
+    import torch
+    w = configs.custom(name, S, gh, gw, d, d // 64, cid=400 + i)
+    inp = synth.make_inputs(w)
+    p = oracle_params(w, inp, pos_offset=off)
+    d_in = to_dev(inp)
+    X = f64(inp["X"])
+    for mode, ref_fn in (("frame", oracle.frame_attention), ("global", oracle.global_attention),
+                         ("register", oracle.register_attention)):
+        log(f"[case] {name} {mode} bf16 operands")
+        m = metrics(np64(run(mode, w, d_in, pos_offset=off, operands="bf16")), ref_fn(X, p))
+        assert m["nonfinite"] == 0 and m["relL1"] <= BF16OPS_RELL1, (name, mode, m)
+        assert m["max_over_max"] <= BF16OPS_MAX and m["mean_over_max"] <= BF16OPS_MEAN, (name, m)
+    rng = np.random.default_rng(7000 + i)
+    F = int(rng.integers(2, 5))
+    wh, ww = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    r = int(rng.integers(1, (F - 1) * wh * ww + 3))  # up to beyond a block's sources
+    log(f"[case] {name} merged F={F} win={wh}x{ww} r={r}")
+    inp_i = dict(inp)
+    inp_i["Wo"] = torch.eye(d, dtype=inp["Wo"].dtype)
+    d_i = to_dev(inp_i)
+    p_i = oracle_params(w, inp_i, pos_offset=off)
+    hp = ohttm.HttmParams(F, wh, ww, r)
+    y = np64(run("merged", w, d_i, pos_offset=off, merge=(F, wh, ww, r))).reshape(w.N, w.H, -1)
+    ref = ohttm.httm_attention(X, p_i, hp).reshape(w.N, w.H, -1)
+    frag = ohttm.fragile(X, p_i, hp)
+    assert np.isfinite(y).all()
+    log(f"  {frag.sum()} of {frag.size} (token, head) pairs fragile")
+    if (~frag).any():
+        assert_parity(y[~frag], ref[~frag], f"{name}/merged")
