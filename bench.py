@@ -319,7 +319,8 @@ def schedule_forward(w, spec, steps, warmup, ls=1e-5, graph=False):
     peak = torch.cuda.max_memory_allocated() - base
     flop = 0.0
     for l in range(spec.n_layers):
-        flop += w.flop("frame") + w.flop(spec.inter_mode(l), spec.sub)
+        mode = spec.inter_mode(l)
+        flop += w.flop("frame") + w.flop(mode, spec.merge if mode == "merged" else spec.sub)
     out = {"S": w.S, "N": w.N, "ms_per_forward": ms, "tflops": flop / ms / 1e9,
            "peak_bytes": peak, "peak_gb": peak / 1e9, "weights_bytes": wbytes,
            "state_bytes": X.numel() * 2, "caches_bytes": caches.numel() * 2,
@@ -357,7 +358,10 @@ def schedule_sweep(frames, steps, warmup, graph=False):
     variants = {"vggt": S.ScheduleSpec(),
                 # AVGGT: the first third of the layers as frame attention, the
                 # remaining global layers subsampled with 3 x 3 windows
-                "avggt_early8_sub3x3": S.ScheduleSpec(early_frame=8, sub=(3, 3))}
+                "avggt_early8_sub3x3": S.ScheduleSpec(early_frame=8, sub=(3, 3)),
+                # HTTM: every global layer with merging in blocks of 4 frames x
+                # 2 x 3 cells, 12 of a block's 18 sources merged
+                "httm_F4w2x3r12": S.ScheduleSpec(merge=(4, 2, 3, 12))}
     rows = []
     for n in frames:
         w = configs.custom(f"s{n}", S=n, grid_h=26, grid_w=39, d=1024, H=16, cid=70)

@@ -370,6 +370,13 @@ typedef struct vggt_attn_schedule {
   uint64_t cached_layers;    /* bit l: layer l's two states are kept */
   int32_t sub_h, sub_w;      /* 1, 1: the remaining inter-frame blocks are global; else they
                                 are subsampled global blocks with these windows */
+  int32_t merge_frames;      /* 0: off; else the remaining inter-frame blocks (not register,
+                                not early frame) are global blocks with HTTM merging,
+                                vggt_attn_global_merged(merge_frames, merge_win_h,
+                                merge_win_w, merge_r) (HTTM article, 10100.com, section
+                                02: merging serves the global attention layers); not
+                                together with subsampling */
+  int32_t merge_win_h, merge_win_w, merge_r;
 } vggt_attn_schedule;
 
 /* Workspace of vggt_attn_schedule_run: the block output buffer plus the
@@ -391,8 +398,9 @@ size_t vggt_attn_schedule_workspace_bytes(const vggt_attn_shape* shape,
    may be X itself, else it must not overlap X).  caches: NULL (nothing kept)
    or bf16 [popcount(cached_layers)][S][T][2d], channels [0, d) the state after
    the frame block, [d, 2d) the state after the inter-frame block.  Masks with
-   bits at or above n_layers, early_frame outside 0..n_layers or windows < 1
-   give VGGT_ATTN_ERANGE; every block and residual call is checked before the
+   bits at or above n_layers, early_frame outside 0..n_layers, windows < 1,
+   merging with subsampling or merge parameters out of range give
+   VGGT_ATTN_ERANGE; every block and residual call is checked before the
    first launch, so on any error nothing is enqueued. */
 int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedule* sched,
                            const vggt_attn_block_weights* blocks, const void* X, void* state,

@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, never by the GPU library; it
 shares no code with the HIP path.  The blocks are those of `vggt_oracle` and
-`avggt_sga`; this module only composes them.
+`avggt_sga` and `httm`; this module only composes them.
 
 Sources and readings:
 
@@ -26,6 +26,10 @@ Sources and readings:
   layers become frame attention (same weights, attention inside each frame);
   step 2: the remaining global layers use subsampled global attention.  How
   many layers count as "early" is not given: it is a parameter.
+* "HTTM" article (10100.com), section 02: token merging is designed for
+  VGGT's global attention layers; read as: with merging on, every global
+  inter-frame block (not register, not early frame) runs with it, with one
+  parameter set for all (`httm`).
 * Storage: the token state and every block output are bf16, the library's
   input/output type.  The oracle computes each block and each residual update
   in float64 from the exact bf16 values and rounds the result once to the
@@ -39,6 +43,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .avggt_sga import sga_attention
+from .httm import HttmParams, httm_attention
 from .vggt_oracle import (N_SPECIAL, OracleParams, frame_attention, global_attention,
                           register_attention)
 
@@ -54,15 +59,22 @@ class Spec:
     cached_layers: tuple = CACHED_LAYERS
     early_frame: int = 0          # AVGGT step 1: layers below this run frame attention
     sub: tuple = field(default=(1, 1))  # AVGGT step 2: windows of the remaining global layers
+    merge: tuple = None           # HTTM: (frames, win_h, win_w, r) of the remaining global layers
 
     def inter_mode(self, l: int) -> str:
         if l in self.register_layers:
             return "register"
         if l < self.early_frame:
             return "frame"
+        if self.merge:
+            return "merged"
         if tuple(self.sub) != (1, 1):
             return "subsampled"
         return "global"
+
+    def params(self, mode: str):
+        """The extra parameters of an inter-frame block in `mode`."""
+        return tuple(self.merge) if mode == "merged" else tuple(self.sub)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -78,6 +90,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def inter_block(x: np.ndarray, p: OracleParams, mode: str, sub, threads=None) -> np.ndarray:
+    """One inter-frame block; `sub` holds the mode's parameters (the windows
+    of subsampled mode, the four merge parameters of merged mode)."""
     if mode == "frame":
         return frame_attention(x, p, threads)
     if mode == "global":
@@ -86,6 +100,8 @@ def inter_block(x: np.ndarray, p: OracleParams, mode: str, sub, threads=None) ->
         return register_attention(x, p, threads)
     if mode == "subsampled":
         return sga_attention(x, p, sub[0], sub[1], threads=threads)
+    if mode == "merged":
+        return httm_attention(x, p, HttmParams(*sub), threads=threads)
     raise ValueError(mode)
 
 
@@ -111,7 +127,8 @@ def run_schedule(X: np.ndarray, blocks: list, layer_scales: list, spec: Spec, th
         y = round_bf16(keep(frame_attention(x, blocks[2 * l], threads), 2 * l))
         a = round_bf16(x + layer_scales[2 * l] * y)
         mode = spec.inter_mode(l)
-        y = round_bf16(keep(inter_block(a, blocks[2 * l + 1], mode, spec.sub, threads), 2 * l + 1))
+        y = round_bf16(keep(inter_block(a, blocks[2 * l + 1], mode, spec.params(mode), threads),
+                            2 * l + 1))
         upd = round_bf16(a + layer_scales[2 * l + 1] * y)
         x = np.where(special, upd, a) if mode == "register" else upd
         if l in spec.cached_layers:

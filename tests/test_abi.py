@@ -291,9 +291,10 @@ def test_residual_errors():
     assert res(C=0x600008, c_stride=512) == B.EALIGN
 
 
-def sched(n=24, reg=(2, 6, 9, 14, 20), cache=(4, 11, 17, 23), early=0, sub=(1, 1)):
+def sched(n=24, reg=(2, 6, 9, 14, 20), cache=(4, 11, 17, 23), early=0, sub=(1, 1),
+          merge=(0, 0, 0, 0)):
     m = lambda ls: sum(1 << l for l in ls)  # noqa: E731
-    return B.vggt_attn_schedule(n, early, m(reg), m(cache), sub[0], sub[1])
+    return B.vggt_attn_schedule(n, early, m(reg), m(cache), sub[0], sub[1], *merge)
 
 
 def test_schedule_workspace_bytes():
@@ -309,6 +310,14 @@ def test_schedule_workspace_bytes():
     assert B.vggt_attn_schedule_workspace_bytes(s, sched(n=65)) == 0
     assert B.vggt_attn_schedule_workspace_bytes(s, sched(n=4, reg=(5,))) == 0
     assert B.vggt_attn_schedule_workspace_bytes(B.make_shape(**dict(TINY, T=80)), sched()) == 0
+    # HTTM merging in the global layers: the merged mode's workspace
+    mg = B.vggt_attn_workspace_bytes(B.MODE_MERGED, s)
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(merge=(2, 2, 2, 4))) == ybytes + max(f, mg)
+    # merging with subsampling, or bad merge parameters: rejected
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(sub=(3, 3), merge=(2, 2, 2, 4))) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(merge=(2, 0, 2, 4))) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(merge=(2, 2, 2, -1))) == 0
+    assert B.vggt_attn_schedule_workspace_bytes(s, sched(merge=(-1, 2, 2, 1))) == 0
 
 
 def fake_blocks(n_blocks, **bad):

@@ -29,6 +29,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import httm as ohttm
 from oracle import schedule as osched
 from oracle.vggt_oracle import OracleParams
 from vggt_global_attention_amd import configs, synth
@@ -110,15 +111,23 @@ def local_block_checks(X, states_gpu, params, scales, spec, label):
         for half, (inp, out, mode) in enumerate(((prev, a_g, "frame"),
                                                  (a_g, x_g, spec.inter_mode(l)))):
             p, gam = params[2 * l + half], scales[2 * l + half]
-            y = osched.round_bf16(osched.inter_block(inp, p, mode, spec.sub))
+            y = osched.round_bf16(osched.inter_block(inp, p, mode, spec.params(mode)))
             ref = osched.round_bf16(inp + gam * y)
             if mode == "register":
                 ref = np.where(special, ref, inp)
                 y = np.where(special, y, 0.0)
+            # merged blocks: tokens whose merge decision in some head is a
+            # near-tie (oracle.httm.fragile) may take the other, equally valid
+            # choice; they are left out of this block's check
+            keep = np.ones(inp.shape[:2], dtype=bool)
+            if mode == "merged":
+                frag = ohttm.fragile(inp, p, ohttm.HttmParams(*spec.merge)).any(axis=1)
+                keep = ~frag.reshape(inp.shape[:2])
             bound = np.abs(gam).max() * 1e-2 * np.abs(y).max() + ulp_bf16(ref)
             err = np.abs(out - ref)
-            assert np.all(err <= bound), (label, l, half, mode, float((err - bound).max()))
-            m = metrics(out - inp, ref - inp)
+            bad = (err > bound) & keep[..., None]
+            assert not bad.any(), (label, l, half, mode, float((err - bound)[bad].max()))
+            m = metrics((out - inp)[keep], (ref - inp)[keep])
             worst = max(worst, m["relL1"])
             # the branch itself: the block bar plus the bf16 rounding of both states
             noise = float(np.mean(ulp_bf16(ref) / 2) / max(np.mean(np.abs(ref - inp)), 1e-30))
@@ -191,6 +200,32 @@ def test_schedule_24_layers_tiny():
     assert torch.equal(st2, state)
     for k, l in enumerate(osched.CACHED_LAYERS):
         assert torch.equal(c2[k], caches[l]), l
+
+
+def test_schedule_with_merging():
+    """Eight layers with HTTM merging in the global inter-frame blocks (runs
+    of 2 frames, 2 x 2 windows, 2 merges per block) and two register
+    layers: every block against the oracle block on the GPU's input state
+    (near-tie tokens of merged blocks left out), and the final state within
+    what block-bar errors carry through the layers."""
+    w = configs.custom("sched_httm", S=4, grid_h=4, grid_w=5, d=128, H=2, cid=63)
+    merge = (2, 2, 2, 2)
+    spec = S.ScheduleSpec(n_layers=8, register_layers=(2, 6), cached_layers=tuple(range(8)),
+                          merge=merge)
+    log(f"[case] schedule with HTTM merging {merge}, 8 layers")
+    dev, params, scales = block_weights(w, 16, 0.25)
+    X = synth.make_inputs(w)["X"]
+    state, caches = run_gpu(w, dev, spec, X)
+    ospec = osched.Spec(n_layers=8, register_layers=(2, 6), cached_layers=tuple(range(8)),
+                        merge=merge)
+    assert [spec.inter_mode(l) for l in range(8)] == [ospec.inter_mode(l) for l in range(8)]
+    assert spec.inter_mode(0) == "merged"
+    local_block_checks(f64(X), split_caches(caches, w.d), params, scales, ospec, "httm")
+    ref, carried = carried_error_bound(f64(X), params, scales, ospec)
+    m = metrics(np64(state), ref)
+    log(f"  end to end: {m}; block-bar errors carried through the layers: {carried}")
+    assert m["nonfinite"] == 0
+    assert m["relL1"] <= 1.25 * carried["relL1"], (m, carried)
 
 
 def test_schedule_avggt_conversions():

@@ -263,3 +263,22 @@ def test_perturb_hook_identity_is_the_composition():
     other, _ = sg.run_schedule(X, blocks, scales, spec, threads=1,
                                perturb=lambda y, b: y * (2.0 if b == 4 else 1.0))
     assert not np.array_equal(ref, other)
+
+
+def test_merging_with_r0_is_the_plain_schedule():
+    """HTTM merging in the global inter-frame blocks with r = 0 merges nothing:
+    the composition is exactly the plain one; with r > 0 it differs."""
+    blocks, scales = make_blocks(8, seed=11, gh=2, gw=3)
+    X = make_x(4, seed=12)
+    spec = sg.Spec(n_layers=4, register_layers=(1,), cached_layers=(3,))
+    ref, c0 = sg.run_schedule(X, blocks, scales, spec, threads=1)
+    same, c1 = sg.run_schedule(X, blocks, scales,
+                               sg.Spec(n_layers=4, register_layers=(1,), cached_layers=(3,),
+                                       merge=(2, 1, 2, 0)), threads=1)
+    assert np.array_equal(ref, same) and np.array_equal(c0, c1)
+    merged, _ = sg.run_schedule(X, blocks, scales,
+                                sg.Spec(n_layers=4, register_layers=(1,), cached_layers=(3,),
+                                        merge=(2, 1, 2, 2)), threads=1)
+    assert not np.array_equal(ref, merged)
+    assert [sg.Spec(n_layers=4, register_layers=(1,), merge=(2, 1, 2, 2)).inter_mode(l)
+            for l in range(4)] == ["merged", "register", "merged", "merged"]

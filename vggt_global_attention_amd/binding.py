@@ -52,7 +52,9 @@ class vggt_attn_block_weights(ctypes.Structure):
 class vggt_attn_schedule(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("early_frame", ctypes.c_int32),
                 ("register_layers", ctypes.c_uint64), ("cached_layers", ctypes.c_uint64),
-                ("sub_h", ctypes.c_int32), ("sub_w", ctypes.c_int32)]
+                ("sub_h", ctypes.c_int32), ("sub_w", ctypes.c_int32),
+                ("merge_frames", ctypes.c_int32), ("merge_win_h", ctypes.c_int32),
+                ("merge_win_w", ctypes.c_int32), ("merge_r", ctypes.c_int32)]
 
 
 class VggtAttnError(RuntimeError):

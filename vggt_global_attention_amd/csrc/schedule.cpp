@@ -3,7 +3,8 @@
 // a per-channel LayerScale ("VGGT-Omega Aggregator explainer", section 三); the
 // inter-frame block is in register mode at the chosen layers and global
 // elsewhere, optionally frame attention in early layers and subsampled global
-// attention in the rest (AVGGT summary, technical summary 2B); the token
+// attention in the rest (AVGGT summary, technical summary 2B) or global
+// attention with HTTM token merging (HTTM article, section 02); the token
 // states after both blocks of the cached layers are kept side by side
 // (section 四).
 //
@@ -27,6 +28,7 @@ bool bit(uint64_t m, int l) { return (m >> l) & 1u; }
 int inter_mode(const vggt_attn_schedule& sc, int l) {
   if (bit(sc.register_layers, l)) return VGGT_ATTN_MODE_REGISTER;
   if (l < sc.early_frame) return VGGT_ATTN_MODE_FRAME;
+  if (sc.merge_frames > 0) return VGGT_ATTN_MODE_MERGED;
   if (sc.sub_h > 1 || sc.sub_w > 1) return VGGT_ATTN_MODE_SUBSAMPLED;
   return VGGT_ATTN_MODE_GLOBAL;
 }
@@ -38,7 +40,27 @@ int check_schedule(const vggt_attn_schedule* sc) {
   if ((sc->register_layers & ~valid) || (sc->cached_layers & ~valid)) return VGGT_ATTN_ERANGE;
   if (sc->early_frame < 0 || sc->early_frame > sc->n_layers) return VGGT_ATTN_ERANGE;
   if (sc->sub_h < 1 || sc->sub_w < 1) return VGGT_ATTN_ERANGE;
+  if (sc->merge_frames < 0) return VGGT_ATTN_ERANGE;
+  if (sc->merge_frames > 0 && (sc->sub_h > 1 || sc->sub_w > 1 || sc->merge_win_h < 1 ||
+                               sc->merge_win_w < 1 || sc->merge_r < 0))
+    return VGGT_ATTN_ERANGE;
   return VGGT_ATTN_OK;
+}
+
+// Call options of a block of the schedule in `mode`.
+CallOpts block_opts(const vggt_attn_schedule& sc, int mode) {
+  CallOpts o;
+  if (mode == VGGT_ATTN_MODE_SUBSAMPLED) {
+    o.sub_h = sc.sub_h;
+    o.sub_w = sc.sub_w;
+  }
+  if (mode == VGGT_ATTN_MODE_MERGED) {
+    o.httm_frames = sc.merge_frames;
+    o.httm_wh = sc.merge_win_h;
+    o.httm_ww = sc.merge_win_w;
+    o.httm_r = sc.merge_r;
+  }
+  return o;
 }
 
 // Block workspace: the largest need over the modes the schedule uses.
@@ -102,11 +124,7 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
   for (int b = 0; b < 2 * sc.n_layers; ++b) {
     const vggt_attn_block_weights& w = blocks[b];
     const int mode = (b & 1) ? inter_mode(sc, b >> 1) : VGGT_ATTN_MODE_FRAME;
-    CallOpts o;
-    if (mode == VGGT_ATTN_MODE_SUBSAMPLED) {
-      o.sub_h = sc.sub_h;
-      o.sub_w = sc.sub_w;
-    }
+    const CallOpts o = block_opts(sc, mode);
     Plan plan;
     const void* in = (b == 0) ? X : state;
     st = check_call(mode, shape, o, in, w.Wqkv, w.Wo, w.q_gamma, w.q_beta, w.k_gamma, w.k_beta,
@@ -132,11 +150,7 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
     for (int half = 0; half < 2; ++half) {
       const vggt_attn_block_weights& w = blocks[2 * l + half];
       const int mode = half ? inter_mode(sc, l) : VGGT_ATTN_MODE_FRAME;
-      CallOpts o;
-      if (mode == VGGT_ATTN_MODE_SUBSAMPLED) {
-        o.sub_h = sc.sub_h;
-        o.sub_w = sc.sub_w;
-      }
+      CallOpts o = block_opts(sc, mode);
       o.keep_status = l > 0 || half > 0;
       // the residual update below reads only the special rows of a register
       // block's output: its patch rows are not copied

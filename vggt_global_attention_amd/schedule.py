@@ -38,12 +38,16 @@ class ScheduleSpec:
     cached_layers: tuple = CACHED_LAYERS
     early_frame: int = 0
     sub: tuple = field(default=(1, 1))
+    # HTTM merging in the global inter-frame blocks: (frames per block, window
+    # rows, window columns, merges per block), or None
+    merge: tuple = None
 
     def c_struct(self) -> B.vggt_attn_schedule:
+        m = tuple(int(x) for x in self.merge) if self.merge else (0, 0, 0, 0)
         return B.vggt_attn_schedule(self.n_layers, self.early_frame,
                                     layer_mask(self.register_layers),
                                     layer_mask(self.cached_layers), int(self.sub[0]),
-                                    int(self.sub[1]))
+                                    int(self.sub[1]), *m)
 
     def inter_mode(self, l: int) -> str:
         """Mode of layer l's inter-frame block (host bookkeeping, e.g. FLOP counts)."""
@@ -51,6 +55,8 @@ class ScheduleSpec:
             return "register"
         if l < self.early_frame:
             return "frame"
+        if self.merge:
+            return "merged"
         return "subsampled" if tuple(self.sub) != (1, 1) else "global"
 
 
