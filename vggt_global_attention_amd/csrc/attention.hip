@@ -549,7 +549,7 @@ __device__ __forceinline__ BlockCoord block_coord(const AttnArgs& p) {
 // load unit (global_load_lds, no register staging), with one workgroup
 // barrier per tile.
 template <int QB, int NW, bool SGA, bool W, bool B16>
-__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
+__global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_kernel(AttnArgs p) {
   constexpr int BQ = NW * QB * 32;
   static_assert(!(B16 && (SGA || W)), "the bf16-operand variant serves plain sets");
   typedef typename Ops16<B16>::T T;  // q, k, v, P and O
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
   // all tiles of the range but its last: no mask; tile t sits in LDS buffer
   // (t - t0) & 1
   int t = t0;
-  if constexpr (NW == 8) {
+  if constexpr (NW == 8 || QB == 1) {
     for (; t + 2 < t1; t += 2) {
       step(std::integral_constant<int, 0>(), t);
       step(std::integral_constant<int, 1>(), t + 1);
@@ -655,9 +655,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs p) {
       ++t;
     }
   } else {
-    // 4-wave tiles keep the rolled loop (unrolled, the extra registers cost
-    // a wave of occupancy); the lane offsets carry the buffer bit instead,
-    // flipped once per tile.
+    // 4-wave tiles of two row blocks per wave keep the rolled loop
+    // (unrolled, the extra registers cost a wave of occupancy); the lane
+    // offsets carry the buffer bit instead, flipped once per tile.  With one
+    // row block per wave (frames) the unrolled loop fits in 168 registers,
+    // three waves per SIMD.
     LanesT lb = ln;
     for (; t < t1 - 1; ++t) {
       issue(t + 1, ((t - t0) & 1) ^ 1);
