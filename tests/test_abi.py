@@ -95,6 +95,32 @@ def test_workspace_bytes():
     assert B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, shape(T=1030)) == 0
 
 
+def _kv_rows(mode, S, T=1031):
+    # the header's padding rule: each set to 64 keys, the total to 2,048 rows
+    # from 16,384 on (else 256)
+    per = -(-T // 64) * 64
+    cover = per * S if mode == B.MODE_FRAME else -(-(S * T) // 64) * 64
+    a = 2048 if cover >= 16384 else 256
+    return -(-cover // a) * a
+
+
+def test_key_value_row_limit():
+    # at most 2^28 key / value rows per head: the last S inside and the first
+    # S beyond, for global and frame sets
+    lim = 1 << 28
+    for mode in (B.MODE_GLOBAL, B.MODE_FRAME):
+        S = 1
+        while _kv_rows(mode, 2 * S) <= lim:
+            S *= 2
+        hi = 2 * S
+        while hi - S > 1:
+            mid = (S + hi) // 2
+            S, hi = (mid, hi) if _kv_rows(mode, mid) <= lim else (S, mid)
+        assert _kv_rows(mode, S) <= lim < _kv_rows(mode, S + 1)
+        assert B.vggt_attn_workspace_bytes(mode, shape(S=S)) > 0
+        assert B.vggt_attn_workspace_bytes(mode, shape(S=S + 1)) == 0
+
+
 FAKE = dict(X=0x100000, Wqkv=0x200000, Wo=0x300000, qg=0x400000, qb=0x400100, kg=0x400200,
             kb=0x400300, Y=0x500000)
 

@@ -193,6 +193,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->kv_seq_stride = p->seq_stride;
     p->nD = 0;
   }
+  if (p->kv_rows > kMaxKvRows) return VGGT_ATTN_ESHAPE;
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {
     p->map = RowMap{p->rows, 0, (int32_t)N, 1, 0};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {

@@ -118,11 +118,19 @@ __device__ __forceinline__ int lds_slot(int row, int col) {
 }
 __device__ __forceinline__ int lds_swz(int row, int col) { return row * 128 + (lds_slot(row, col) << 4); }
 
-// 16 bytes per lane global -> LDS by the load unit (global_load_lds): lane i
-// of the wave writes lds_wave_base + 16 i.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// 16 bytes per lane global -> LDS by the load unit (buffer_load ... lds):
+// lane i of the wave writes lds_wave_base + 16 i.  The source is a buffer
+// resource -- a wave-uniform base in scalar registers -- plus the lane's byte
+// offset in a vector register, so moving to the next tile costs scalar adds
+// only, no per-lane 64-bit address arithmetic.  The resource spans 4 GB from
+// `base` with no range clamping (every copy of the loop is in bounds).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off,
+                                          void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                           16, lane_off, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -563,7 +571,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
   f16* const sizes_lds = reinterpret_cast<f16*>(smem_raw + 2 * 2 * 64 * 128);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: LDS destinations and copy bases stay scalar
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // single-set grids may have a split tail
   constexpr bool kSplit = true;
@@ -601,25 +610,32 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
   // both tiles.  A tile is complete once every wave has waited for its own
   // copies (vmcnt) and passed the workgroup barrier.
   constexpr int KI = 8 / NW;
-  const f16* gk[KI];
-  const f16* gv[KI];
+  // Copy i of this wave fills rows 8 (wave KI + i) .. +7 of a tile.  Its
+  // source is a wave-uniform base -- the first of those rows of K, or of v^T
+  // at the tile's first key -- moved per tile by scalar adds, plus the lane's
+  // byte offset within the eight rows: below 8 * 128 bytes for K, below
+  // 8 kv_rows * 2 bytes for v^T (kv_rows <= 2^28 keeps it in 32 bits).
+  uint32_t ok[KI], ov[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int row = 8 * (wave * KI + i) + (lane >> 3);
     const int col = lds_slot(row, lane & 7);
-    gk[i] = kh + (kv0 + row) * kDh + col * 8;
-    gv[i] = vh + (int64_t)row * p.kv_rows + kv0 + col * 8;
+    ok[i] = (uint32_t)(((lane >> 3) * kDh + col * 8) * 2);
+    ov[i] = (uint32_t)((lane >> 3) * 2) * (uint32_t)p.kv_rows + (uint32_t)(col * 16);
   }
   auto issue = [&](int tile, int buf) {
+    const int64_t key0 = kv0 + (int64_t)tile * 64;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      lds_dma16(gk[i] + (int64_t)tile * 64 * kDh, &smem[buf][0][0] + (wave * KI + i) * 1024);
-      lds_dma16(gv[i] + (int64_t)tile * 64, &smem[buf][1][0] + (wave * KI + i) * 1024);
+      const int row0 = 8 * (wave * KI + i);
+      lds_dma16(dma_rsrc(kh + (key0 + row0) * kDh), ok[i], &smem[buf][0][0] + (wave * KI + i) * 1024);
+      lds_dma16(dma_rsrc(vh + (int64_t)row0 * p.kv_rows + key0), ov[i],
+                &smem[buf][1][0] + (wave * KI + i) * 1024);
     }
     // the 64 key sizes (128 bytes): every lane of every wave copies chunk
     // i % 8 to slot i, so slots 0..7 hold the sizes (the waves write the
     // same bytes; no branch around the copy)
-    if (W) lds_dma16(nh + (int64_t)tile * 64 + (lane & 7) * 8, sizes_lds + buf * 512);
+    if (W) lds_dma16(dma_rsrc(nh + (int64_t)tile * 64), (uint32_t)((lane & 7) * 16), sizes_lds + buf * 512);
   };
   auto land = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS

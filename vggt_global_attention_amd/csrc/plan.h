@@ -20,6 +20,9 @@ constexpr int kAttnBK = 64;         // keys per attention tile
 // padding would be large (fewer than kRowAlignFrom rows).
 constexpr int kRowAlign = 2048;
 constexpr int kRowAlignFrom = 16384;
+// Key / value rows per head at most 2^28: the attention kernel's copies address
+// eight v^T rows from one base with a 32-bit byte offset (8 * kv_rows * 2 < 2^32).
+constexpr int64_t kMaxKvRows = (int64_t)1 << 28;
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
 // Split attention tail: its partial-result buffer holds at most
 // kSplitMaxRows query rows x key ranges; a split workgroup runs at most
