@@ -853,39 +853,65 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  auto compute = [&](int stage) {
+  const int nk = g.K / kWBK;
+  // Operand fragments of one 16-deep k-chunk of a stage: the A rows of the
+  // wave's two feature blocks and the B rows of its four token blocks.
+  struct Frag {
+    V8 a[2], b[4];
+  };
+  auto load = [&](int stage, int kc, Frag& f) {
     const char* As = &smem[stage][0];
     const char* Bs = As + kAB;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      V8 af[2], bfr[4];
+    for (int fb = 0; fb < 2; ++fb)
+      f.a[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 32 + j, kc * 2 + h));
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-        af[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 32 + j, kc * 2 + h));
+    for (int tb = 0; tb < 4; ++tb)
+      f.b[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 128 + tb * 32 + j, kc * 2 + h));
+  };
+  // MFMAs i in [lo, hi) of a chunk's eight (feature block i / 4, token block
+  // i % 4), fenced so that the compiler keeps them where they are written
+  auto mma = [&](const Frag& f, int lo, int hi) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        bfr[tb] = *reinterpret_cast<const V8*>(Bs + swz(wm * 128 + tb * 32 + j, kc * 2 + h));
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mfma32x32x16(af[fb], bfr[tb], acc[fb][tb]);
-    }
+    for (int i = 0; i < 8; ++i)
+      if (i >= lo && i < hi) acc[i >> 2][i & 3] = mfma32x32x16(f.a[i >> 2], f.b[i & 3], acc[i >> 2][i & 3]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Eight DMA instructions per wave per k-step; stage kt+1 is fetched while
-  // stage kt is computed.  Bare s_barrier after an explicit wait that also
-  // covers this wave's LDS reads (lgkmcnt(0), as in gemm_dma_kernel): the
-  // stage overwritten next was last read before the previous barrier.
+  // stage kt is computed.  The four k-chunks of a stage are software
+  // pipelined: the fragments of chunk c+1 are read from LDS between the
+  // second and third of chunk c's eight MFMAs, and after the stage barrier
+  // the first chunk of the next stage is read there in the last chunk.  A
+  // chunk's first MFMA then waits only for reads that were issued six MFMAs
+  // earlier.  Bare s_barrier after an explicit wait that also covers this
+  // wave's LDS reads (lgkmcnt(0), as in gemm_dma_kernel): every read of the
+  // stage that the next copy overwrites was issued and completed before that
+  // barrier.
   constexpr int kVm0 = 0x0070;  // s_waitcnt vmcnt(0) lgkmcnt(0)
-  const int nk = g.K / kWBK;
   dma(0, 0);
   __builtin_amdgcn_s_waitcnt(kVm0);
   __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  load(0, 0, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) dma(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
+    const int st = kt & 1;
+    if (kt + 1 < nk) dma(kt + 1, st ^ 1);
+    mma(f0, 0, 2);
+    load(st, 1, f1);
+    mma(f0, 2, 8);
+    mma(f1, 0, 2);
+    load(st, 2, f0);
+    mma(f1, 2, 8);
+    mma(f0, 0, 2);
+    load(st, 3, f1);
+    mma(f0, 2, 8);
     __builtin_amdgcn_s_waitcnt(kVm0);
     __builtin_amdgcn_s_barrier();
+    mma(f1, 0, 2);
+    if (kt + 1 < nk) load(st ^ 1, 0, f0);
+    mma(f1, 2, 8);
   }
 
   // the loop's last barrier: no wave reads the operand stages any more
