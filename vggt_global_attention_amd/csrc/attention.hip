@@ -660,42 +660,29 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
   land();
   // all tiles of the range but its last: no mask; tile t sits in LDS buffer
   // (t - t0) & 1
+  // (Every tile shape runs this unrolled loop: 4-wave tiles of one row block
+  // per wave fit it in 168 registers, three waves per SIMD, and those of two
+  // row blocks in 256 with the short-tile path below left out.)
   int t = t0;
-  if constexpr (NW == 8 || QB == 1) {
-    for (; t + 2 < t1; t += 2) {
-      step(std::integral_constant<int, 0>(), t);
-      step(std::integral_constant<int, 1>(), t + 1);
-    }
-    if (t < t1 - 1) {
-      step(std::integral_constant<int, 0>(), t);
-      ++t;
-    }
-  } else {
-    // 4-wave tiles of two row blocks per wave keep the rolled loop
-    // (unrolled, the extra registers cost a wave of occupancy); the lane
-    // offsets carry the buffer bit instead, flipped once per tile.  With one
-    // row block per wave (frames) the unrolled loop fits in 168 registers,
-    // three waves per SIMD.
-    LanesT lb = ln;
-    for (; t < t1 - 1; ++t) {
-      issue(t + 1, ((t - t0) & 1) ^ 1);
-      if (active)
-        tile_run<false, 4, W>(R, lb, smem[0][0], smem[0][1], sizes_lds + ((t - t0) & 1) * 512, lane, 64,
-                              t == t0, t - t0 < kEagerTiles);
-      land();
-      lb.flip(2 * 64 * 128);  // the other buffer
-    }
+  for (; t + 2 < t1; t += 2) {
+    step(std::integral_constant<int, 0>(), t);
+    step(std::integral_constant<int, 1>(), t + 1);
+  }
+  if (t < t1 - 1) {
+    step(std::integral_constant<int, 0>(), t);
+    ++t;
   }
   // last tile of the range (t = t1 - 1): keys past the end of the set masked.  Small
-  // sets (4-wave tiles: frames, register sets) often end in a short tile --
-  // 7 of 64 keys for a 26 x 39 frame -- whose second half is skipped (its
-  // probabilities are exactly zero, so the result is the same bit for bit).
+  // sets on 4-wave tiles of one row block per wave (frames) often end in a
+  // short tile -- 7 of 64 keys for a 26 x 39 frame -- whose second half is
+  // skipped (its probabilities are exactly zero, so the result is the same bit
+  // for bit); the two-row-block tile leaves that path out for its registers.
   if (active) {
     LanesT lb = ln;
     lb.flip(((t - t0) & 1) * 2 * 64 * 128);
     const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
     const f16* Ns = sizes_lds + ((t - t0) & 1) * 512;
-    if (NW == 4 && last_valid <= 32) {
+    if (NW == 4 && QB == 1 && last_valid <= 32) {
       tile_run<true, 2, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
     } else {
       tile_run<true, 4, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
