@@ -87,6 +87,7 @@ struct AttnArgs {
   int64_t kv_rows;     // key rows per head; set s starts at key s * kv_seq_stride
   int64_t kv_seq_stride;
   int nseq, L, Lk, H, qtiles;  // sets, query end and keys per set, heads, query tiles
+  FastDiv qt_div, h_div;       // division by qtiles and by H (scalar on the device)
   int q0;                      // first query row of a set (a window of the global set), else 0
   const Scalars* sc;
   // subsampled global set only: every token's key / value (for the diagonal)
@@ -503,10 +504,10 @@ struct BlockCoord {
 };
 __device__ __forceinline__ BlockCoord coord_of(const AttnArgs& p, int logical) {
   BlockCoord c;
-  c.qt = logical % p.qtiles;
-  const int t2 = logical / p.qtiles;
-  c.h = t2 % p.H;
-  c.s = t2 / p.H;
+  const int t2 = fdiv(logical, p.qt_div);
+  c.qt = logical - t2 * p.qtiles;
+  c.s = fdiv(t2, p.h_div);
+  c.h = t2 - c.s * p.H;
   c.ks = -1;
   c.unit = -1;
   c.skip = false;
@@ -823,6 +824,8 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.H = p.H;
   g.q0 = p.q0;
   g.qtiles = (p.L - p.q0 + BQ - 1) / BQ;
+  g.qt_div = fast_div(g.qtiles);
+  g.h_div = fast_div(p.H);
   g.sc = ws_scalars(p, a);
   if (SGA) {
     g.k_all = ws_k(p, a);

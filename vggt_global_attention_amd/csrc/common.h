@@ -71,6 +71,31 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Exact floor(n / d) for 0 <= n < 2^31 and 1 <= d < 2^31 by one multiply:
+// m = ceil(2^k / d) with k = 31 + l, l = ceil(log2 d).  The excess e = m d - 2^k
+// is below d, so n m / 2^k = n / d + n e / (d 2^k) with n e / (d 2^k) < 2^-l <= 1/d,
+// which never reaches the next multiple of 1/d (division by invariant integers
+// using multiplication, after Granlund and Montgomery).  m <= 2^32 and
+// n m < 2^64.
+struct FastDiv {
+  uint64_t m;
+  int k;
+  int d;
+};
+
+inline FastDiv fast_div(int64_t d) {
+  if (d < 1) d = 1;
+  if (d > 0x7fffffff) d = 0x7fffffff;  // every numerator is below d then: quotient 0
+  int l = 0;
+  while (((int64_t)1 << l) < d) ++l;
+  const int k = 31 + l;
+  return FastDiv{(((uint64_t)1 << k) + (uint64_t)d - 1) / (uint64_t)d, k, (int)d};
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+  return (int)(((uint64_t)(uint32_t)n * f.m) >> f.k);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
