@@ -92,7 +92,7 @@ inline FastDiv fast_div(int64_t d) {
   return FastDiv{(((uint64_t)1 << k) + (uint64_t)d - 1) / (uint64_t)d, k, (int)d};
 }
 
-__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+__host__ __device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
   return (int)(((uint64_t)(uint32_t)n * f.m) >> f.k);
 }
 
