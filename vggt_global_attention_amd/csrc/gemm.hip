@@ -745,7 +745,10 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Wide kernel (output features a multiple of 256): 256 token rows x 256
 // output features per workgroup, 8 waves of 128 x 64 (2 x 4), 64-deep
-// k-steps in two LDS stages of 64 KB.  A DMA instruction moves 8 whole
+// k-steps; 160 KB of LDS: two 32 KB weight stages and three 32 KB token-row
+// stages (token rows copied two k-steps ahead, weights one; measured at the
+// s500 frame QKV shape against two stages of both: 3.86 vs 3.91 ms, s100
+// QKV 0.77 vs 0.79 ms).  A DMA instruction moves 8 whole
 // 128-byte rows (8 cache lines, all bytes used), and the 256 x 256 tile moves
 // half the bytes per FLOP of the 256 x 128 one.  LDS rows use the 128-byte
 // swizzle chunk ^ (row & 7) ^ ((row >> 3) & 1); lane i of a DMA instruction
@@ -762,7 +765,11 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
   typedef typename GemmTypes<EPI>::V8 V8;
   constexpr int kAB = kWBN * 128;  // A stage: 256 feature rows x 128 B
   constexpr int kBB = kWBM * 128;  // B stage: 256 token rows x 128 B
-  __shared__ __attribute__((aligned(1024))) char smem[2][kAB + kBB];
+  // Two A (weight) stages and three B (token row) stages, 160 KB: the token
+  // rows are read from HBM for the first time and are copied two k-steps
+  // ahead; the weight slice is L2-resident and is copied one step ahead.
+  constexpr int kAStages = 2, kBStages = 3;
+  __shared__ __attribute__((aligned(1024))) char smem[kAStages * kAB + kBStages * kBB];
   static_assert(sizeof(smem) >= 8 * 16384, "staged epilogue: 16 KB of LDS per wave");
 
   const int tid = threadIdx.x;
@@ -808,15 +815,18 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
       bptr[q] = Bb + w * kDh + lcol * 8;
     }
   }
-  auto dma = [&](int kt, int stage) {
-    char* base = &smem[stage][0];
+  auto dma_a = [&](int kt, int stage) {
+    char* base = smem + stage * kAB;
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(aptr[q] + kt * kWBK, base + (q * 8 + wave) * 1024);
+  };
+  auto dma_b = [&](int kt, int stage) {
+    char* base = smem + kAStages * kAB + stage * kBB;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint16_t* src = epi_qkv(EPI) ? bptr[q] + kt * kWBK
                                            : bptr[q] + (int64_t)kt * g.rows * kDh;
-      dma16(src, base + kAB + (q * 8 + wave) * 1024);
+      dma16(src, base + (q * 8 + wave) * 1024);
     }
   };
 
@@ -834,9 +844,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
   struct Frag {
     V8 a[2], b[4];
   };
-  auto load = [&](int stage, int kc, Frag& f) {
-    const char* As = &smem[stage][0];
-    const char* Bs = As + kAB;
+  auto load = [&](int kt, int kc, Frag& f) {
+    const char* As = smem + (kt & 1) * kAB;
+    const char* Bs = smem + kAStages * kAB + (kt % kBStages) * kBB;
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
       f.a[fb] = *reinterpret_cast<const V8*>(As + swz(wn * 64 + fb * 32 + j, kc * 2 + h));
@@ -854,44 +864,59 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Eight DMA instructions per wave per k-step; stage kt+1 is fetched while
-  // stage kt is computed.  The four k-chunks of a stage are software
-  // pipelined: the fragments of chunk c+1 are read from LDS between the
-  // second and third of chunk c's eight MFMAs, and after the stage barrier
-  // the first chunk of the next stage is read there in the last chunk.  A
-  // chunk's first MFMA then waits only for reads that were issued six MFMAs
-  // earlier.  Bare s_barrier after an explicit wait that also covers this
-  // wave's LDS reads (lgkmcnt(0), as in gemm_dma_kernel): every read of the
-  // stage that the next copy overwrites was issued and completed before that
-  // barrier.
-  constexpr int kVm0 = 0x0070;  // s_waitcnt vmcnt(0) lgkmcnt(0)
-  dma(0, 0);
-  __builtin_amdgcn_s_waitcnt(kVm0);
+  // Per k-step each wave issues four DMA instructions for the next step's
+  // weights, then four for the token rows two steps ahead.  At the end of
+  // step kt, step kt+1 must have landed (weights and token rows); the token
+  // rows of step kt+2 may still be in flight: vmcnt counts a wave's loads in
+  // issue order, so vmcnt(4) leaves exactly those.  The four 16-deep k-chunks
+  // of a stage are software pipelined: the fragments of chunk c+1 are read
+  // from LDS between the second and third of chunk c's eight MFMAs, and after
+  // the stage barrier the first chunk of the next stage is read there in the
+  // last chunk.  A chunk's first MFMA then waits only for reads that were
+  // issued six MFMAs earlier.  Bare s_barrier after an explicit wait that
+  // also covers this wave's LDS reads (lgkmcnt(0), as in gemm_dma_kernel):
+  // every read of a stage that a later copy overwrites was issued and
+  // completed before that barrier (weights: the stage of step kt-1, refilled
+  // in step kt; token rows: the stage of step kt-1, refilled for kt+2).
+  constexpr int kVm0 = 0x0070, kVm4 = 0x0074;  // s_waitcnt vmcnt(0|4) lgkmcnt(0)
+  dma_a(0, 0);
+  dma_b(0, 0);
+  if (nk > 1) {
+    dma_b(1, 1);
+    __builtin_amdgcn_s_waitcnt(kVm4);
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVm0);
+  }
   __builtin_amdgcn_s_barrier();
   Frag f0, f1;
   load(0, 0, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) dma(kt + 1, st ^ 1);
+    if (kt + 1 < nk) dma_a(kt + 1, (kt + 1) & 1);
+    const bool ahead = kt + 2 < nk;
+    if (ahead) dma_b(kt + 2, (kt + 2) % kBStages);
     mma(f0, 0, 2);
-    load(st, 1, f1);
+    load(kt, 1, f1);
     mma(f0, 2, 8);
     mma(f1, 0, 2);
-    load(st, 2, f0);
+    load(kt, 2, f0);
     mma(f1, 2, 8);
     mma(f0, 0, 2);
-    load(st, 3, f1);
+    load(kt, 3, f1);
     mma(f0, 2, 8);
-    __builtin_amdgcn_s_waitcnt(kVm0);
+    if (ahead) {
+      __builtin_amdgcn_s_waitcnt(kVm4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVm0);
+    }
     __builtin_amdgcn_s_barrier();
     mma(f1, 0, 2);
-    if (kt + 1 < nk) load(st ^ 1, 0, f0);
+    if (kt + 1 < nk) load(kt + 1, 0, f0);
     mma(f1, 2, 8);
   }
 
   // the loop's last barrier: no wave reads the operand stages any more
   gemm_epilogue_staged<EPI>(g, acc, m0 + wm * 128, n0 + wn * 64, j, h, lane,
-                            &smem[0][0] + wave * 16384);
+                            smem + wave * 16384);
 }
 
 // Smallest number of output-feature groups (a divisor of the feature tile
