@@ -589,119 +589,136 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
   const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
   const f16* nh = W ? p.nw + (int64_t)bc.h * p.kv_rows + kv0 : nullptr;
 
-  // the wave's QB * 32 queries as 2 QB blocks of 16 (16x16x32 tile)
   using LanesT = Lanes;
-  Rows<2 * QB, typename Ops16<B16>::T8> R;
-  rows_init(R, qh, seq0, qloc0, L, lane, p.sc->kmax[bc.h]);
+  typedef typename Ops16<B16>::T8 T8;
 
-  // key tiles [t0, t1): all of them, or one key range of a split workgroup
-  // (only the range that ends the set has a masked last tile)
-  const int ntiles = (p.Lk + 63) / 64;
-  int t0 = 0, t1 = ntiles;
-  if (bc.ks >= 0) {
-    t0 = bc.ks * ntiles / p.split_p;
-    t1 = (bc.ks + 1) * ntiles / p.split_p;
-  }
-  const int last_valid = t1 == ntiles ? p.Lk - 64 * (ntiles - 1) : 64;
+  // The tile loop for a wave of NB 16-row query blocks (2 QB, or one block
+  // for a wave of a short last query tile, below).
+  auto run = [&](auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    Rows<NB, T8> R;
+    rows_init(R, qh, seq0, qloc0, L, lane, p.sc->kmax[bc.h]);
 
-  // K and v^T tiles are 64 rows of 128 bytes each.  The load unit copies them
-  // straight into LDS: one instruction fills 8 consecutive rows (1 KB; lane i
-  // lands in row i/8, slot i%8), so lane i fetches the source chunk that the
-  // row swizzle puts in that slot.  Wave w fills rows [8 KI w, 8 KI (w+1)) of
-  // both tiles.  A tile is complete once every wave has waited for its own
-  // copies (vmcnt) and passed the workgroup barrier.
-  constexpr int KI = 8 / NW;
-  // Copy i of this wave fills rows 8 (wave KI + i) .. +7 of a tile.  Its
-  // source is a wave-uniform base -- the first of those rows of K, or of v^T
-  // at the tile's first key -- moved per tile by scalar adds, plus the lane's
-  // byte offset within the eight rows: below 8 * 128 bytes for K, below
-  // 8 kv_rows * 2 bytes for v^T (kv_rows <= 2^28 keeps it in 32 bits).
-  uint32_t ok[KI], ov[KI];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int row = 8 * (wave * KI + i) + (lane >> 3);
-    const int col = lds_slot(row, lane & 7);
-    ok[i] = (uint32_t)(((lane >> 3) * kDh + col * 8) * 2);
-    ov[i] = (uint32_t)((lane >> 3) * 2) * (uint32_t)p.kv_rows + (uint32_t)(col * 16);
-  }
-  auto issue = [&](int tile, int buf) {
-    const int64_t key0 = kv0 + (int64_t)tile * 64;
+    // key tiles [t0, t1): all of them, or one key range of a split workgroup
+    // (only the range that ends the set has a masked last tile)
+    const int ntiles = (p.Lk + 63) / 64;
+    int t0 = 0, t1 = ntiles;
+    if (bc.ks >= 0) {
+      t0 = bc.ks * ntiles / p.split_p;
+      t1 = (bc.ks + 1) * ntiles / p.split_p;
+    }
+    const int last_valid = t1 == ntiles ? p.Lk - 64 * (ntiles - 1) : 64;
+
+    // K and v^T tiles are 64 rows of 128 bytes each.  The load unit copies them
+    // straight into LDS: one instruction fills 8 consecutive rows (1 KB; lane i
+    // lands in row i/8, slot i%8), so lane i fetches the source chunk that the
+    // row swizzle puts in that slot.  Wave w fills rows [8 KI w, 8 KI (w+1)) of
+    // both tiles.  A tile is complete once every wave has waited for its own
+    // copies (vmcnt) and passed the workgroup barrier.
+    constexpr int KI = 8 / NW;
+    // Copy i of this wave fills rows 8 (wave KI + i) .. +7 of a tile.  Its
+    // source is a wave-uniform base -- the first of those rows of K, or of v^T
+    // at the tile's first key -- moved per tile by scalar adds, plus the lane's
+    // byte offset within the eight rows: below 8 * 128 bytes for K, below
+    // 8 kv_rows * 2 bytes for v^T (kv_rows <= 2^28 keeps it in 32 bits).
+    uint32_t ok[KI], ov[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int row0 = 8 * (wave * KI + i);
-      lds_dma16(dma_rsrc(kh + (key0 + row0) * kDh), ok[i], &smem[buf][0][0] + (wave * KI + i) * 1024);
-      lds_dma16(dma_rsrc(vh + (int64_t)row0 * p.kv_rows + key0), ov[i],
-                &smem[buf][1][0] + (wave * KI + i) * 1024);
+      const int row = 8 * (wave * KI + i) + (lane >> 3);
+      const int col = lds_slot(row, lane & 7);
+      ok[i] = (uint32_t)(((lane >> 3) * kDh + col * 8) * 2);
+      ov[i] = (uint32_t)((lane >> 3) * 2) * (uint32_t)p.kv_rows + (uint32_t)(col * 16);
     }
-    // the 64 key sizes (128 bytes): every lane of every wave copies chunk
-    // i % 8 to slot i, so slots 0..7 hold the sizes (the waves write the
-    // same bytes; no branch around the copy)
-    if (W) lds_dma16(dma_rsrc(nh + (int64_t)tile * 64), (uint32_t)((lane & 7) * 16), sizes_lds + buf * 512);
-  };
-  auto land = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS
-    __syncthreads();
-  };
+    auto issue = [&](int tile, int buf) {
+      const int64_t key0 = kv0 + (int64_t)tile * 64;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int row0 = 8 * (wave * KI + i);
+        lds_dma16(dma_rsrc(kh + (key0 + row0) * kDh), ok[i], &smem[buf][0][0] + (wave * KI + i) * 1024);
+        lds_dma16(dma_rsrc(vh + (int64_t)row0 * p.kv_rows + key0), ov[i],
+                  &smem[buf][1][0] + (wave * KI + i) * 1024);
+      }
+      // the 64 key sizes (128 bytes): every lane of every wave copies chunk
+      // i % 8 to slot i, so slots 0..7 hold the sizes (the waves write the
+      // same bytes; no branch around the copy)
+      if (W) lds_dma16(dma_rsrc(nh + (int64_t)tile * 64), (uint32_t)((lane & 7) * 16), sizes_lds + buf * 512);
+    };
+    auto land = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's copies are in LDS
+      __syncthreads();
+    };
 
-  const LanesT ln(lane);
-  // One tile from LDS buffer BUF while the next tile moves into BUF ^ 1.  The
-  // loop is unrolled by two so that BUF is a constant and every LDS address
-  // is a lane offset plus an immediate; a scheduling barrier keeps the two
-  // halves from being interleaved (which would only add live registers).
-  auto step = [&](auto buf_c, int t) {
-    constexpr int BUF = decltype(buf_c)::value;
-    issue(t + 1, BUF ^ 1);
-    if (active)
-      tile_run<false, 4, W>(R, ln, smem[BUF][0], smem[BUF][1], sizes_lds + BUF * 512, lane, 64, t == t0,
-                            t - t0 < kEagerTiles);
+    const LanesT ln(lane);
+    // One tile from LDS buffer BUF while the next tile moves into BUF ^ 1.  The
+    // loop is unrolled by two so that BUF is a constant and every LDS address
+    // is a lane offset plus an immediate; a scheduling barrier keeps the two
+    // halves from being interleaved (which would only add live registers).
+    auto step = [&](auto buf_c, int t) {
+      constexpr int BUF = decltype(buf_c)::value;
+      issue(t + 1, BUF ^ 1);
+      if (active)
+        tile_run<false, 4, W>(R, ln, smem[BUF][0], smem[BUF][1], sizes_lds + BUF * 512, lane, 64, t == t0,
+                              t - t0 < kEagerTiles);
+      land();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(t0, 0);
     land();
-    __builtin_amdgcn_sched_barrier(0);
+    // all tiles of the range but its last: no mask; tile t sits in LDS buffer
+    // (t - t0) & 1
+    // (Every tile shape runs this unrolled loop: 4-wave tiles of one row block
+    // per wave fit it in 168 registers, three waves per SIMD, and those of two
+    // row blocks in 256 with the short-tile path below left out.)
+    int t = t0;
+    for (; t + 2 < t1; t += 2) {
+      step(std::integral_constant<int, 0>(), t);
+      step(std::integral_constant<int, 1>(), t + 1);
+    }
+    if (t < t1 - 1) {
+      step(std::integral_constant<int, 0>(), t);
+      ++t;
+    }
+    // last tile of the range (t = t1 - 1): keys past the end of the set masked.  Small
+    // sets on 4-wave tiles of one row block per wave (frames) often end in a
+    // short tile -- 7 of 64 keys for a 26 x 39 frame -- whose second half is
+    // skipped (its probabilities are exactly zero, so the result is the same bit
+    // for bit); the two-row-block tile leaves that path out for its registers.
+    if (active) {
+      LanesT lb = ln;
+      lb.flip(((t - t0) & 1) * 2 * 64 * 128);
+      const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
+      const f16* Ns = sizes_lds + ((t - t0) & 1) * 512;
+      if (NW == 4 && QB == 1 && last_valid <= 32) {
+        tile_run<true, 2, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
+      } else {
+        tile_run<true, 4, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
+      }
+    }
+    // the diagonal and mean columns enter once per row: in its last key range
+    if constexpr (SGA) {
+      if (active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, lane);
+    }
+    if (kSplit && bc.unit >= 0) {
+      // a key range of a split workgroup: unnormalised state for the merge
+      float* po = p.part + (int64_t)bc.unit * BQ * kDh;
+      float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)kXcds * p.umax * BQ * kDh) +
+                    (int64_t)bc.unit * BQ;
+      if (active) rows_store_partial(R, po, pml, wave * QB * 32, lane);
+    } else if (active) {
+      rows_store(R, qh, seq0, qloc0, L, lane);
+    }
   };
-  issue(t0, 0);
-  land();
-  // all tiles of the range but its last: no mask; tile t sits in LDS buffer
-  // (t - t0) & 1
-  // (Every tile shape runs this unrolled loop: 4-wave tiles of one row block
-  // per wave fit it in 168 registers, three waves per SIMD, and those of two
-  // row blocks in 256 with the short-tile path below left out.)
-  int t = t0;
-  for (; t + 2 < t1; t += 2) {
-    step(std::integral_constant<int, 0>(), t);
-    step(std::integral_constant<int, 1>(), t + 1);
-  }
-  if (t < t1 - 1) {
-    step(std::integral_constant<int, 0>(), t);
-    ++t;
-  }
-  // last tile of the range (t = t1 - 1): keys past the end of the set masked.  Small
-  // sets on 4-wave tiles of one row block per wave (frames) often end in a
-  // short tile -- 7 of 64 keys for a 26 x 39 frame -- whose second half is
-  // skipped (its probabilities are exactly zero, so the result is the same bit
-  // for bit); the two-row-block tile leaves that path out for its registers.
-  if (active) {
-    LanesT lb = ln;
-    lb.flip(((t - t0) & 1) * 2 * 64 * 128);
-    const bool first = t1 - t0 == 1, eager = t - t0 < kEagerTiles;
-    const f16* Ns = sizes_lds + ((t - t0) & 1) * 512;
-    if (NW == 4 && QB == 1 && last_valid <= 32) {
-      tile_run<true, 2, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
-    } else {
-      tile_run<true, 4, W>(R, lb, smem[0][0], smem[0][1], Ns, lane, last_valid, first, eager);
+  // A wave with at most 16 rows -- in the short last query tile of a frame
+  // set (7 of 32 for a 26 x 39 frame), or with none -- runs one row block:
+  // the same per-row arithmetic (bit for bit the same rows), half the MFMAs
+  // and softmax work, so the short tile's workgroup leaves sooner.
+  if constexpr (QB == 1 && !SGA) {
+    if (L - qloc0 <= 16) {
+      run(std::integral_constant<int, 1>());
+      return;
     }
   }
-  // the diagonal and mean columns enter once per row: in its last key range
-  if constexpr (SGA) {
-    if (active && (bc.ks < 0 || bc.ks == p.split_p - 1)) sga_columns(R, p, bc.h, qloc0, lane);
-  }
-  if (kSplit && bc.unit >= 0) {
-    // a key range of a split workgroup: unnormalised state for the merge
-    float* po = p.part + (int64_t)bc.unit * BQ * kDh;
-    float2* pml = reinterpret_cast<float2*>(p.part + (int64_t)kXcds * p.umax * BQ * kDh) +
-                  (int64_t)bc.unit * BQ;
-    if (active) rows_store_partial(R, po, pml, wave * QB * 32, lane);
-  } else if (active) {
-    rows_store(R, qh, seq0, qloc0, L, lane);
-  }
+  run(std::integral_constant<int, 2 * QB>());
 }
 
 // Merge of a split tail: for each query row of a split workgroup, the
