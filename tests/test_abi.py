@@ -86,7 +86,8 @@ def test_workspace_bytes():
     r = B.vggt_attn_workspace_bytes(B.MODE_REGISTER, s)
     N = 100 * 1031
     assert g >= 3 * 16 * N * 64 * 2          # q, k, v in fp16 for every token and head
-    assert f >= 3 * 16 * 100 * 1088 * 64 * 2  # frames are padded to whole key tiles
+    # frames: q / k rows padded to 16 per frame, v^T columns to whole 64-key tiles
+    assert f >= 2 * 16 * 100 * 1040 * 64 * 2 + 16 * 100 * 1088 * 64 * 2
     # global sets also hold the partial results of a split tail: at most 512
     # key-range units of 512 queries x (64 + 2) fp32
     assert g - 3 * 16 * 104448 * 64 * 2 <= 3 * 1024 * 1024 + 512 * 512 * 66 * 4  # + Wo copy, tables
@@ -96,10 +97,16 @@ def test_workspace_bytes():
 
 
 def _kv_rows(mode, S, T=1031):
-    # the header's padding rule: each set to 64 keys, the total to 2,048 rows
-    # from 16,384 on (else 256)
-    per = -(-T // 64) * 64
-    cover = per * S if mode == B.MODE_FRAME else -(-(S * T) // 64) * 64
+    # the header's padding rule: the global set to 64 keys, the total to 2,048
+    # rows from 16,384 on (else 256); frame sets: q / k rows 16 per frame (plus
+    # the last frame's last key tile), v^T columns 64 per frame, the total to
+    # 256 -- the larger of the two counts
+    if mode == B.MODE_FRAME:
+        ss, vts = -(-T // 16) * 16, -(-T // 64) * 64
+        cover = ss * (S - 1) + vts
+        a = 2048 if cover >= 16384 else 256
+        return max(-(-cover // a) * a, -(-(S * vts) // 256) * 256)
+    cover = -(-(S * T) // 64) * 64
     a = 2048 if cover >= 16384 else 256
     return -(-cover // a) * a
 

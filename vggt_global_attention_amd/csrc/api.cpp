@@ -117,8 +117,10 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
     p->nseq = s->S;
     p->L = s->T;
-    p->seq_stride = round_up(s->T, kAttnBK);
-    cover = p->seq_stride * s->S;
+    // q / k rows: frames padded to 16 rows; the last frame's last key tile
+    // (64 rows from a multiple of 64) must stay inside the buffer
+    p->seq_stride = round_up(s->T, kFrameRowAlign);
+    cover = p->seq_stride * (s->S - 1) + round_up(s->T, kAttnBK);
     p->attn_qb = 1;
     p->attn_waves = 4;
   } else {
@@ -193,7 +195,14 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->kv_seq_stride = p->seq_stride;
     p->nD = 0;
   }
-  if (p->kv_rows > kMaxKvRows) return VGGT_ATTN_ESHAPE;
+  // v^T columns: frames padded to whole 64-key tiles; elsewhere the rows
+  p->vt_rows = p->rows;
+  p->vt_seq_stride = p->seq_stride;
+  if (mode == VGGT_ATTN_MODE_FRAME) {
+    p->vt_seq_stride = round_up(s->T, kAttnBK);
+    p->vt_rows = round_up((int64_t)s->S * p->vt_seq_stride, 256);
+  }
+  if (p->kv_rows > kMaxKvRows || p->vt_rows > kMaxKvRows) return VGGT_ATTN_ESHAPE;
   if (mode == VGGT_ATTN_MODE_GLOBAL || subsampled || desc || merged) {
     p->map = RowMap{p->rows, 0, (int32_t)N, 1, 0};
   } else if (mode == VGGT_ATTN_MODE_FRAME) {
@@ -251,7 +260,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->off_k = off;
     off += qkv;
     p->off_v = off;
-    off += qkv;
+    off += (size_t)s->H * (size_t)p->vt_rows * kDh * 2;
   }
   if (merged) {
     // merged queries, keys, values and key sizes, kv_rows per head (sized for

@@ -81,11 +81,13 @@ constexpr int kEagerTiles = 16;    // unsettled rows follow the exact running ma
 struct AttnArgs {
   f16* q;              // [H][rows][64] scaled queries; overwritten with O
   const f16* k;        // [H][kv_rows][64] keys of the loop
-  const f16* vt;       // [H][64][kv_rows], keys permuted inside aligned 16-groups
+  const f16* vt;       // [H][64][vt_rows], keys permuted inside aligned 16-groups
   int64_t rows;        // query rows per head; set s starts at row s * seq_stride
   int64_t seq_stride;
   int64_t kv_rows;     // key rows per head; set s starts at key s * kv_seq_stride
   int64_t kv_seq_stride;
+  int64_t vt_rows;     // columns per v^T row; set s starts at column s * vt_seq_stride
+  int64_t vt_seq_stride;
   int nseq, L, Lk, H, qtiles;  // sets, query end and keys per set, heads, query tiles
   FastDiv qt_div, h_div;       // division by qtiles and by H (scalar on the device)
   int q0;                      // first query row of a set (a window of the global set), else 0
@@ -581,12 +583,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
   if (kSplit && bc.skip) return;  // whole block: before any barrier
   const int64_t seq0 = (int64_t)bc.s * p.seq_stride;
   const int64_t kv0 = (int64_t)bc.s * p.kv_seq_stride;
+  const int64_t vt0 = (int64_t)bc.s * p.vt_seq_stride;
   const int L = p.L;
   const int qloc0 = p.q0 + bc.qt * BQ + wave * QB * 32;
   const bool active = __builtin_amdgcn_readfirstlane(qloc0) < L;
   T* qh = reinterpret_cast<T*>(p.q) + (int64_t)bc.h * p.rows * kDh;
   const f16* kh = p.k + (int64_t)bc.h * p.kv_rows * kDh;
-  const f16* vh = p.vt + (int64_t)bc.h * kDh * p.kv_rows;
+  const f16* vh = p.vt + (int64_t)bc.h * kDh * p.vt_rows;
   const f16* nh = W ? p.nw + (int64_t)bc.h * p.kv_rows + kv0 : nullptr;
 
   using LanesT = Lanes;
@@ -620,22 +623,22 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && QB == 1) ? 3 : 2) void attn_ke
     // source is a wave-uniform base -- the first of those rows of K, or of v^T
     // at the tile's first key -- moved per tile by scalar adds, plus the lane's
     // byte offset within the eight rows: below 8 * 128 bytes for K, below
-    // 8 kv_rows * 2 bytes for v^T (kv_rows <= 2^28 keeps it in 32 bits).
+    // 8 vt_rows * 2 bytes for v^T (vt_rows <= 2^28 keeps it in 32 bits).
     uint32_t ok[KI], ov[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int row = 8 * (wave * KI + i) + (lane >> 3);
       const int col = lds_slot(row, lane & 7);
       ok[i] = (uint32_t)(((lane >> 3) * kDh + col * 8) * 2);
-      ov[i] = (uint32_t)((lane >> 3) * 2) * (uint32_t)p.kv_rows + (uint32_t)(col * 16);
+      ov[i] = (uint32_t)((lane >> 3) * 2) * (uint32_t)p.vt_rows + (uint32_t)(col * 16);
     }
     auto issue = [&](int tile, int buf) {
-      const int64_t key0 = kv0 + (int64_t)tile * 64;
+      const int64_t key0 = kv0 + (int64_t)tile * 64, col0 = vt0 + (int64_t)tile * 64;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
         const int row0 = 8 * (wave * KI + i);
         lds_dma16(dma_rsrc(kh + (key0 + row0) * kDh), ok[i], &smem[buf][0][0] + (wave * KI + i) * 1024);
-        lds_dma16(dma_rsrc(vh + (int64_t)row0 * p.kv_rows + key0), ov[i],
+        lds_dma16(dma_rsrc(vh + (int64_t)row0 * p.vt_rows + col0), ov[i],
                   &smem[buf][1][0] + (wave * KI + i) * 1024);
       }
       // the 64 key sizes (128 bytes): every lane of every wave copies chunk
@@ -835,6 +838,11 @@ static hipError_t launch_attn_t(const Plan& p, const Ptrs& a, hipStream_t st) {
   g.seq_stride = p.seq_stride;
   g.kv_rows = p.kv_rows;
   g.kv_seq_stride = p.kv_seq_stride;
+  // v^T of the loop: the projection's own (frame, global, register sets) or a
+  // compact copy (subsampled, merged, descriptor keys), which has the keys' rows
+  const bool own_vt = !compact_kv(p) && p.mode != VGGT_ATTN_MODE_DESCRIPTOR;
+  g.vt_rows = own_vt ? p.vt_rows : p.kv_rows;
+  g.vt_seq_stride = own_vt ? p.vt_seq_stride : p.kv_seq_stride;
   g.nseq = p.nseq;
   g.L = p.L;
   g.Lk = p.Lk;

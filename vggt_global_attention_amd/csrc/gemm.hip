@@ -31,6 +31,11 @@ struct GemmArgs {
   const void* A;  // weights [Nf][K], row-major (bf16 for QKV, fp16 for OUT)
   const void* B;  // QKV: X bf16 [S*T][d] through `map`; OUT: O fp16 [H][rows][64]
   int64_t rows;   // workspace rows (multiple of 128)
+  int64_t vt_rows;  // QKV: columns of v^T [H][64][vt_rows]
+  int vt_seq;       // QKV: 0, or the v^T column stride of a set (frame sets): workspace row
+                    // w = s * seq_stride + t has its value at column s * vt_seq + t
+  FastDiv dss;      // division by seq_stride (used when vt_seq != 0)
+  int vt_sets;      // (vt_seq != 0) sets with a v^T column range: rows past them store no v^T
   int Nf, K;
   int fgroups;    // output-feature groups walked one after the other (divides Nf / 128)
   int64_t m_first;       // first workspace row of the token tiles (a multiple of the tile)
@@ -61,6 +66,30 @@ __device__ __forceinline__ int64_t row_src(const GemmArgs& g, int64_t w64) {
   const int grp = fdiv(v, g.dgrp);
   const int t = v - grp * g.dgrp.d;
   return (t < m.grp_valid && grp < m.ngroups) ? (int64_t)(grp * (int)m.src_stride + t) : -1;
+}
+
+// v^T column of workspace row x (below 2^31).  For frame sets also the row's
+// place t in its set and the set's padding columns [pad0, pad1): the columns
+// past the set's last row up to the next multiple of 64, which no row maps to.
+// They hold masked keys of the attention kernel's last tile, whose zero
+// probabilities must meet finite values, so the epilogue writes zeros there
+// with the set's last rows.  Rows past the last set (the buffer's tail
+// padding) get column -1: no v^T store.  Identity (t = -1) for the other sets.
+struct VtCol {
+  int64_t col, pad0, pad1;
+  int t;
+};
+__device__ __forceinline__ VtCol vt_column(const GemmArgs& g, int64_t x) {
+  VtCol c{x, 0, 0, -1};
+  if (g.vt_seq == 0) return c;
+  const int x32 = (int)x;
+  const int s = fdiv(x32, g.dss);
+  c.t = x32 - s * g.dss.d;
+  const int64_t base = (int64_t)s * g.vt_seq;
+  c.col = s < g.vt_sets ? base + c.t : -1;
+  c.pad0 = base + g.dss.d;
+  c.pad1 = base + g.vt_seq;
+  return c;
 }
 
 // Grid position of X row `src` for the RoPE of q and k: (row, column) plus the
@@ -257,12 +286,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
       }
     } else {
       const int kv = range_exponent(g.sc->xnorm * g.sc->wvnorm);
-      OT* dst = reinterpret_cast<OT*>(g.vt) + (int64_t)hd * kDh * g.rows;
+      OT* dst = reinterpret_cast<OT*>(g.vt) + (int64_t)hd * kDh * g.vt_rows;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int64_t w = mbase + tb * 32 + j;
         if (g.real_only && row_src(g, w) < 0) continue;
-        const int64_t x = w + g.dst_off;
+        const VtCol vc = vt_column(g, w + g.dst_off);
+        if (vc.col < 0) continue;
+        const int64_t x = vc.col;
         // Key position inside its aligned group of 16: key 8a + 4c + b is
         // stored at 8c + 4a + b (bits 2 and 3 swapped), the order in which
         // the attention kernel's MFMA consumes probabilities.
@@ -272,8 +303,19 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            dst[(int64_t)e * g.rows + pos] = (OT)ldexpf(acc[fb][tb][r], kv);
+            dst[(int64_t)e * g.vt_rows + pos] = (OT)ldexpf(acc[fb][tb][r], kv);
           }
+        // the set's last row: zero its padding columns (whole aligned
+        // 16-groups, so the key order inside them is moot)
+        if (vc.t == g.dss.d - 1) {  // (col >= 0 here)
+#pragma unroll
+          for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              for (int64_t z = vc.pad0; z < vc.pad1; ++z) dst[(int64_t)e * g.vt_rows + z] = (OT)0.f;
+            }
+        }
       }
     }
   } else {
@@ -425,13 +467,21 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, f32x16 (
           }
       }
       lds_wave_sync();
-      f16* dst = g.vt + (int64_t)hd * kDh * g.rows + mbase + g.dst_off;
+      // lane l stores the 8 keys of chunk c = l % 16 of feature rows l / 16,
+      // + 4, ..: one v^T column (and padding choice) per lane
+      const VtCol vc = vt_column(g, mbase + g.dst_off + (lane & 15) * 8);
+      const bool pad = vc.col >= 0 && vc.t == g.dss.d - 8;  // the set's last chunk of 8 rows
+      f16* dst = g.vt + (int64_t)hd * kDh * g.vt_rows;
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
         const int q = it * 64 + lane, e = q >> 4, c = q & 15;
         const u32x4 v =
             *reinterpret_cast<const u32x4*>(lds + e * 256 + ((c ^ (((e >> 2) & 1) << 2)) << 4));
-        *reinterpret_cast<u32x4*>(dst + (int64_t)e * g.rows + c * 8) = v;
+        if (vc.col >= 0) *reinterpret_cast<u32x4*>(dst + (int64_t)e * g.vt_rows + vc.col) = v;
+        if (pad) {
+          for (int64_t z = vc.pad0; z < vc.pad1; z += 8)
+            *reinterpret_cast<u32x4*>(dst + (int64_t)e * g.vt_rows + z) = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   } else {
@@ -966,6 +1016,10 @@ static void set_divisors(GemmArgs& g) {
 static GemmArgs base_args(const Plan& p, const Ptrs& a) {
   GemmArgs g{};
   g.rows = p.rows;
+  g.vt_rows = p.vt_rows;
+  g.vt_seq = p.vt_seq_stride != p.seq_stride ? (int)p.vt_seq_stride : 0;
+  g.dss = fast_div(g.vt_seq != 0 ? (int)p.seq_stride : 1);
+  g.vt_sets = p.nseq;
   g.map = p.map;
   g.T = p.T;
   g.gw = p.gw;
@@ -1036,6 +1090,10 @@ hipError_t launch_desc_kv(char* cache, const DescLayout& L, int H, int d, float 
   g.A = Wqkv + (int64_t)d * d;
   g.B = D;
   g.rows = L.cap_rows;  // head stride of the cache arrays
+  g.vt_rows = L.cap_rows;
+  g.vt_seq = 0;
+  g.dss = fast_div(1);
+  g.vt_sets = 1;
   g.Nf = 2 * d;
   g.K = d;
   g.m_first = 0;

@@ -24,6 +24,7 @@ constexpr int kRowAlignFrom = 16384;
 // eight v^T rows from one base with a 32-bit byte offset (8 * kv_rows * 2 < 2^32).
 constexpr int64_t kMaxKvRows = (int64_t)1 << 28;
 constexpr int kKvAlign = 256;       // compact key rows (subsampled mode) are padded to this
+constexpr int kFrameRowAlign = 16;  // q / k rows of a frame set are padded to this
 // Split attention tail: its partial-result buffer holds at most
 // kSplitMaxRows query rows x key ranges; a split workgroup runs at most
 // kSplitMaxWays key ranges of at least kSplitMinTiles key tiles each.
@@ -96,7 +97,15 @@ struct Plan {
   int L;               // query rows of a set end here (= q0 + query count)
   int q0;              // first query row (a window of the global set), else 0
   int64_t seq_stride;
-  int64_t rows;        // workspace rows held by q/k/v (multiple of 256)
+  int64_t rows;        // workspace rows held by q / k (multiple of 256)
+  // v^T [H][64][vt_rows]: set s's keys start at column s * vt_seq_stride.  The
+  // same as rows / seq_stride except for frame sets, whose q / k rows are
+  // padded to 16 per frame and whose v^T columns to 64, so that a 64-key v^T
+  // tile row is one aligned 128-byte line while the projections compute
+  // fewer padding rows.  A workspace row w = s * seq_stride + t has its value
+  // column at s * vt_seq_stride + t (vt_column()).
+  int64_t vt_rows;
+  int64_t vt_seq_stride;
   RowMap map;          // workspace row -> X row
   RowMap out_map;      // workspace row -> Y row (the window's rows only, when windowed)
   bool window;         // global mode restricted to query rows [q0, L)
