@@ -305,16 +305,27 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[2
             const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             dst[(int64_t)e * g.vt_rows + pos] = (OT)ldexpf(acc[fb][tb][r], kv);
           }
-        // the set's last row: zero its padding columns (whole aligned
-        // 16-groups, so the key order inside them is moot)
-        if (vc.t == g.dss.d - 1) {  // (col >= 0 here)
+      }
+      // A set's last row in this wave's rows: the whole wave zeroes the set's
+      // padding columns of the 64 features, 16 bytes a lane (whole aligned
+      // 16-groups, so the key order inside them is moot).  A 32-row block
+      // holds at most one set end (sets have at least 32 rows).
+      if (g.vt_seq != 0) {
 #pragma unroll
-          for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int e = fb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              for (int64_t z = vc.pad0; z < vc.pad1; ++z) dst[(int64_t)e * g.vt_rows + z] = (OT)0.f;
-            }
+        for (int tb = 0; tb < TB; ++tb) {
+          const int64_t w = mbase + tb * 32 + j;
+          const VtCol vc = vt_column(g, w + g.dst_off);
+          const uint64_t ends = __ballot(vc.col >= 0 && vc.t == g.dss.d - 1 &&
+                                         !(g.real_only && row_src(g, w) < 0));
+          if (ends == 0) continue;
+          const int src = __builtin_ctzll(ends);
+          const int64_t pad0 = __shfl(vc.pad0, src), pad1 = __shfl(vc.pad1, src);
+          const int chunks = (int)((pad1 - pad0) >> 3);  // 16-byte chunks per feature row
+          for (int i = lane; i < kDh * chunks; i += 64) {
+            const int e = i / chunks, c = i - e * chunks;
+            *reinterpret_cast<u32x4*>(dst + (int64_t)e * g.vt_rows + pad0 + c * 8) =
+                u32x4{0u, 0u, 0u, 0u};
+          }
         }
       }
     }
