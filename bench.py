@@ -108,14 +108,17 @@ def gpu_inputs(w):
     return inp, {k: inp[k].to("cuda").contiguous() for k in keys}
 
 
-def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None, operands="fp16"):
+def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None, operands="fp16", inplace=False):
     """ms per full call and ms per attention-core stage, both with HIP events
     on the stream the library launches on (torch's current stream).  rows =
-    (begin, count): the query-row window of the global block instead."""
+    (begin, count): the query-row window of the global block instead.
+    inplace (register mode): Y = X on a copy of X, so the patch rows stay
+    where they are and only the special rows are written."""
     import torch
     from vggt_global_attention_amd import api
     from vggt_global_attention_amd import binding as B
-    args = (d["X"], d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
+    X = d["X"].clone() if inplace else d["X"]
+    args = (X, d["Wqkv"], d["Wo"], d["q_gamma"], d["q_beta"], d["k_gamma"], d["k_beta"])
     if rows is not None:
         blk = api.RowsBlock(d["X"], w.H, w.grid_h, w.grid_w, rows[0], rows[1])
         Y = torch.empty((rows[1], w.d), dtype=d["X"].dtype, device=d["X"].device)
@@ -124,7 +127,7 @@ def time_block(w, mode, d, steps, warmup, sub=(1, 1), rows=None, operands="fp16"
             blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, merge=sub)
         else:
             blk = api.Block(mode, d["X"], w.H, w.grid_h, w.grid_w, sub=sub, operands=operands)
-        Y = torch.empty_like(d["X"])
+        Y = X if inplace else torch.empty_like(d["X"])
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         blk(*args, Y=Y)
@@ -649,7 +652,7 @@ def main():
         # (mode, sub / merge parameters, attention operand type)
         runs = (("s24", (("global", (1, 1), "fp16"), ("frame", (1, 1), "fp16"))),
                 ("s500", (("frame", (1, 1), "fp16"), ("frame", (1, 1), "bf16"),
-                          ("register", (1, 1), "fp16"))),
+                          ("register", (1, 1), "fp16"), ("register", (1, 1), "fp16", "inplace"))),
                 ("s100", (("global", (1, 1), "bf16"), ("subsampled", (3, 3), "fp16"),
                           ("merged", httm, "fp16"))),
                 ("s300", (("global", (1, 1), "fp16"), ("subsampled", (3, 3), "fp16"),
@@ -657,9 +660,11 @@ def main():
         for name, modes in runs:
             ww = configs.WORKLOADS[name]
             dd = d if name == a.workload else gpu_inputs(ww)[1]
-            for mode, esub, ops in modes:
-                print(f"[bench] extra {name} {mode} {esub} {ops}", file=sys.stderr, flush=True)
-                m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub, operands=ops)
+            for mode, esub, ops, *flags in modes:
+                print(f"[bench] extra {name} {mode} {esub} {ops} {' '.join(flags)}", file=sys.stderr,
+                      flush=True)
+                m2, c2 = time_block(ww, mode, dd, max(3, a.steps // 2), 2, esub, operands=ops,
+                                    inplace="inplace" in flags)
                 key = f"{name}_{mode}"
                 if mode == "subsampled":
                     key += f"{esub[0]}x{esub[1]}"
@@ -667,6 +672,8 @@ def main():
                     key += "_F{}w{}x{}r{}".format(*esub)
                 if ops == "bf16":
                     key += "_bf16ops"
+                if "inplace" in flags:
+                    key += "_inplace"
                 # merged mode: FLOP of the attention over the merged tokens
                 # (the merge and unmerge kernels run inside core_ms)
                 extra[key] = {"ms_per_layer": m2, "tflops": ww.flop(mode, esub) / m2 / 1e9,
