@@ -39,10 +39,11 @@
  *   - v1 limits: Dh = d/H must be 64, d a multiple of 128, S >= 1, grid_h,
  *     grid_w >= 0, T = 17 + grid_h*grid_w, S*T < 2^31 tokens, and at most
  *     2^28 key / value rows per head in the workspace (the tokens, each set
- *     padded to 64 and the total to 2,048 from 16,384 rows, else to 256 --
- *     frame sets: query / key rows padded to 16 per frame, value columns to
- *     64 per frame; or the kept, merged or descriptor keys padded to 256):
- *     ESHAPE beyond, and vggt_attn_workspace_bytes reports 0.
+ *     padded to 64 and the total to a multiple of 2,048 when that adds at
+ *     most 1/64 of the rows, else of 256 -- frame sets: query / key rows
+ *     padded to 16 per frame, value columns to 64 per frame; or the kept,
+ *     merged or descriptor keys padded to 256): ESHAPE beyond, and
+ *     vggt_attn_workspace_bytes reports 0.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it and the call returns without synchronising; kernel
  *     faults surface at the caller's next synchronisation.

@@ -96,19 +96,21 @@ def test_workspace_bytes():
     assert B.vggt_attn_workspace_bytes(B.MODE_GLOBAL, shape(T=1030)) == 0
 
 
+def _pad_rows(cover):
+    # the header's rule: to a multiple of 2,048 when that adds at most 1/64 of
+    # the rows, else to a multiple of 256
+    wide = -(-cover // 2048) * 2048
+    return wide if wide - cover <= cover // 64 else -(-cover // 256) * 256
+
+
 def _kv_rows(mode, S, T=1031):
-    # the header's padding rule: the global set to 64 keys, the total to 2,048
-    # rows from 16,384 on (else 256); frame sets: q / k rows 16 per frame (plus
-    # the last frame's last key tile), v^T columns 64 per frame, the total to
-    # 256 -- the larger of the two counts
+    # the global set padded to 64 keys; frame sets: q / k rows 16 per frame
+    # (plus the last frame's last key tile), v^T columns 64 per frame, the
+    # total to 256 -- the larger of the two counts
     if mode == B.MODE_FRAME:
         ss, vts = -(-T // 16) * 16, -(-T // 64) * 64
-        cover = ss * (S - 1) + vts
-        a = 2048 if cover >= 16384 else 256
-        return max(-(-cover // a) * a, -(-(S * vts) // 256) * 256)
-    cover = -(-(S * T) // 64) * 64
-    a = 2048 if cover >= 16384 else 256
-    return -(-cover // a) * a
+        return max(_pad_rows(ss * (S - 1) + vts), -(-(S * vts) // 256) * 256)
+    return _pad_rows(-(-(S * T) // 64) * 64)
 
 
 def test_key_value_row_limit():

@@ -142,7 +142,7 @@ int make_plan(int mode, const vggt_attn_shape* s, const CallOpts& o, Plan* p) {
     p->attn_waves = knob;
     tile_forced = true;
   }
-  p->rows = round_up(cover, cover >= kRowAlignFrom ? kRowAlign : 256);
+  p->rows = row_padding(cover);
   if (p->rows >= ((int64_t)1 << 31)) return VGGT_ATTN_ESHAPE;  // kernels index rows in 32 bits
   p->sub_h = sub_h;
   p->sub_w = sub_w;

@@ -16,10 +16,14 @@ constexpr int kGemmBN = 128;        // output features per GEMM tile (two heads)
 constexpr int kGemmBK = 64;
 constexpr int kAttnBK = 64;         // keys per attention tile
 // Workspace rows are padded to kRowAlign (8 XCDs x 256-row GEMM tiles, so
-// each XCD walks whole token tiles), or to one 256-row tile when that
-// padding would be large (fewer than kRowAlignFrom rows).
+// each XCD walks whole token tiles) when that adds at most 1/64 of the rows,
+// else to one 256-row tile (the GEMMs would compute more padding rows than
+// the even XCD split saves).
 constexpr int kRowAlign = 2048;
-constexpr int kRowAlignFrom = 16384;
+inline int64_t row_padding(int64_t cover) {
+  const int64_t wide = (cover + kRowAlign - 1) / kRowAlign * kRowAlign;
+  return wide - cover <= cover / 64 ? wide : (cover + 255) / 256 * 256;
+}
 // Key / value rows per head at most 2^28: the attention kernel's copies address
 // eight v^T rows from one base with a 32-bit byte offset (8 * kv_rows * 2 < 2^32).
 constexpr int64_t kMaxKvRows = (int64_t)1 << 28;
