@@ -424,8 +424,8 @@ int vggt_attn_schedule_run(const vggt_attn_shape* shape, const vggt_attn_schedul
    what the block call of that mode computes with a workspace of its own.
    Calls whose workspace need (vggt_attn_workspace_bytes) exceeds the array
    return VGGT_ATTN_ESCRATCH before anything is enqueued (e.g. 128 MiB holds
-   register mode up to 500+ frames and global mode up to 9 frames of
-   26 x 39 patches at d = 1024).  All other checks and status codes are the
+   register mode up to 587 frames, frame mode up to 20 and global mode up to
+   9 frames of 26 x 39 patches at d = 1024).  All other checks and status codes are the
    block call's.  Every call on a device shares that device's array: calls
    that overlap in time on one device (different streams, or several host
    threads) race; order them on one stream.  Nothing needs clearing between
