@@ -683,6 +683,14 @@ def main():
                     extra[key]["kept_keys"] = ww.kept_keys(*esub)
                 if mode == "merged":
                     extra[key]["merged_tokens"] = ww.merged_tokens(*esub)
+                if key.endswith("register_inplace") and key[:-len("_inplace")] in extra:
+                    # the patch-row copy: the out-of-place call minus the in-place one
+                    # (HBM-bound; 2 bytes read + 2 written per patch element)
+                    pb = 4.0 * ww.S * (ww.T - 17) * ww.d
+                    pm = extra[key[:-len("_inplace")]]["ms_per_layer"] - m2
+                    extra[f"{name}_register_patch_copy"] = {"bytes": pb, "ms": pm,
+                                                           "gbs": pb / pm / 1e6 if pm > 0 else None,
+                                                           "peak_gbs": 8000.0}
             if dd is not d:
                 del dd
             torch.cuda.empty_cache()
