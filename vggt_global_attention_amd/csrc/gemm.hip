@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // [x*ntm/8, (x+1)*ntm/8) -- every X (or O) row is fetched from HBM by one
   // XCD only -- and walks them once per group of output features, all token
   // tiles of a group before the next group: the group's slice of the weights
-  // (fgroups is picked on the host so that a slice is about 2 MB) stays in
+  // (fgroups is picked on the host so that a slice is at most 3 MB) stays in
   // the XCD's L2 while the token tiles stream past, and X is read fgroups
   // times in all.  Otherwise fall back to one contiguous range of (token
   // tile, feature tile) per XCD.
@@ -981,14 +981,16 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g) {
 }
 
 // Smallest number of output-feature groups (a divisor of the feature tile
-// count) whose weight slice fits a ~2 MB share of an XCD's 4 MB L2.
+// count) whose weight slice fits a 3 MB share of an XCD's 4 MB L2 (Wqkv at
+// d = 1024 in two slices: measured against three 2 MB slices, QKV at s100
+// 0.74 vs 0.77 ms and at s500 frame 3.71 vs 3.76 ms).
 static int feature_groups(int nf, int k, int elem_bytes, int bn) {
   const int ntn = nf / bn;
   int v = 0;  // tuning override (must divide the tile count)
   if (tuning_knob("VGGT_GEMM_FGROUPS", &v) && v >= 1 && ntn % v == 0) return v;
   const int64_t bytes = (int64_t)nf * k * elem_bytes;
   for (int gcount = 1; gcount < ntn; ++gcount)
-    if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)2 << 20)) return gcount;
+    if (ntn % gcount == 0 && bytes / gcount <= ((int64_t)3 << 20)) return gcount;
   return ntn;
 }
 
