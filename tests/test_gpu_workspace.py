@@ -40,8 +40,11 @@ def _run(mode, w, d, fill):
 
 
 # tiny (T = 81: rows 96 per frame, v^T 128), a ragged 3-frame set (T = 52:
-# 64 / 64), a single frame and the 24-frame layer (T = 1,031: 1,040 / 1,088)
-CASES = [("tiny", None), ("ragged", (3, 5, 7, 256, 4)), ("one", (1, 26, 39, 256, 4)),
+# 64 / 64), frames of 48 tokens (48 / 64: one padding 16-group), of 64 (64 /
+# 64) and of 17 (special tokens only: 32 / 64), a single frame and the
+# 24-frame layer (T = 1,031: 1,040 / 1,088)
+CASES = [("tiny", None), ("ragged", (3, 5, 7, 256, 4)), ("t48", (5, 1, 31, 256, 4)),
+         ("t64", (4, 1, 47, 256, 4)), ("t17", (6, 0, 0, 128, 2)), ("one", (1, 26, 39, 256, 4)),
          ("s24", None)]
 
 
